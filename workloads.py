@@ -1,0 +1,302 @@
+"""Seeded synthetic inputs for one flash-decoding attention step.
+
+This module only *makes data*: sequence lengths, Q, paged or contiguous K/V caches
+(optionally FP8 E4M3 with fp32 scales), block tables.  It holds none of the
+attention arithmetic, and both the HIP path and the fp64 oracle consume exactly
+the tensors it returns.  Nothing here imports either side.
+
+Workloads (sizes as specified for the decode workloads this library targets):
+
+* ``tiny_mqa_f16``      batch 2, 4 q heads / 1 kv head, head_dim 64, seq_len {37, 100},
+                        contiguous fp16 KV.
+* ``gqa_bf16``          batch 16, 32 q / 8 kv heads, head_dim 128, seq_len ~ U[512, 4096],
+                        bf16 KV, block_size 64, randomly permuted block table.
+* ``fp8_32k``           batch 32, 64 q / 8 kv heads, head_dim 128, seq_len ~ logU[1K, 32K],
+                        E4M3 KV with per-(token, kv-head) fp32 scales, block_size 64.
+* ``mqa_fp8_128k``      batch 4, seq_len 131072, 128 q / 1 kv head, head_dim 128,
+                        E4M3 KV with one per-tensor scale, block_size 64.
+* ``ragged_fp8``        batch 256, 90 % seq_len ~ U[256, 2048] and 10 % ~ U[32K, 128K],
+                        32 q / 8 kv heads, head_dim 128, E4M3 KV, block_size 32, shuffled blocks.
+
+Recipe (the readings are listed in the design doc):
+
+* Sequence lengths come from ``numpy.random.Generator(PCG64(seed))``; integer bounds are
+  inclusive; log-uniform is ``round(exp(U(ln a, ln b)))``; the ragged mix has exactly
+  ``round(0.1 * batch)`` long sequences at seeded positions.
+* Q, K, V source values are N(0, 1) fp32 from ``torch.Generator(device).manual_seed(seed)``
+  (the stream depends on the device; every consumer gets the same tensors, so this is fine).
+* FP8 rows are quantised row-absmax style, the way activations are quantised in the
+  "小算子融合 residual + RMSNorm + quant" passage of the ch.15 profiling page:
+  ``scale = amax / 448`` (1 if amax is 0), ``byte = RNE(x / scale)`` via torch's own
+  ``float8_e4m3fn`` cast.  Per-tensor scale takes amax over the whole tensor.
+* Paged caches hold ``sum(ceil(n_b / bs))`` live blocks plus 8 spare blocks, placed by a random
+  permutation (the "fragmented" page placement of the ch.15 paged-KV scan passage).
+  Everything the kernels must never read is poisoned: slots past ``seq_len`` in the last block,
+  spare blocks (NaN payload, NaN scales) and unused block-table entries (-1).
+* Contiguous caches put sequences back to back with 3 NaN rows between them (``kv_start``).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+FP8_MAX = 448.0
+SPARE_BLOCKS = 8
+CONTIG_GAP_ROWS = 3
+
+# dtype names shared by the binding, the oracle wrapper and the tests
+KV_DTYPES = ("f16", "bf16", "fp8_e4m3")
+Q_DTYPES = ("f16", "bf16")
+SCALE_MODES = ("none", "tensor", "token_head")
+
+_TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+WORKLOADS = {
+    "tiny_mqa_f16": dict(batch=2, hq=4, hkv=1, d=64, lens=("fixed_list", [37, 100]), kv="f16",
+                         q="f16", block_size=0, scale="none", paged=False),
+    "gqa_bf16": dict(batch=16, hq=32, hkv=8, d=128, lens=("uniform", 512, 4096), kv="bf16",
+                     q="bf16", block_size=64, scale="none", paged=True),
+    "fp8_32k": dict(batch=32, hq=64, hkv=8, d=128, lens=("loguniform", 1024, 32768), kv="fp8_e4m3",
+                    q="bf16", block_size=64, scale="token_head", paged=True),
+    "mqa_fp8_128k": dict(batch=4, hq=128, hkv=1, d=128, lens=("fixed", 131072), kv="fp8_e4m3",
+                         q="bf16", block_size=64, scale="tensor", paged=True),
+    "ragged_fp8": dict(batch=256, hq=32, hkv=8, d=128,
+                       lens=("mix", 0.1, (256, 2048), (32768, 131072)), kv="fp8_e4m3",
+                       q="bf16", block_size=32, scale="token_head", paged=True),
+}
+
+
+@dataclasses.dataclass
+class Case:
+    """One decode step's inputs.  Tensors live on ``device``; ``seq_lens`` is a host list."""
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    kv_dtype: str
+    q_dtype: str
+    scale_mode: str
+    block_size: int            # 0 in contiguous mode
+    paged: bool
+    seq_lens: list
+    max_seq_len: int
+    q: torch.Tensor            # [B][Hq][D] f16/bf16
+    k_cache: torch.Tensor      # paged [NB][bs][Hkv][D] / contiguous [rows][Hkv][D]; uint8 for FP8
+    v_cache: torch.Tensor
+    k_scale: Optional[torch.Tensor]   # fp32: [1] or paged [NB][bs][Hkv] / contiguous [rows][Hkv]
+    v_scale: Optional[torch.Tensor]
+    block_table: Optional[torch.Tensor]  # int32 [B][max_blocks] (paged)
+    kv_start: Optional[torch.Tensor]     # int32 [B] (contiguous)
+    seq_len: torch.Tensor                # int32 [B]
+    max_blocks: int
+    softmax_scale: float
+
+    @property
+    def group(self) -> int:
+        return self.hq // self.hkv
+
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.kv_dtype == "fp8_e4m3" else 2
+
+    def kv_read_bytes(self) -> int:
+        """K+V payload plus scale bytes the method must read for this step."""
+        toks = sum(self.seq_lens)
+        b = toks * self.hkv * self.d * self.kv_elem_bytes() * 2
+        if self.scale_mode == "token_head":
+            b += toks * self.hkv * 4 * 2
+        elif self.scale_mode == "tensor":
+            b += 8
+        return b
+
+    def to(self, device) -> "Case":
+        kw = {}
+        for f in dataclasses.fields(self):
+            v = getattr(self, f.name)
+            kw[f.name] = v.to(device) if isinstance(v, torch.Tensor) else v
+        return Case(**kw)
+
+
+def draw_seq_lens(spec, batch: int, rng: np.random.Generator) -> list:
+    kind = spec[0]
+    if kind == "fixed_list":
+        lens = list(spec[1])
+        assert len(lens) == batch
+        return [int(x) for x in lens]
+    if kind == "fixed":
+        return [int(spec[1])] * batch
+    if kind == "uniform":
+        return [int(x) for x in rng.integers(spec[1], spec[2], size=batch, endpoint=True)]
+    if kind == "loguniform":
+        u = rng.uniform(math.log(spec[1]), math.log(spec[2]), size=batch)
+        return [int(x) for x in np.clip(np.rint(np.exp(u)), spec[1], spec[2])]
+    if kind == "mix":
+        frac, short, long_ = spec[1], spec[2], spec[3]
+        n_long = int(round(frac * batch))
+        long_pos = set(int(x) for x in rng.choice(batch, size=n_long, replace=False))
+        short_l = rng.integers(short[0], short[1], size=batch, endpoint=True)
+        long_l = rng.integers(long_[0], long_[1], size=batch, endpoint=True)
+        return [int(long_l[i]) if i in long_pos else int(short_l[i]) for i in range(batch)]
+    raise ValueError(f"unknown length spec {spec!r}")
+
+
+def _nan_bits(dtype: str) -> int:
+    return {"f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}[dtype]
+
+
+def _quant_rows(x: torch.Tensor):
+    """Row-absmax FP8 quantisation of the last dim: returns (uint8 bytes, fp32 scales)."""
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    y = (x / scale.unsqueeze(-1)).clamp_(-FP8_MAX, FP8_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), scale.to(torch.float32)
+
+
+def _quant_tensor(x: torch.Tensor, amax: float):
+    scale = amax / FP8_MAX if amax > 0 else 1.0
+    scale = float(np.float32(scale))
+    y = (x / scale).clamp_(-FP8_MAX, FP8_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
+
+
+def _fill_store(n_rows: int, hkv: int, d: int, kv: str, scale: str, device, gen,
+                chunk_rows: int = 1 << 19):
+    """Generate K and V row stores ([n_rows][hkv][d]) plus scales, chunk by chunk."""
+    storage_dtype = torch.uint8 if kv == "fp8_e4m3" else _TORCH[kv]
+    k = torch.empty((n_rows, hkv, d), dtype=storage_dtype, device=device)
+    v = torch.empty_like(k)
+    ks = vs = None
+    if scale == "token_head":
+        ks = torch.empty((n_rows, hkv), dtype=torch.float32, device=device)
+        vs = torch.empty_like(ks)
+    if scale == "tensor":
+        # per-tensor amax needs the whole tensor: generate at once (sizes here allow it)
+        ksrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32)
+        vsrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32)
+        kb, kscale = _quant_tensor(ksrc, float(ksrc.abs().max()))
+        vb, vscale = _quant_tensor(vsrc, float(vsrc.abs().max()))
+        k.copy_(kb)
+        v.copy_(vb)
+        del ksrc, vsrc
+        ks = torch.tensor([kscale], dtype=torch.float32, device=device)
+        vs = torch.tensor([vscale], dtype=torch.float32, device=device)
+        return k, v, ks, vs
+    for r0 in range(0, n_rows, chunk_rows):
+        r1 = min(n_rows, r0 + chunk_rows)
+        for dst, sdst in ((k, ks), (v, vs)):
+            src = torch.randn((r1 - r0, hkv, d), generator=gen, device=device, dtype=torch.float32)
+            if kv == "fp8_e4m3":
+                b, s = _quant_rows(src)
+                dst[r0:r1] = b
+                sdst[r0:r1] = s
+            else:
+                dst[r0:r1] = src.to(storage_dtype)
+    return k, v, ks, vs
+
+
+def _poison_rows(t: torch.Tensor, rows: torch.Tensor, nan_bits: int):
+    if rows.numel() == 0:
+        return
+    if t.dtype == torch.uint8:
+        t[rows] = nan_bits
+    elif t.dtype == torch.float32:
+        t[rows] = float("nan")
+    else:
+        t.view(torch.int16)[rows] = np.int16(np.uint16(nan_bits).view(np.int16))
+
+
+def make_case(name: str = "fp8_32k", seed: int = 0, device="cpu", seq_lens=None,
+              **overrides) -> Case:
+    """Build the inputs of one named workload (fields can be overridden, e.g. batch, lens)."""
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    return _build(name, cfg, seed, device, seq_lens)
+
+
+def _build(name, cfg, seed, device, seq_lens) -> Case:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    batch = cfg["batch"]
+    if seq_lens is None:
+        seq_lens = draw_seq_lens(cfg["lens"], batch, rng)
+    seq_lens = [int(x) for x in seq_lens]
+    assert len(seq_lens) == batch
+    hq, hkv, d = cfg["hq"], cfg["hkv"], cfg["d"]
+    kv, qd, scale, paged = cfg["kv"], cfg["q"], cfg["scale"], cfg["paged"]
+    bs = cfg["block_size"] if paged else 0
+    if kv != "fp8_e4m3":
+        scale = "none"
+    max_seq_len = int(cfg.get("max_seq_len", max(seq_lens) if seq_lens else 0))
+    gen = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn((batch, hq, d), generator=gen, device=device, dtype=torch.float32).to(_TORCH[qd])
+    nan = _nan_bits(kv)
+    if paged:
+        nb_per = [(n + bs - 1) // bs for n in seq_lens]
+        live = sum(nb_per)
+        num_blocks = live + SPARE_BLOCKS
+        max_blocks = max(1, (max_seq_len + bs - 1) // bs)
+        perm = rng.permutation(num_blocks) if cfg.get("shuffle", True) else np.arange(num_blocks)
+        table = np.full((batch, max_blocks), -1, dtype=np.int32)
+        off = 0
+        for b, nb in enumerate(nb_per):
+            table[b, :nb] = perm[off:off + nb]
+            off += nb
+        spare = perm[live:]
+        k, v, ks, vs = _fill_store(num_blocks * bs, hkv, d, kv, scale, device, gen)
+        # poison rows that must never be read
+        dead = [np.arange(p * bs, (p + 1) * bs) for p in spare]
+        for b, n in enumerate(seq_lens):
+            if n % bs:
+                p = table[b, nb_per[b] - 1]
+                dead.append(np.arange(p * bs + n % bs, (p + 1) * bs))
+        dead_rows = torch.from_numpy(np.concatenate(dead) if dead else np.zeros(0, np.int64)).to(device)
+        for t in (k, v):
+            _poison_rows(t, dead_rows, nan)
+        if scale == "token_head":
+            for t in (ks, vs):
+                _poison_rows(t, dead_rows, 0)
+            ks = ks.view(num_blocks, bs, hkv)
+            vs = vs.view(num_blocks, bs, hkv)
+        k = k.view(num_blocks, bs, hkv, d)
+        v = v.view(num_blocks, bs, hkv, d)
+        block_table = torch.from_numpy(table).to(device)
+        kv_start = None
+    else:
+        starts, rows = [], 0
+        for n in seq_lens:
+            rows += CONTIG_GAP_ROWS
+            starts.append(rows)
+            rows += n
+        rows += CONTIG_GAP_ROWS
+        k, v, ks, vs = _fill_store(rows, hkv, d, kv, scale, device, gen)
+        live = np.zeros(rows, dtype=bool)
+        for s, n in zip(starts, seq_lens):
+            live[s:s + n] = True
+        dead_rows = torch.from_numpy(np.nonzero(~live)[0]).to(device)
+        for t in (k, v):
+            _poison_rows(t, dead_rows, nan)
+        if scale == "token_head":
+            for t in (ks, vs):
+                _poison_rows(t, dead_rows, 0)
+        block_table = None
+        max_blocks = 0
+        kv_start = torch.tensor(starts, dtype=torch.int32, device=device)
+    seq_len = torch.tensor(seq_lens, dtype=torch.int32, device=device)
+    return Case(name=name, batch=batch, hq=hq, hkv=hkv, d=d, kv_dtype=kv, q_dtype=qd,
+                scale_mode=scale, block_size=bs, paged=paged, seq_lens=seq_lens,
+                max_seq_len=max_seq_len, q=q, k_cache=k, v_cache=v, k_scale=ks, v_scale=vs,
+                block_table=block_table, kv_start=kv_start, seq_len=seq_len,
+                max_blocks=max_blocks, softmax_scale=1.0 / math.sqrt(d))
+
+
+def custom_case(seed=0, device="cpu", *, batch, hq, hkv, d, seq_lens, kv="fp8_e4m3", q="bf16",
+                block_size=64, scale="token_head", paged=True, shuffle=True, max_seq_len=None):
+    """A case with explicit shapes (edge cases and small parity sizes)."""
+    cfg = dict(batch=batch, hq=hq, hkv=hkv, d=d, lens=("fixed_list", list(seq_lens)), kv=kv,
+               q=q, block_size=block_size, scale=scale, paged=paged, shuffle=shuffle)
+    if max_seq_len is not None:
+        cfg["max_seq_len"] = max_seq_len
+    return _build("custom", cfg, seed, device, list(seq_lens))
