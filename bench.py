@@ -1,0 +1,203 @@
+"""Benchmark: one flash-decoding step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fp8_32k] [--num-splits 0]
+
+Prints ONE JSON line.  A step is one fd_decode_attention call (split-KV partition kernel +
+combine kernel) over one batch of synthetic, seeded inputs already resident in HBM.  Each step
+reads a different copy of the KV cache (the copies are rotated) so no step is served from the
+256 MB Infinity Cache left warm by the previous one.
+
+value           = KV-read bytes (K + V payload + scales) per step / mean step time, in GB/s.
+roofline        = the partition kernel: the same algorithmic bytes / its mean duration from
+                  HIP events recorded around it on its stream, against 8 TB/s HBM peak.
+cpu_baseline    = the fp64 oracle on the host cores, same inputs (a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved KV-read HBM GB/s (% of peak) and µs per decode step"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_06_amd", "csrc", "fd_kernels.hip")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM traffic per partition launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_partition_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fp8_32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="KV copies rotated across steps (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this decode path is single-GPU by design.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_06_amd as fd
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    case = workloads.make_case(args.workload, seed=args.seed, device=dev)
+    kv_bytes = case.kv_read_bytes()
+    ncopy = args.copies or max(2, math.ceil(2 * MALL_BYTES / max(kv_bytes, 1)) + 1)
+    copies = [case]
+    for _ in range(ncopy - 1):
+        c = workloads.Case(**{k: getattr(case, k) for k in case.__dataclass_fields__})
+        c.k_cache = case.k_cache.clone()
+        c.v_cache = case.v_cache.clone()
+        if case.k_scale is not None:
+            c.k_scale = case.k_scale.clone()
+            c.v_scale = case.v_scale.clone()
+        copies.append(c)
+    out = torch.empty((case.batch, case.hq, case.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((case.batch, case.hq), dtype=torch.float32, device=dev)
+    wsb = fd.workspace_bytes(case.batch, case.hq, case.hkv, case.d, case.max_seq_len, case.block_size,
+                             case.kv_dtype, args.num_splits)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    nsplit, split_tokens = fd.plan_splits(case.batch, case.hq, case.hkv, case.d, case.max_seq_len,
+                                          case.block_size, case.kv_dtype, args.num_splits)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        fd.decode_case(copies[i % ncopy], out=out, lse=lse, workspace=ws, num_splits=args.num_splits,
+                       stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, back to back
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # ---- partition-kernel durations from HIP events recorded around it, on its stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        fd.set_profile_events(*evs[i])
+        step(i)
+    fd.set_profile_events(None, None)
+    torch.cuda.synchronize()
+    kdur_ms = [a.elapsed_time(b) for a, b in evs]
+    kmean_ms = float(np.mean(kdur_ms))
+    k_achieved = kv_bytes / (kmean_ms * 1e-3) / 1e9
+
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": case.batch, "num_q_heads": case.hq,
+            "num_kv_heads": case.hkv, "head_dim": case.d, "kv_dtype": case.kv_dtype,
+            "q_dtype": case.q_dtype, "scale_mode": case.scale_mode, "block_size": case.block_size,
+            "tokens": int(sum(case.seq_lens)), "max_seq_len": case.max_seq_len,
+            "kv_read_bytes": kv_bytes, "num_splits": nsplit, "split_tokens": split_tokens,
+            "kv_copies_rotated": ncopy, "seed": args.seed,
+            "compute": "E4M3/bf16 K -> bf16 MFMA q.k, f16 MFMA p.v, f32 softmax and accumulate",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "partition_kernel",
+            "bound": "hbm",
+            "achieved": round(k_achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k_achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(args.workload),
+            "kernel_us_mean": round(kmean_ms * 1e3, 2),
+            "kernel_us_p10_p90": [round(float(np.percentile(kdur_ms, 10)) * 1e3, 2),
+                                  round(float(np.percentile(kdur_ms, 90)) * 1e3, 2)],
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        prob = oracle.Problem.from_case(case)
+        # bounded sample: the longest sequences until ~1/4 of the step's tokens (the oracle's
+        # cost is linear in tokens x heads), timed once
+        order = sorted(range(case.batch), key=lambda b: -case.seq_lens[b])
+        sample, toks = [], 0
+        for b in order:
+            if toks >= sum(case.seq_lens) / 4 and sample:
+                break
+            sample.append(b)
+            toks += case.seq_lens[b]
+        t0 = time.perf_counter()
+        oracle.decode_attention(prob, seqs=sample, nthreads=threads)
+        dt = time.perf_counter() - t0
+        sample_bytes = kv_bytes * toks / max(1, sum(case.seq_lens))
+        result["cpu_baseline"] = {
+            "value": round(sample_bytes / dt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(sample)} longest of {case.batch} sequences ({toks} of "
+                      f"{sum(case.seq_lens)} tokens, all heads), 1 run, {dt:.2f} s wall",
+            "us_per_step_extrapolated": round(dt * 1e6 * sum(case.seq_lens) / max(1, toks), 1),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""Python binding of the flash-decoding C ABI (``include/fd.h``), via ctypes.
+
+Argument marshalling only: every step of the attention runs in the HIP kernels of
+``libfd.so``.  PyTorch provides device memory and the current HIP stream.  If the library
+cannot be loaded (or built) the calls raise -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfd.so")
+
+FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_LAUNCH = 0, 1, 2, 3, 4
+FD_F32, FD_F16, FD_BF16, FD_FP8_E4M3 = 0, 1, 2, 3
+FD_SCALE_NONE, FD_SCALE_PER_TENSOR, FD_SCALE_PER_TOKEN_HEAD = 0, 1, 2
+
+DTYPE_CODES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8_e4m3": FD_FP8_E4M3}
+SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head": FD_SCALE_PER_TOKEN_HEAD}
+EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_splits", "fd_status_string",
+           "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, what: str = "fd_decode_attention"):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)} ({status})")
+
+
+def _c_int(x):
+    return ctypes.c_int(int(x))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfd.so, building it first if it is not there."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            from . import _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.fd_decode_attention.restype = i32
+        L.fd_decode_attention.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, vp, vp, ctypes.c_float, vp, i32, vp, vp, sz,
+                                          i32, vp]
+        L.fd_workspace_bytes.restype = sz
+        L.fd_workspace_bytes.argtypes = [i32] * 8
+        L.fd_plan_splits.restype = i32
+        L.fd_plan_splits.argtypes = [i32] * 8 + [ctypes.POINTER(i32)]
+        L.fd_status_string.restype = ctypes.c_char_p
+        L.fd_status_string.argtypes = [i32]
+        L.fd_version.restype = i32
+        L.fd_version.argtypes = []
+        L.fd_fp8_e4m3_decode.restype = i32
+        L.fd_fp8_e4m3_decode.argtypes = [vp, vp, i32, vp]
+        L.fd_set_profile_events.restype = i32
+        L.fd_set_profile_events.argtypes = [vp, vp]
+        _lib = L
+        return L
+
+
+def status_string(status: int) -> str:
+    return lib().fd_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return lib().fd_version()
+
+
+def workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0,
+                    kv_dtype="fp8_e4m3", num_splits=0) -> int:
+    n = lib().fd_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                 block_size, DTYPE_CODES.get(kv_dtype, kv_dtype), num_splits)
+    if n == ctypes.c_size_t(-1).value:
+        raise FdError(FD_ERR_INVALID_ARG, "fd_workspace_bytes")
+    return n
+
+
+def plan_splits(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0,
+                kv_dtype="fp8_e4m3", num_splits=0):
+    """(max splits per sequence, split length in tokens) the library will use."""
+    st = ctypes.c_int(0)
+    n = lib().fd_plan_splits(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
+                             DTYPE_CODES.get(kv_dtype, kv_dtype), num_splits, ctypes.byref(st))
+    if n < 0:
+        raise FdError(FD_ERR_INVALID_ARG, "fd_plan_splits")
+    return n, st.value
+
+
+def decode_attention_raw(q, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start, seq_len,
+                         batch, max_seq_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                         kv_dtype, q_dtype, scale_mode, k_scale, v_scale, softmax_scale, out,
+                         out_dtype, lse, workspace, workspace_bytes_, num_splits, stream) -> int:
+    """Direct call of fd_decode_attention with integer pointers/codes; returns the status."""
+    return lib().fd_decode_attention(q, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start,
+                                     seq_len, batch, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                                     block_size, kv_dtype, q_dtype, scale_mode, k_scale, v_scale,
+                                     ctypes.c_float(softmax_scale), out, out_dtype, lse, workspace,
+                                     workspace_bytes_, num_splits, stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _require_cuda(**tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+
+
+def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_table=None,
+                     kv_start=None, kv_dtype: str, scale_mode: str = "none", k_scale=None,
+                     v_scale=None, softmax_scale: float, num_kv_heads: int | None = None,
+                     block_size: int = 0, out=None, out_dtype: str = "f32", lse=None,
+                     workspace=None, num_splits: int = 0, stream=None):
+    """One decode step on the GPU.  Shapes follow ``include/fd.h``; sizes are read from the
+    tensors.  ``out``/``workspace`` are allocated with torch when not given (pass them in to
+    keep the call allocation-free).  Returns ``out``."""
+    import torch
+
+    _require_cuda(q=q, k_cache=k_cache, v_cache=v_cache, seq_len=seq_len, block_table=block_table,
+                  kv_start=kv_start, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse,
+                  workspace=workspace)
+    batch, hq, d = q.shape
+    hkv = num_kv_heads if num_kv_heads is not None else k_cache.shape[-2]
+    q_code = {torch.float16: FD_F16, torch.bfloat16: FD_BF16}[q.dtype]
+    kv_code = DTYPE_CODES[kv_dtype]
+    out_code = DTYPE_CODES[out_dtype]
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype={"f32": torch.float32, "f16": torch.float16,
+                                                 "bf16": torch.bfloat16}[out_dtype], device=q.device)
+    max_blocks = 0 if block_table is None else block_table.shape[1]
+    need = workspace_bytes(batch, hq, hkv, d, max_seq_len, block_size, kv_dtype, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = decode_attention_raw(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), max_blocks,
+                              _ptr(kv_start), _ptr(seq_len), batch, max_seq_len, hq, hkv, d,
+                              block_size, kv_code, q_code, SCALE_CODES[scale_mode], _ptr(k_scale),
+                              _ptr(v_scale), float(softmax_scale), _ptr(out), out_code, _ptr(lse),
+                              _ptr(workspace), ws_bytes, num_splits, stream)
+    if st != FD_OK:
+        raise FdError(st)
+    return out
+
+
+def decode_case(case, *, out=None, out_dtype="f32", lse=None, workspace=None, num_splits=0,
+                stream=None):
+    """Convenience: run one ``workloads.Case`` (duck-typed) through the library."""
+    return decode_attention(case.q, case.k_cache, case.v_cache, case.seq_len,
+                            max_seq_len=case.max_seq_len, block_table=case.block_table,
+                            kv_start=case.kv_start, kv_dtype=case.kv_dtype,
+                            scale_mode=case.scale_mode, k_scale=case.k_scale, v_scale=case.v_scale,
+                            softmax_scale=case.softmax_scale, num_kv_heads=case.hkv,
+                            block_size=case.block_size, out=out, out_dtype=out_dtype, lse=lse,
+                            workspace=workspace, num_splits=num_splits, stream=stream)
+
+
+def fp8_e4m3_decode(x, stream=None):
+    """Diagnostic: decode a uint8 GPU tensor with the kernels' conversions -> float32 [n][2]
+    (column 0 via f16, column 1 via bf16)."""
+    import torch
+
+    _require_cuda(x=x)
+    out = torch.empty((x.numel(), 2), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib().fd_fp8_e4m3_decode(x.data_ptr(), out.data_ptr(), x.numel(), stream)
+    if st != FD_OK:
+        raise FdError(st, "fd_fp8_e4m3_decode")
+    return out
+
+
+def set_profile_events(begin=None, end=None):
+    """Diagnostic: record torch.cuda.Event ``begin``/``end`` around the partition kernel of the
+    following calls from this thread (None, None clears)."""
+    if (begin is None) != (end is None):
+        raise ValueError("pass both events or neither")
+    bp = None if begin is None else begin.cuda_event
+    ep = None if end is None else end.cuda_event
+    st = lib().fd_set_profile_events(bp, ep)
+    if st != FD_OK:
+        raise FdError(st, "fd_set_profile_events")

@@ -1,0 +1,194 @@
+// fd_api.cpp -- host side of the C ABI declared in include/fd.h: argument validation, the
+// split plan for 256 compute units, workspace carve-up and the two kernel launches.
+// Nothing here reads device memory or synchronises (no per-step host sync, as the ch.15
+// profiling page's section 15.17 asks; no allocation on the hot path, section 15.22).
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "fd.h"
+#include "fd_internal.h"
+
+namespace {
+
+constexpr int kMinSplit = 256;     // tokens: keeps partial-state traffic small next to KV bytes
+constexpr int kMaxSplit = 4096;    // tokens: keeps enough waves in flight for short batches
+constexpr long kTargetWaves = 8192;  // ~32 waves per CU on 256 CUs when every sequence is full
+
+thread_local hipEvent_t t_prof_begin = nullptr, t_prof_end = nullptr;
+
+inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+    int nhb;
+    int split_tokens;
+    int nsplit;
+};
+
+bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
+    if (batch <= 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0) return false;
+    if (hq % hkv) return false;
+    if (batch > 65535) return false;
+    (void)head_dim;
+    return true;
+}
+
+// Split plan.  Each (sequence, kv head, head block) is a stream of waves; the KV range of a
+// sequence is cut into `nsplit` ranges of `split_tokens` tokens so that a batch of full-length
+// sequences yields about kTargetWaves waves, within [kMinSplit, kMaxSplit] tokens per split.
+Plan make_plan(int batch, int hq, int hkv, int max_seq_len, int num_splits) {
+    Plan pl;
+    const int group = hq / hkv;
+    pl.nhb = (int)cdiv(group, fd::kHeadBlock);
+    const long units = (long)batch * hkv * pl.nhb;
+    long S;
+    if (max_seq_len <= 0) {
+        S = fd::kTile;
+    } else if (num_splits > 0) {
+        S = cdiv(cdiv(max_seq_len, num_splits), fd::kTile) * fd::kTile;
+    } else {
+        S = cdiv((long)max_seq_len * units, kTargetWaves);
+        S = cdiv(S, fd::kTile) * fd::kTile;
+        if (S < kMinSplit) S = kMinSplit;
+        if (S > kMaxSplit) S = kMaxSplit;
+    }
+    pl.split_tokens = (int)S;
+    pl.nsplit = max_seq_len <= 0 ? 1 : (int)cdiv(max_seq_len, S);
+    return pl;
+}
+
+size_t ws_bytes(const Plan &pl, int batch, int hq, int head_dim) {
+    if (pl.nsplit <= 1) return 0;
+    const size_t slots = (size_t)batch * hq * pl.nsplit;
+    return align256(slots * sizeof(float) * 2) + slots * head_dim * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fd_version(void) { return FD_VERSION; }
+
+const char *fd_status_string(int status) {
+    switch (status) {
+    case FD_OK: return "FD_OK";
+    case FD_ERR_INVALID_ARG: return "FD_ERR_INVALID_ARG";
+    case FD_ERR_UNSUPPORTED: return "FD_ERR_UNSUPPORTED";
+    case FD_ERR_WORKSPACE: return "FD_ERR_WORKSPACE";
+    case FD_ERR_LAUNCH: return "FD_ERR_LAUNCH";
+    default: return "FD_UNKNOWN_STATUS";
+    }
+}
+
+int fd_plan_splits(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                   int block_size, int kv_dtype, int num_splits, int *split_tokens) {
+    (void)block_size;
+    (void)kv_dtype;
+    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_splits < 0) return -1;
+    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits);
+    if (split_tokens) *split_tokens = pl.split_tokens;
+    return pl.nsplit;
+}
+
+size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                          int block_size, int kv_dtype, int num_splits) {
+    (void)block_size;
+    (void)kv_dtype;
+    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_splits < 0)
+        return (size_t)-1;
+    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits);
+    return ws_bytes(pl, batch, num_q_heads, head_dim);
+}
+
+int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_table, int max_blocks_per_seq,
+                        const int32_t *kv_start, const int32_t *seq_len,
+                        int batch, int max_seq_len,
+                        int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int kv_dtype, int q_dtype, int scale_mode,
+                        const float *k_scale, const float *v_scale,
+                        float softmax_scale,
+                        void *out, int out_dtype, float *lse,
+                        void *workspace, size_t workspace_bytes,
+                        int num_splits, hipStream_t stream) {
+    // ---- argument validation (host only, nothing launched on failure)
+    if (!q || !k_cache || !v_cache || !seq_len || !out) return FD_ERR_INVALID_ARG;
+    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len)) return FD_ERR_INVALID_ARG;
+    if (num_splits < 0) return FD_ERR_INVALID_ARG;
+    if ((block_table == nullptr) == (kv_start == nullptr)) return FD_ERR_INVALID_ARG;
+    if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
+    if (q_dtype != FD_F16 && q_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
+    if (out_dtype != FD_F32 && out_dtype != FD_F16 && out_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return FD_ERR_INVALID_ARG;
+    if (kv_dtype == FD_FP8_E4M3) {
+        if (scale_mode != FD_SCALE_PER_TENSOR && scale_mode != FD_SCALE_PER_TOKEN_HEAD) return FD_ERR_INVALID_ARG;
+        if (!k_scale || !v_scale) return FD_ERR_INVALID_ARG;
+    } else {
+        if (scale_mode != FD_SCALE_NONE) return FD_ERR_INVALID_ARG;
+        if (q_dtype != kv_dtype) return FD_ERR_UNSUPPORTED;
+    }
+    if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
+    if (block_table) {
+        if (block_size != 32 && block_size != 64) return FD_ERR_UNSUPPORTED;
+        if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
+        if ((long)max_seq_len > (long)max_blocks_per_seq * block_size) return FD_ERR_INVALID_ARG;
+    }
+    const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits);
+    if ((long)num_kv_heads * pl.nhb > 65535) return FD_ERR_UNSUPPORTED;
+    const size_t need = ws_bytes(pl, batch, num_q_heads, head_dim);
+    if (need) {
+        if (!workspace || workspace_bytes < need) return FD_ERR_WORKSPACE;
+        if ((uintptr_t)workspace & 255) return FD_ERR_WORKSPACE;
+    }
+
+    fd::Params p;
+    memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.block_table = block_table;
+    p.kv_start = kv_start;
+    p.seq_len = seq_len;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.out = out;
+    p.lse = lse;
+    p.batch = batch;
+    p.hq = num_q_heads;
+    p.hkv = num_kv_heads;
+    p.d = head_dim;
+    p.block_size = block_table ? block_size : 0;
+    p.max_blocks = block_table ? max_blocks_per_seq : 0;
+    p.max_seq_len = max_seq_len;
+    p.group = num_q_heads / num_kv_heads;
+    p.nhb = pl.nhb;
+    p.split_tokens = pl.split_tokens;
+    p.nsplit = pl.nsplit;
+    p.out_dtype = out_dtype;
+    p.qk_scale = (float)((double)softmax_scale * 1.4426950408889634074);  // log2(e)
+    if (need) {
+        const size_t slots = (size_t)batch * num_q_heads * pl.nsplit;
+        p.ws_ml = (float2 *)workspace;
+        p.ws_acc = (float *)((char *)workspace + align256(slots * sizeof(float) * 2));
+    }
+
+    if (t_prof_begin) (void)hipEventRecord(t_prof_begin, stream);
+    if (fd::launch_partition(p, kv_dtype, q_dtype, scale_mode, stream) != hipSuccess) return FD_ERR_LAUNCH;
+    if (t_prof_end) (void)hipEventRecord(t_prof_end, stream);
+    if (pl.nsplit > 1 && fd::launch_combine(p, stream) != hipSuccess) return FD_ERR_LAUNCH;
+    return FD_OK;
+}
+
+int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end) {
+    t_prof_begin = partition_begin;
+    t_prof_end = partition_end;
+    return FD_OK;
+}
+
+int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream) {
+    if (n < 0 || (n > 0 && (!in || !out))) return FD_ERR_INVALID_ARG;
+    return fd::launch_fp8_decode(in, out, n, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// fd_internal.h -- parameters shared by the host launcher and the gfx950 kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace fd {
+
+// Tokens per wave tile: two 16-row MFMA blocks for q.k^T, one 32-deep MFMA step for p.V.
+constexpr int kTile = 32;
+// Heads per MFMA column block (a GQA group wider than this takes several head blocks).
+constexpr int kHeadBlock = 16;
+
+struct Params {
+    const void *q;
+    const void *k;
+    const void *v;
+    const int32_t *block_table;  // paged mode
+    const int32_t *kv_start;     // contiguous mode
+    const int32_t *seq_len;
+    const float *k_scale;
+    const float *v_scale;
+    void *out;
+    float *lse;
+    float *ws_acc;   // [batch][hq][nsplit][d]   unnormalised partial outputs
+    float2 *ws_ml;   // [batch][hq][nsplit]      (running max in log2 units, running sum)
+    int batch, hq, hkv, d;
+    int block_size, max_blocks;
+    int max_seq_len;  // host bound; seq_len values above it are clamped (never read past it)
+    int group;        // hq / hkv
+    int nhb;          // head blocks per kv head: ceil(group / kHeadBlock)
+    int split_tokens; // tokens per split, multiple of kTile
+    int nsplit;       // maximum splits per sequence
+    int out_dtype;
+    float qk_scale;   // softmax_scale * log2(e): scores are kept in log2 units
+};
+
+// Host-side launchers (defined in fd_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode,
+                            hipStream_t stream);
+hipError_t launch_combine(const Params &p, hipStream_t stream);
+hipError_t launch_fp8_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
+
+}  // namespace fd

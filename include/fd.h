@@ -1,0 +1,161 @@
+/*
+ * fd.h -- C ABI of the flash-decoding attention library for AMD MI355X (gfx950).
+ *
+ * One call computes one decode step of attention: a single query token per sequence against
+ * that sequence's KV cache, out[b][h][:] = softmax(q[b][h] . K_b^T * softmax_scale) . V_b,
+ * where K_b, V_b are the dequantised first seq_len[b] tokens of the sequence's cache and
+ * q head h reads kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Passages this interface follows (page titles; section numbers as on the pages):
+ *   - "从 SGLang Kernel源码到 GPU Trace：DeepSeek V4.1 Flash-Decode", section 3.1: the decode
+ *     kernel's arguments -- q, uint8 k/v caches, output, per-sequence kv start index and
+ *     seq_len, max_seq_len (an upper bound used for sizing only; work follows seq_len),
+ *     num_heads, head_dim, block_size (32 or 64, chosen at run time), softmax_scale, batch.
+ *   - same page, sections 2.2 and 3.2: FP8 KV dequantised in the load stage of the kernel.
+ *   - "SGLang Prefill 性能优化：用 GPU Trace 剖析 FlashAttention 内核瓶颈", section 2.2: the
+ *     block-wise online-softmax recurrence (running max, running sum, rescaled accumulator).
+ *   - "第 15 章 · GPU Profiling 与 LLM 推理优化实战", section 15.26 (paged KV: physical page
+ *     = block_table[b * max_pages + logical_page], row ((page * page_size + slot) * H + h) * D),
+ *     15.11 (quantised KV with per-token k/v scales), 15.12 (GQA/MQA head groups),
+ *     15.13 (ragged batch: each sequence scans only its own length), 15.22 (no allocation on
+ *     the hot path: caller-owned workspace), 15.17 (no host synchronisation per step).
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees, copies to the host or synchronises; it enqueues kernels on `stream`
+ *     and returns.  Calls on different streams with different outputs/workspaces may overlap.
+ *   - Argument errors are detected on the host, before anything is launched, and reported
+ *     as an fd_status; nothing is written in that case.  Device-side contract violations
+ *     (see fd_decode_attention) are not detected.
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FD_VERSION 1
+
+typedef enum {
+    FD_OK = 0,
+    FD_ERR_INVALID_ARG = 1, /* null pointer, bad count, inconsistent dtype / scale mode      */
+    FD_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, block_size not 32/64, dtype combination   */
+    FD_ERR_WORKSPACE = 3,   /* workspace missing, too small or not 256-byte aligned           */
+    FD_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch                        */
+} fd_status;
+
+typedef enum {
+    FD_F32 = 0,      /* output only                                                       */
+    FD_F16 = 1,      /* IEEE binary16                                                     */
+    FD_BF16 = 2,     /* bfloat16                                                          */
+    FD_FP8_E4M3 = 3  /* OCP E4M3FN bytes (KV only): bias 7, no infinities, 0x7F/0xFF = NaN */
+} fd_dtype;
+
+typedef enum {
+    FD_SCALE_NONE = 0,           /* f16 / bf16 KV                                            */
+    FD_SCALE_PER_TENSOR = 1,     /* k_scale, v_scale each point at one fp32                  */
+    FD_SCALE_PER_TOKEN_HEAD = 2  /* one fp32 per (token row, kv head), laid out like the cache
+                                    rows: paged [num_blocks][block_size][num_kv_heads],
+                                    contiguous [rows][num_kv_heads]                           */
+} fd_scale_mode;
+
+/*
+ * fd_decode_attention -- one flash-decoding step (split-KV partition + log-sum-exp combine).
+ *
+ *   q            [batch][num_q_heads][head_dim], q_dtype (FD_F16 or FD_BF16), contiguous.
+ *   k_cache,     paged mode:      [num_blocks][block_size][num_kv_heads][head_dim]
+ *   v_cache      contiguous mode: [rows][num_kv_heads][head_dim]
+ *                element type kv_dtype.  With f16/bf16 KV, q_dtype must equal kv_dtype.
+ *                Each (row, kv head) vector must start 16-byte aligned (true for the layouts
+ *                above when the base pointers are 16-byte aligned).
+ *   block_table  [batch][max_blocks_per_seq] int32 physical block ids (paged mode), or NULL.
+ *   kv_start     [batch] int32 first row of each sequence (contiguous mode), or NULL.
+ *                Exactly one of block_table / kv_start must be given.
+ *   seq_len      [batch] int32, 0 <= seq_len[b] <= max_seq_len (device memory).
+ *   max_seq_len  host-side upper bound of seq_len; sizes the grid and the workspace only.
+ *                Paged mode needs max_seq_len <= max_blocks_per_seq * block_size.
+ *   block_size   32 or 64 in paged mode; ignored (pass 0) in contiguous mode.
+ *   scale_mode   FD_SCALE_NONE for f16/bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 KV.
+ *   k_scale,     fp32 dequantisation scales (value = decode(byte) * scale), NULL when none.
+ *   v_scale
+ *   softmax_scale  multiplies q . k (natural-exp softmax); usually 1/sqrt(head_dim).
+ *   out          [batch][num_q_heads][head_dim] in out_dtype (FD_F32, FD_F16 or FD_BF16).
+ *   lse          optional [batch][num_q_heads] fp32 natural-log sum of exp(scores); NULL = skip.
+ *                An empty sequence (seq_len 0) yields out = 0 and lse = -inf.
+ *   workspace    device scratch of at least fd_workspace_bytes(...) bytes, 256-byte aligned
+ *                (may be NULL when that size is 0).  Contents need no initialisation and are
+ *                clobbered; one workspace must not be shared by calls that may overlap.
+ *   num_splits   0 = automatic split of each sequence's KV range (sized for 256 CUs);
+ *                > 0 forces at most that many splits per sequence (testing and tuning).
+ *   stream       HIP stream to enqueue on (0 = null stream).
+ *
+ * Device-side contract (not checked; violating it is undefined): seq_len[b] <= max_seq_len,
+ * block_table entries for logical blocks < ceil(seq_len[b] / block_size) are valid block ids,
+ * kv_start[b] + seq_len[b] rows exist.  The kernels read only those entries and rows, so
+ * unused table entries and unused slots of a last block may hold anything.
+ *
+ * Returns FD_OK or an fd_status.
+ */
+int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_table, int max_blocks_per_seq,
+                        const int32_t *kv_start, const int32_t *seq_len,
+                        int batch, int max_seq_len,
+                        int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int kv_dtype, int q_dtype, int scale_mode,
+                        const float *k_scale, const float *v_scale,
+                        float softmax_scale,
+                        void *out, int out_dtype, float *lse,
+                        void *workspace, size_t workspace_bytes,
+                        int num_splits, hipStream_t stream);
+
+/*
+ * fd_workspace_bytes -- workspace size fd_decode_attention needs for these sizes (0 when no
+ * sequence can be split).  The same arguments must be passed to fd_decode_attention.
+ * Returns (size_t)-1 for arguments fd_decode_attention would reject as invalid.
+ */
+size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                          int max_seq_len, int block_size, int kv_dtype, int num_splits);
+
+/*
+ * fd_plan_splits -- the split plan fd_decode_attention will use for these sizes: returns the
+ * maximum number of splits per sequence and stores the split length in tokens (a multiple
+ * of 32) in *split_tokens when non-NULL.  Returns -1 for invalid sizes.  Host-only; for
+ * tests and tuning.
+ */
+int fd_plan_splits(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                   int max_seq_len, int block_size, int kv_dtype, int num_splits,
+                   int *split_tokens);
+
+/*
+ * fd_fp8_e4m3_decode -- diagnostic: decodes n E4M3 bytes with the exact hardware conversions the
+ * attention kernels use and writes out[2*i] = value via the f16 path, out[2*i+1] = value via the
+ * bf16 path (both fp32, [2*n]).  Format: OCP 8-bit floating point, E4M3 (as for fd_dtype).
+ * Device pointers; asynchronous on `stream`.  Returns FD_OK, FD_ERR_INVALID_ARG or FD_ERR_LAUNCH.
+ */
+int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
+
+/*
+ * fd_set_profile_events -- diagnostic timing hook.  While set (non-NULL), every later
+ * fd_decode_attention call made by the calling thread records `partition_begin` right before
+ * and `partition_end` right after its split-KV partition kernel, on that call's stream, so
+ * hipEventElapsedTime gives that kernel's duration.  Pass NULL, NULL to clear.  The events are
+ * owned by the caller.  Thread-local; returns FD_OK.
+ */
+int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end);
+
+/* fd_status_string -- static, NUL-terminated name of a status code (never NULL). */
+const char *fd_status_string(int status);
+
+/* fd_version -- FD_VERSION of the built library. */
+int fd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Bar (per KV type): max |gpu - oracle| over all output elements and relative L2 error
+||gpu - oracle|| / ||oracle|| must stay within 2e-3 / 1e-3 for f16/bf16 KV and 5e-3 / 3e-3 for
+E4M3 KV (the oracle dequantises the same bytes with the same scales).  Results are printed as
+``[case] PASS max_abs=... rel_l2=...`` lines.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_06_amd as fd
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3), "fp8_e4m3": (5e-3, 3e-3)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    fd.lib()
+    yield
+
+
+def compare(name, got, ref, kv_dtype, seqs=None):
+    got = got.detach().float().cpu().numpy().astype(np.float64)
+    if seqs is not None:
+        got, ref = got[list(seqs)], ref[list(seqs)]
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    err = got - ref
+    max_abs = float(np.max(np.abs(err))) if err.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel_l2 = float(np.linalg.norm(err) / nref) if nref > 0 else float(np.linalg.norm(err))
+    tol_abs, tol_rel = TOL[kv_dtype]
+    ok = max_abs <= tol_abs and rel_l2 <= tol_rel
+    print(f"[{name}] {'PASS' if ok else 'FAIL'} max_abs={max_abs:.3e} rel_l2={rel_l2:.3e}", flush=True)
+    assert ok, f"{name}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} (tol {tol_abs}, {tol_rel})"
+    return max_abs, rel_l2
+
+
+def run_gpu(case, **kw):
+    lse = torch.empty((case.batch, case.hq), dtype=torch.float32, device="cuda")
+    out = fd.decode_case(case, lse=lse, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_case(name, case, seqs=None, num_splits=0, out_dtype="f32"):
+    print(f"[{name}] lens={case.seq_lens[:8]}{'...' if case.batch > 8 else ''} G={case.group} "
+          f"D={case.d} kv={case.kv_dtype} scale={case.scale_mode} bs={case.block_size} "
+          f"splits={num_splits}", flush=True)
+    out, lse = run_gpu(case, num_splits=num_splits, out_dtype=out_dtype)
+    prob = oracle.Problem.from_case(case)
+    ref, ref_lse = oracle.decode_attention(prob, seqs=seqs)
+    compare(name, out, ref, case.kv_dtype, seqs)
+    lg = lse.cpu().numpy().astype(np.float64)
+    rl = ref_lse if seqs is None else ref_lse[list(seqs)]
+    lg = lg if seqs is None else lg[list(seqs)]
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lg)), f"{name}: lse finiteness differs"
+    if fin.any():
+        assert np.max(np.abs(lg[fin] - rl[fin])) < 1e-3, f"{name}: lse mismatch"
+    return out
+
+
+# ------------------------------------------------------------------ E4M3 conversion
+def test_fp8_hardware_decode_matches_format_definition():
+    allb = torch.arange(256, dtype=torch.uint8, device="cuda")
+    got = fd.fp8_e4m3_decode(allb).cpu().numpy()
+    for byte in range(256):
+        ref = oracle.e4m3_to_double(byte)
+        for col in range(2):
+            if math.isnan(ref):
+                assert math.isnan(got[byte, col]), (hex(byte), col)
+            else:
+                assert got[byte, col] == ref, (hex(byte), col, got[byte, col], ref)
+
+
+# ------------------------------------------------------------------ small shapes
+SMALL = [
+    # name, kwargs for workloads.custom_case
+    ("mqa_f16_d64_contig", dict(batch=2, hq=4, hkv=1, d=64, seq_lens=[37, 100], kv="f16", q="f16",
+                                scale="none", paged=False, block_size=0)),
+    ("gqa4_bf16_d128", dict(batch=3, hq=8, hkv=2, d=128, seq_lens=[1, 100, 777], kv="bf16", q="bf16",
+                            scale="none", block_size=64)),
+    ("gqa8_fp8_tok", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[65, 1500, 31], kv="fp8_e4m3",
+                          q="bf16", scale="token_head", block_size=64)),
+    ("gqa8_fp8_tok_f16q", dict(batch=2, hq=8, hkv=1, d=128, seq_lens=[300, 64], kv="fp8_e4m3",
+                               q="f16", scale="token_head", block_size=32)),
+    ("mqa128_fp8_tensor", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[2049, 333], kv="fp8_e4m3",
+                               q="bf16", scale="tensor", block_size=64)),
+    ("g32_fp8_tensor_d64", dict(batch=2, hq=32, hkv=1, d=64, seq_lens=[513, 7], kv="fp8_e4m3",
+                                q="bf16", scale="tensor", block_size=32)),
+    ("mha_f16_d64_paged", dict(batch=2, hq=4, hkv=4, d=64, seq_lens=[33, 250], kv="f16", q="f16",
+                               scale="none", block_size=32)),
+    ("g16_bf16_d64", dict(batch=2, hq=16, hkv=1, d=64, seq_lens=[95, 64], kv="bf16", q="bf16",
+                          scale="none", block_size=64)),
+    ("g4_fp8_tok_d64_contig", dict(batch=3, hq=8, hkv=2, d=64, seq_lens=[40, 1, 129], kv="fp8_e4m3",
+                                   q="bf16", scale="token_head", paged=False, block_size=0)),
+    ("g2_fp8_tok_bs32", dict(batch=2, hq=4, hkv=2, d=128, seq_lens=[1000, 2], kv="fp8_e4m3", q="bf16",
+                             scale="token_head", block_size=32)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("splits", [0, 1, 2, 7])
+def test_small_shapes(name, kw, splits):
+    case = workloads.custom_case(seed=3, device="cuda", **kw)
+    check_case(f"{name}/s{splits}", case, num_splits=splits)
+
+
+@pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 4095])
+def test_length_edges(n):
+    lens = [n, 5, n]
+    case = workloads.custom_case(seed=n, device="cuda", batch=3, hq=16, hkv=2, d=128, seq_lens=lens,
+                                 kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64,
+                                 max_seq_len=max(lens + [1]))
+    for splits in (0, 3):
+        check_case(f"len{n}/s{splits}", case, num_splits=splits)
+
+
+def test_max_splits_one_tile_each():
+    case = workloads.custom_case(seed=9, device="cuda", batch=2, hq=8, hkv=1, d=128,
+                                 seq_lens=[32 * 40 + 3, 200], kv="fp8_e4m3", q="bf16",
+                                 scale="token_head", block_size=64)
+    nmax = -(-case.max_seq_len // 32)
+    check_case("maxsplits", case, num_splits=nmax)
+
+
+def test_peaky_scores():
+    case = workloads.custom_case(seed=10, device="cuda", batch=2, hq=16, hkv=2, d=128,
+                                 seq_lens=[3000, 700], kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=64)
+    case.q.mul_(4.0)
+    check_case("peaky_q4", case, num_splits=0)
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
+def test_half_outputs_are_rounded_f32(out_dtype):
+    case = workloads.custom_case(seed=11, device="cuda", batch=2, hq=16, hkv=2, d=128,
+                                 seq_lens=[900, 3], kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=64)
+    o32, _ = run_gpu(case, out_dtype="f32")
+    oh, _ = run_gpu(case, out_dtype=out_dtype)
+    ref = o32.to({"f16": torch.float16, "bf16": torch.bfloat16}[out_dtype])
+    assert torch.equal(oh, ref)
+
+
+# ------------------------------------------------------------------ properties
+def test_run_to_run_bitwise_deterministic():
+    case = workloads.make_case("fp8_32k", seed=1, device="cuda", batch=4)
+    a, la = run_gpu(case)
+    b, lb = run_gpu(case)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_block_placement_bitwise_invariant():
+    case = workloads.custom_case(seed=12, device="cuda", batch=3, hq=16, hkv=2, d=128,
+                                 seq_lens=[1000, 64, 333], kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=64)
+    a, _ = run_gpu(case)
+    # move every block to a new physical slot and rewrite the table
+    nb = case.k_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(4)).cuda()
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(nb, device="cuda")
+    k2, v2 = torch.empty_like(case.k_cache), torch.empty_like(case.v_cache)
+    k2[perm] = case.k_cache
+    v2[perm] = case.v_cache
+    ks2, vs2 = torch.empty_like(case.k_scale), torch.empty_like(case.v_scale)
+    ks2[perm] = case.k_scale
+    vs2[perm] = case.v_scale
+    bt = case.block_table.clone()
+    live = bt >= 0
+    bt[live] = perm[bt[live].long()].int()
+    case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table = k2, v2, ks2, vs2, bt
+    b, _ = run_gpu(case)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ full-size workloads
+def test_workload_tiny_mqa_f16():
+    check_case("tiny_mqa_f16", workloads.make_case("tiny_mqa_f16", device="cuda"))
+
+
+def test_workload_gqa_bf16_full():
+    check_case("gqa_bf16", workloads.make_case("gqa_bf16", device="cuda"))
+
+
+def test_workload_fp8_32k_full():
+    check_case("fp8_32k", workloads.make_case("fp8_32k", device="cuda"))
+
+
+def test_workload_mqa_fp8_128k_sampled():
+    case = workloads.make_case("mqa_fp8_128k", device="cuda")
+    check_case("mqa_fp8_128k[seq 0,3]", case, seqs=[0, 3])
+
+
+def test_workload_ragged_fp8_sampled():
+    case = workloads.make_case("ragged_fp8", device="cuda")
+    longs = [i for i, n in enumerate(case.seq_lens) if n >= 32768][:2]
+    shorts = [i for i, n in enumerate(case.seq_lens) if n < 32768][:6]
+    check_case("ragged_fp8[sampled]", case, seqs=longs + shorts)
