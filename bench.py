@@ -119,6 +119,10 @@ def main():
     # ---- partition-kernel durations from HIP events recorded around it, on its stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for a, b in evs:  # create the underlying HIP events (torch creates them on first record)
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
     for i in range(args.steps):
         fd.set_profile_events(*evs[i])
         step(i)
