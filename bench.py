@@ -1,6 +1,6 @@
 """Benchmark: one flash-decoding step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fp8_32k] [--num-splits 0]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fp8_32k] [--num-partitions 0]
 
 Prints ONE JSON line.  A step is one fd_decode_attention call (split-KV partition kernel +
 combine kernel) over one batch of synthetic, seeded inputs already resident in HBM.  Each step
@@ -55,7 +55,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_32k")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--num-partitions", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="KV copies rotated across steps (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -90,15 +90,15 @@ def main():
     out = torch.empty((case.batch, case.hq, case.d), dtype=torch.float32, device=dev)
     lse = torch.empty((case.batch, case.hq), dtype=torch.float32, device=dev)
     wsb = fd.workspace_bytes(case.batch, case.hq, case.hkv, case.d, case.max_seq_len, case.block_size,
-                             case.kv_dtype, args.num_splits)
+                             case.kv_dtype, args.num_partitions)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    nsplit, split_tokens = fd.plan_splits(case.batch, case.hq, case.hkv, case.d, case.max_seq_len,
-                                          case.block_size, case.kv_dtype, args.num_splits)
+    nparts = fd.plan_partitions(case.batch, case.hq, case.hkv, case.d, case.max_seq_len,
+                                case.block_size, case.kv_dtype, args.num_partitions)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
-        fd.decode_case(copies[i % ncopy], out=out, lse=lse, workspace=ws, num_splits=args.num_splits,
-                       stream=stream.cuda_stream)
+        fd.decode_case(copies[i % ncopy], out=out, lse=lse, workspace=ws,
+                       num_partitions=args.num_partitions, stream=stream.cuda_stream)
 
     for i in range(args.warmup):
         step(i)
@@ -153,7 +153,7 @@ def main():
             "num_kv_heads": case.hkv, "head_dim": case.d, "kv_dtype": case.kv_dtype,
             "q_dtype": case.q_dtype, "scale_mode": case.scale_mode, "block_size": case.block_size,
             "tokens": int(sum(case.seq_lens)), "max_seq_len": case.max_seq_len,
-            "kv_read_bytes": kv_bytes, "num_splits": nsplit, "split_tokens": split_tokens,
+            "kv_read_bytes": kv_bytes, "partitions": nparts,
             "kv_copies_rotated": ncopy, "seed": args.seed,
             "compute": "E4M3/bf16 K -> bf16 MFMA q.k, f16 MFMA p.v, f32 softmax and accumulate",
             "parallelism": "single GPU",

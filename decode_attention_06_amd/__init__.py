@@ -19,7 +19,7 @@ FD_SCALE_NONE, FD_SCALE_PER_TENSOR, FD_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 
 DTYPE_CODES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8_e4m3": FD_FP8_E4M3}
 SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head": FD_SCALE_PER_TOKEN_HEAD}
-EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_splits", "fd_status_string",
+EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
            "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events")
 
 _lock = threading.Lock()
@@ -53,8 +53,8 @@ def lib() -> ctypes.CDLL:
                                           i32, vp]
         L.fd_workspace_bytes.restype = sz
         L.fd_workspace_bytes.argtypes = [i32] * 8
-        L.fd_plan_splits.restype = i32
-        L.fd_plan_splits.argtypes = [i32] * 8 + [ctypes.POINTER(i32)]
+        L.fd_plan_partitions.restype = i32
+        L.fd_plan_partitions.argtypes = [i32] * 8
         L.fd_status_string.restype = ctypes.c_char_p
         L.fd_status_string.argtypes = [i32]
         L.fd_version.restype = i32
@@ -76,35 +76,34 @@ def version() -> int:
 
 
 def workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0,
-                    kv_dtype="fp8_e4m3", num_splits=0) -> int:
+                    kv_dtype="fp8_e4m3", num_partitions=0) -> int:
     n = lib().fd_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                 block_size, DTYPE_CODES.get(kv_dtype, kv_dtype), num_splits)
+                                 block_size, DTYPE_CODES.get(kv_dtype, kv_dtype), num_partitions)
     if n == ctypes.c_size_t(-1).value:
         raise FdError(FD_ERR_INVALID_ARG, "fd_workspace_bytes")
     return n
 
 
-def plan_splits(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0,
-                kv_dtype="fp8_e4m3", num_splits=0):
-    """(max splits per sequence, split length in tokens) the library will use."""
-    st = ctypes.c_int(0)
-    n = lib().fd_plan_splits(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
-                             DTYPE_CODES.get(kv_dtype, kv_dtype), num_splits, ctypes.byref(st))
+def plan_partitions(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0,
+                    kv_dtype="fp8_e4m3", num_partitions=0) -> int:
+    """Number of partitions (partition-kernel waves) the library will use."""
+    n = lib().fd_plan_partitions(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
+                                 DTYPE_CODES.get(kv_dtype, kv_dtype), num_partitions)
     if n < 0:
-        raise FdError(FD_ERR_INVALID_ARG, "fd_plan_splits")
-    return n, st.value
+        raise FdError(FD_ERR_INVALID_ARG, "fd_plan_partitions")
+    return n
 
 
 def decode_attention_raw(q, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start, seq_len,
                          batch, max_seq_len, num_q_heads, num_kv_heads, head_dim, block_size,
                          kv_dtype, q_dtype, scale_mode, k_scale, v_scale, softmax_scale, out,
-                         out_dtype, lse, workspace, workspace_bytes_, num_splits, stream) -> int:
+                         out_dtype, lse, workspace, workspace_bytes_, num_partitions, stream) -> int:
     """Direct call of fd_decode_attention with integer pointers/codes; returns the status."""
     return lib().fd_decode_attention(q, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start,
                                      seq_len, batch, max_seq_len, num_q_heads, num_kv_heads, head_dim,
                                      block_size, kv_dtype, q_dtype, scale_mode, k_scale, v_scale,
                                      ctypes.c_float(softmax_scale), out, out_dtype, lse, workspace,
-                                     workspace_bytes_, num_splits, stream)
+                                     workspace_bytes_, num_partitions, stream)
 
 
 def _ptr(t):
@@ -121,7 +120,7 @@ def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_ta
                      kv_start=None, kv_dtype: str, scale_mode: str = "none", k_scale=None,
                      v_scale=None, softmax_scale: float, num_kv_heads: int | None = None,
                      block_size: int = 0, out=None, out_dtype: str = "f32", lse=None,
-                     workspace=None, num_splits: int = 0, stream=None):
+                     workspace=None, num_partitions: int = 0, stream=None):
     """One decode step on the GPU.  Shapes follow ``include/fd.h``; sizes are read from the
     tensors.  ``out``/``workspace`` are allocated with torch when not given (pass them in to
     keep the call allocation-free).  Returns ``out``."""
@@ -139,8 +138,8 @@ def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_ta
         out = torch.empty((batch, hq, d), dtype={"f32": torch.float32, "f16": torch.float16,
                                                  "bf16": torch.bfloat16}[out_dtype], device=q.device)
     max_blocks = 0 if block_table is None else block_table.shape[1]
-    need = workspace_bytes(batch, hq, hkv, d, max_seq_len, block_size, kv_dtype, num_splits)
-    if workspace is None and need:
+    need = workspace_bytes(batch, hq, hkv, d, max_seq_len, block_size, kv_dtype, num_partitions)
+    if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
@@ -149,13 +148,13 @@ def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_ta
                               _ptr(kv_start), _ptr(seq_len), batch, max_seq_len, hq, hkv, d,
                               block_size, kv_code, q_code, SCALE_CODES[scale_mode], _ptr(k_scale),
                               _ptr(v_scale), float(softmax_scale), _ptr(out), out_code, _ptr(lse),
-                              _ptr(workspace), ws_bytes, num_splits, stream)
+                              _ptr(workspace), ws_bytes, num_partitions, stream)
     if st != FD_OK:
         raise FdError(st)
     return out
 
 
-def decode_case(case, *, out=None, out_dtype="f32", lse=None, workspace=None, num_splits=0,
+def decode_case(case, *, out=None, out_dtype="f32", lse=None, workspace=None, num_partitions=0,
                 stream=None):
     """Convenience: run one ``workloads.Case`` (duck-typed) through the library."""
     return decode_attention(case.q, case.k_cache, case.v_cache, case.seq_len,
@@ -164,7 +163,7 @@ def decode_case(case, *, out=None, out_dtype="f32", lse=None, workspace=None, nu
                             scale_mode=case.scale_mode, k_scale=case.k_scale, v_scale=case.v_scale,
                             softmax_scale=case.softmax_scale, num_kv_heads=case.hkv,
                             block_size=case.block_size, out=out, out_dtype=out_dtype, lse=lse,
-                            workspace=workspace, num_splits=num_splits, stream=stream)
+                            workspace=workspace, num_partitions=num_partitions, stream=stream)
 
 
 def fp8_e4m3_decode(x, stream=None):

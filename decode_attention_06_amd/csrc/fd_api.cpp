@@ -11,9 +11,10 @@
 
 namespace {
 
-constexpr int kMinSplit = 256;     // tokens: keeps partial-state traffic small next to KV bytes
-constexpr int kMaxSplit = 4096;    // tokens: keeps enough waves in flight for short batches
-constexpr long kTargetWaves = 8192;  // ~32 waves per CU on 256 CUs when every sequence is full
+// Partition-kernel waves per step: 8 per CU on 256 CUs (two per SIMD), all resident at once,
+// each workgroup of `wpg` waves with an equal share of the step's KV tiles.
+constexpr long kDefaultWaves = 2048;
+constexpr int kMaxSeqLen = 1 << 24;
 
 thread_local hipEvent_t t_prof_begin = nullptr, t_prof_end = nullptr;
 
@@ -21,46 +22,43 @@ inline long cdiv(long a, long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-    int nhb;
-    int split_tokens;
-    int nsplit;
+    int nhb;     // head blocks per kv head
+    int wpg;     // waves per partition workgroup (units processed side by side)
+    int groups;  // unit groups per sequence
+    int nparts;  // partition workgroups
 };
 
 bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
     if (batch <= 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0) return false;
     if (hq % hkv) return false;
-    if (batch > 65535) return false;
+    if (batch > 65535 || max_seq_len > kMaxSeqLen) return false;
     (void)head_dim;
     return true;
 }
 
-// Split plan.  Each (sequence, kv head, head block) is a stream of waves; the KV range of a
-// sequence is cut into `nsplit` ranges of `split_tokens` tokens so that a batch of full-length
-// sequences yields about kTargetWaves waves, within [kMinSplit, kMaxSplit] tokens per split.
-Plan make_plan(int batch, int hq, int hkv, int max_seq_len, int num_splits) {
+// Units per sequence (kv head x head block) are grouped `wpg` at a time, wpg the largest
+// divisor of their count up to 8; workgroup w of the partition kernel takes tiles
+// [w*q + min(w, r), ...) of the concatenation of all unit groups (TT tiles of 32 tokens).
+// The workgroup count is capped by the largest TT the sizes allow.
+Plan make_plan(int batch, int hq, int hkv, int max_seq_len, int num_partitions) {
     Plan pl;
     const int group = hq / hkv;
     pl.nhb = (int)cdiv(group, fd::kHeadBlock);
-    const long units = (long)batch * hkv * pl.nhb;
-    long S;
-    if (max_seq_len <= 0) {
-        S = fd::kTile;
-    } else if (num_splits > 0) {
-        S = cdiv(cdiv(max_seq_len, num_splits), fd::kTile) * fd::kTile;
-    } else {
-        S = cdiv((long)max_seq_len * units, kTargetWaves);
-        S = cdiv(S, fd::kTile) * fd::kTile;
-        if (S < kMinSplit) S = kMinSplit;
-        if (S > kMaxSplit) S = kMaxSplit;
-    }
-    pl.split_tokens = (int)S;
-    pl.nsplit = max_seq_len <= 0 ? 1 : (int)cdiv(max_seq_len, S);
+    const long ups = (long)hkv * pl.nhb;
+    pl.wpg = 1;
+    for (int d = fd::kMaxWavesPerGroup; d >= 1; d--)
+        if (ups % d == 0) { pl.wpg = d; break; }
+    pl.groups = (int)(ups / pl.wpg);
+    const long tt_max = (long)batch * pl.groups * cdiv(max_seq_len, fd::kTile);
+    long W = num_partitions > 0 ? num_partitions : kDefaultWaves / pl.wpg;
+    if (W > tt_max) W = tt_max;
+    if (W < 1) W = 1;
+    pl.nparts = (int)W;
     return pl;
 }
 
-size_t ws_bytes(const Plan &pl, int batch, int hq, int head_dim) {
-    if (pl.nsplit <= 1) return 0;
-    const size_t slots = (size_t)batch * hq * pl.nsplit;
+size_t ws_bytes(const Plan &pl, int head_dim) {
+    const size_t slots = (size_t)pl.nparts * 2 * pl.wpg * fd::kHeadBlock;
     return align256(slots * sizeof(float) * 2) + slots * head_dim * sizeof(float);
 }
 
@@ -81,24 +79,22 @@ const char *fd_status_string(int status) {
     }
 }
 
-int fd_plan_splits(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
-                   int block_size, int kv_dtype, int num_splits, int *split_tokens) {
+int fd_plan_partitions(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                       int block_size, int kv_dtype, int num_partitions) {
     (void)block_size;
     (void)kv_dtype;
-    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_splits < 0) return -1;
-    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits);
-    if (split_tokens) *split_tokens = pl.split_tokens;
-    return pl.nsplit;
+    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_partitions < 0) return -1;
+    return make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_partitions).nparts;
 }
 
 size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
-                          int block_size, int kv_dtype, int num_splits) {
+                          int block_size, int kv_dtype, int num_partitions) {
     (void)block_size;
     (void)kv_dtype;
-    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_splits < 0)
+    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_partitions < 0)
         return (size_t)-1;
-    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits);
-    return ws_bytes(pl, batch, num_q_heads, head_dim);
+    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_partitions);
+    return ws_bytes(pl, head_dim);
 }
 
 int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
@@ -111,11 +107,11 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
                         float softmax_scale,
                         void *out, int out_dtype, float *lse,
                         void *workspace, size_t workspace_bytes,
-                        int num_splits, hipStream_t stream) {
+                        int num_partitions, hipStream_t stream) {
     // ---- argument validation (host only, nothing launched on failure)
     if (!q || !k_cache || !v_cache || !seq_len || !out) return FD_ERR_INVALID_ARG;
     if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len)) return FD_ERR_INVALID_ARG;
-    if (num_splits < 0) return FD_ERR_INVALID_ARG;
+    if (num_partitions < 0) return FD_ERR_INVALID_ARG;
     if ((block_table == nullptr) == (kv_start == nullptr)) return FD_ERR_INVALID_ARG;
     if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
     if (q_dtype != FD_F16 && q_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
@@ -134,13 +130,10 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
         if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
         if ((long)max_seq_len > (long)max_blocks_per_seq * block_size) return FD_ERR_INVALID_ARG;
     }
-    const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits);
-    if ((long)num_kv_heads * pl.nhb > 65535) return FD_ERR_UNSUPPORTED;
-    const size_t need = ws_bytes(pl, batch, num_q_heads, head_dim);
-    if (need) {
-        if (!workspace || workspace_bytes < need) return FD_ERR_WORKSPACE;
-        if ((uintptr_t)workspace & 255) return FD_ERR_WORKSPACE;
-    }
+    const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_partitions);
+    const size_t need = ws_bytes(pl, head_dim);
+    if (!workspace || workspace_bytes < need) return FD_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255) return FD_ERR_WORKSPACE;
 
     fd::Params p;
     memset(&p, 0, sizeof(p));
@@ -163,12 +156,13 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     p.max_seq_len = max_seq_len;
     p.group = num_q_heads / num_kv_heads;
     p.nhb = pl.nhb;
-    p.split_tokens = pl.split_tokens;
-    p.nsplit = pl.nsplit;
+    p.wpg = pl.wpg;
+    p.groups = pl.groups;
+    p.nparts = pl.nparts;
     p.out_dtype = out_dtype;
     p.qk_scale = (float)((double)softmax_scale * 1.4426950408889634074);  // log2(e)
-    if (need) {
-        const size_t slots = (size_t)batch * num_q_heads * pl.nsplit;
+    {
+        const size_t slots = (size_t)pl.nparts * 2 * pl.wpg * fd::kHeadBlock;
         p.ws_ml = (float2 *)workspace;
         p.ws_acc = (float *)((char *)workspace + align256(slots * sizeof(float) * 2));
     }
@@ -176,7 +170,7 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     if (t_prof_begin) (void)hipEventRecord(t_prof_begin, stream);
     if (fd::launch_partition(p, kv_dtype, q_dtype, scale_mode, stream) != hipSuccess) return FD_ERR_LAUNCH;
     if (t_prof_end) (void)hipEventRecord(t_prof_end, stream);
-    if (pl.nsplit > 1 && fd::launch_combine(p, stream) != hipSuccess) return FD_ERR_LAUNCH;
+    if (fd::launch_combine(p, stream) != hipSuccess) return FD_ERR_LAUNCH;
     return FD_OK;
 }
 

@@ -10,6 +10,8 @@ namespace fd {
 constexpr int kTile = 32;
 // Heads per MFMA column block (a GQA group wider than this takes several head blocks).
 constexpr int kHeadBlock = 16;
+// Most waves (units of one sequence) a partition workgroup runs side by side.
+constexpr int kMaxWavesPerGroup = 8;
 
 struct Params {
     const void *q;
@@ -22,15 +24,16 @@ struct Params {
     const float *v_scale;
     void *out;
     float *lse;
-    float *ws_acc;   // [batch][hq][nsplit][d]   unnormalised partial outputs
-    float2 *ws_ml;   // [batch][hq][nsplit]      (running max in log2 units, running sum)
+    float *ws_acc;   // [nparts][2][wpg][kHeadBlock][d]  unnormalised partial outputs
+    float2 *ws_ml;   // [nparts][2][wpg][kHeadBlock]     (running max in log2 units, running sum)
     int batch, hq, hkv, d;
     int block_size, max_blocks;
     int max_seq_len;  // host bound; seq_len values above it are clamped (never read past it)
     int group;        // hq / hkv
     int nhb;          // head blocks per kv head: ceil(group / kHeadBlock)
-    int split_tokens; // tokens per split, multiple of kTile
-    int nsplit;       // maximum splits per sequence
+    int wpg;          // waves per partition workgroup = units per unit group (divides hkv*nhb)
+    int groups;       // unit groups per sequence: hkv * nhb / wpg
+    int nparts;       // partition workgroups (equal shares of the step's tiles)
     int out_dtype;
     float qk_scale;   // softmax_scale * log2(e): scores are kept in log2 units
 };

@@ -132,58 +132,199 @@ __device__ __forceinline__ void store_row_chunk(void *out, int out_dtype, size_t
     }
 }
 
-// ---------------------------------------------------------------- split-KV partition kernel
+// ---------------------------------------------------------------- work split helpers
 //
-// Grid: x = split, y = kv_head * nhb + head_block, z = sequence.  Block: one wave (64 lanes).
-// Computes the unnormalised softmax state of the split's tokens [split*S, min(n, (split+1)*S))
-// for up to 16 query heads sharing one kv head, then writes either the final output (the
-// sequence has a single split) or the partial state (m, l, acc) to the workspace.
-template <int D, int KVT, int QT, int SCALE, bool PAGED>
-__global__ __launch_bounds__(64) void partition_kernel(Params p) {
-    constexpr int EB = (KVT == KV_FP8) ? 1 : 2;       // bytes per KV element
-    constexpr int E = 16 / EB;                        // elements per 16-byte load
-    constexpr int KSTEPS = D / 32;                    // MFMA k-steps of q.k^T
-    constexpr int KLOADS = (D / 4) / E;               // 16-byte K loads per lane per 16-token half
-    constexpr int DT = D / 16;                        // d-tiles of p.V == elements per V chunk
-    constexpr int VDW = (DT * EB) / 4;                // dwords per V chunk (1, 2 or 4)
+// Balanced split of one step's KV work.  A *unit* is (sequence b, kv head, head block): the
+// G <= 16 query heads of one head block that share one kv head.  The units of a sequence are
+// taken in groups of `wpg` by the `wpg` waves of one workgroup (wave i takes unit grp*wpg + i),
+// so the waves of a workgroup stream the same token rows of the cache at the same time.
+// Unit group (b, grp) owns T_b = ceil(seq_len[b] / 32) tiles; groups are concatenated
+// sequence-major into TT tiles, and workgroup w of W takes tiles [lo_w, lo_{w+1}) with
+// lo_w = w*q + min(w, r), q = TT / W, r = TT % W: every workgroup gets the same amount of KV
+// (up to one tile) whatever the length mix.  A group cut by workgroup boundaries leaves one
+// partial state per piece: slot 0 of a workgroup holds its first piece, slot 1 its last one.
 
-    const int lane = threadIdx.x;
-    const int c = lane & 15, g = lane >> 4;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y / p.nhb, hb = blockIdx.y % p.nhb;
-    const int b = blockIdx.z;
-    const int S = p.split_tokens;
-
+__device__ __forceinline__ int seq_tiles(const Params &p, int b) {
     int n = p.seq_len[b];
     n = max(0, min(n, p.max_seq_len));
-    const int nsp = (n + S - 1) / S;
-    const int hloc = hb * kHeadBlock + c;
-    const bool hvalid = hloc < p.group;
-    const int h = kvh * p.group + hloc;
-    const size_t orow = ((size_t)b * p.hq + h) * D;     // output row of head h
+    return (n + kTile - 1) / kTile;
+}
 
-    const int t_begin = split * S;
-    if (t_begin >= n) {
-        if (split == 0 && hvalid) {  // empty sequence: out = 0, lse = -inf
-            float z[DT];
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
-            for (int i = 0; i < DT; i++) z[i] = 0.0f;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+struct Split {
+    int64_t q, r;
+};
+
+__device__ __forceinline__ Split make_split(int64_t TT, int64_t W) { return Split{TT / W, TT % W}; }
+
+__device__ __forceinline__ int64_t split_lo(const Split &s, int64_t w) { return w * s.q + min(w, s.r); }
+
+// Workgroup whose range holds tile t (0 <= t < TT).
+__device__ __forceinline__ int64_t split_owner(const Split &s, int64_t t) {
+    const int64_t big = s.r * (s.q + 1);
+    return t < big ? t / (s.q + 1) : s.r + (t - big) / s.q;
+}
+
+// Total tiles over all sequences (one unit group each); every lane gets the same value.
+__device__ __forceinline__ int64_t total_seq_tiles(const Params &p, int lane) {
+    int64_t tot = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        int t = b < p.batch ? seq_tiles(p, b) : 0;
 #pragma unroll
-            for (int r = 0; r < 4; r++) store_row_chunk<DT>(p.out, p.out_dtype, orow + DT * (4 * g + r), z);
-            if (p.lse && g == 0) p.lse[(size_t)b * p.hq + h] = -INFINITY;
+        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+        tot += t;
+    }
+    return tot;
+}
+
+// Tiles of the sequences before b; every lane gets the same value.
+__device__ __forceinline__ int64_t tiles_before(const Params &p, int b, int lane) {
+    int64_t tot = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+        int t = (b0 + lane < b) ? seq_tiles(p, b0 + lane) : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+        tot += t;
+    }
+    return tot;
+}
+
+// ---------------------------------------------------------------- split-KV partition kernel
+//
+// Grid: W waves (one 64-lane workgroup each).  Each wave walks its tile range unit by unit
+// ("segments"): for each segment it computes the unnormalised softmax state of the segment's
+// tokens for the head block's heads and writes either the final output (whole unit) or a
+// partial state (m, l, acc) to its workspace slot.
+//
+// Per 32-token tile a lane loads: K -- 16 bytes x KLOADS from each of its two token rows
+// (16*half + c); V -- one DT-element chunk of each of its 8 token rows pv_token(g, j); and, with
+// per-(token, head) scales, one fp32 scale (lane 16g+i holds the k (i < 8) or v (i >= 8) scale
+// of token pv_token(g, i & 7)), shared through LDS.  The next tile's loads are issued before the
+// current tile is computed (two register sets, used alternately).
+
+template <int D, int KVT>
+struct Geometry {
+    static constexpr int EB = (KVT == KV_FP8) ? 1 : 2;  // bytes per KV element
+    static constexpr int E = 16 / EB;                   // elements per 16-byte load
+    static constexpr int KSTEPS = D / 32;               // MFMA k-steps of q.k^T
+    static constexpr int KLOADS = (D / 4) / E;          // 16-byte K loads per lane per 16-token half
+    static constexpr int DT = D / 16;                   // d-tiles of p.V == elements per V chunk
+    static constexpr int VDW = (DT * EB) / 4;           // dwords per V chunk (1, 2 or 4)
+};
+
+template <int KLOADS, int VDW>
+struct TileRaw {
+    u32x4_t k[2][KLOADS];
+    uint32_t v[8][VDW];
+    float sc;
+};
+
+// Byte offsets of a lane's loads relative to the tile's first row of its kv head.
+template <int KLOADS>
+struct LaneOffsets {
+    uint32_t k[2][KLOADS];
+    uint32_t v[8];
+    uint32_t s;  // in floats, relative to the tile's first row of the scale array
+};
+
+template <int D, int KVT>
+__device__ __forceinline__ void lane_offsets(LaneOffsets<Geometry<D, KVT>::KLOADS> &o, int g, int c,
+                                             uint32_t row_bytes, int hkv, int last) {
+    using G = Geometry<D, KVT>;
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+        const uint32_t tok = (uint32_t)min(16 * half + c, last);
+#pragma unroll
+        for (int L = 0; L < G::KLOADS; L++)
+            o.k[half][L] = tok * row_bytes + (uint32_t)(4 * G::E * L + G::E * g) * G::EB;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        o.v[j] = (uint32_t)min(pv_token(g, j), last) * row_bytes + (uint32_t)(G::DT * c * G::EB);
+    o.s = (uint32_t)min(pv_token(g, c & 7), last) * (uint32_t)hkv;
+}
+
+template <int D, int KVT, int SCALE>
+__device__ __forceinline__ void load_tile(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
+                                          const uint8_t *kt, const uint8_t *vt, const float *st,
+                                          const LaneOffsets<Geometry<D, KVT>::KLOADS> &o) {
+    using G = Geometry<D, KVT>;
+#pragma unroll
+    for (int half = 0; half < 2; half++)
+#pragma unroll
+        for (int L = 0; L < G::KLOADS; L++) r.k[half][L] = *(const u32x4_t *)(kt + o.k[half][L]);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint8_t *src = vt + o.v[j];
+        if constexpr (G::VDW == 4) {
+            const u32x4_t x = *(const u32x4_t *)src;
+            r.v[j][0] = x[0]; r.v[j][1] = x[1]; r.v[j][2] = x[2]; r.v[j][3] = x[3];
+        } else if constexpr (G::VDW == 2) {
+            const u32x2_t x = *(const u32x2_t *)src;
+            r.v[j][0] = x[0]; r.v[j][1] = x[1];
+        } else {
+            r.v[j][0] = *(const uint32_t *)src;
         }
-        return;
     }
-    const int t_end = min(n, t_begin + S);
+    if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[o.s];
+}
 
-    // q operand (B of q.k^T): column c = head hloc, k-slots of lane group g.
-    u32x4_t qop[KSTEPS];
+template <int D, int KVT, int QT, int SCALE, bool PAGED>
+__global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
+void partition_kernel(Params p) {
+    using G = Geometry<D, KVT>;
+    constexpr int EB = G::EB, E = G::E, KSTEPS = G::KSTEPS, KLOADS = G::KLOADS, DT = G::DT, VDW = G::VDW;
+    __shared__ float sh_scale_all[kMaxWavesPerGroup][64];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float *sh_scale = sh_scale_all[wave];
+    const int c = lane & 15, g = lane >> 4;
+    const int64_t wg = blockIdx.x, W = gridDim.x;
+    const int groups = p.groups;  // unit groups per sequence
+
+    // ---- this workgroup's tile range [lo, hi) in the concatenation of all unit groups
+    const int64_t TT = total_seq_tiles(p, lane) * groups;
+    const Split sp = make_split(TT, W);
+    const int64_t lo = split_lo(sp, wg), hi = split_lo(sp, wg + 1);
+    if (lo >= hi) return;
+
+    // ---- locate lo: sequence b with P_b * groups <= lo < (P_b + T_b) * groups
+    int b = 0, Tb = 0;
+    int64_t Pb = 0;
     {
-        const uint16_t *qrow = (const uint16_t *)p.q + orow;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; kk++)
-            qop[kk] = hvalid ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
+        int64_t base = 0;
+        for (int b0 = 0; b0 < p.batch; b0 += 64) {
+            const int bb = b0 + lane;
+            const int t = bb < p.batch ? seq_tiles(p, bb) : 0;
+            const int incl = wave_incl_scan(t, lane);
+            const int64_t excl = base + incl - t;
+            const bool here = t > 0 && excl * groups <= lo && (excl + t) * groups > lo;
+            const uint64_t mask = __ballot(here);
+            if (mask) {
+                const int src = __builtin_ctzll(mask);
+                b = b0 + src;
+                Tb = __shfl(t, src, 64);
+                Pb = base + __shfl(incl, src, 64) - Tb;
+                break;
+            }
+            base += __shfl(incl, 63, 64);
+        }
     }
+    if (Tb == 0) return;  // unreachable: some sequence owns tile lo
+    const int64_t rel = lo - Pb * groups;
+    int grp = (int)(rel / Tb);     // unit group within the sequence
+    int t_off = (int)(rel % Tb);   // first tile of the segment within the unit
+    int64_t pos = lo;
+    int seg_index = 0;
 
     float tensor_k = 1.0f, tensor_v = 1.0f;
     if constexpr (SCALE == SC_TENSOR) {
@@ -191,247 +332,336 @@ __global__ __launch_bounds__(64) void partition_kernel(Params p) {
         tensor_v = p.v_scale[0];
     }
     const float qk_scale = p.qk_scale * tensor_k;
+    const uint32_t row_bytes = (uint32_t)p.hkv * D * EB;  // bytes per cache row (all kv heads)
+    LaneOffsets<KLOADS> full;
+    lane_offsets<D, KVT>(full, g, c, row_bytes, p.hkv, kTile - 1);
 
-    const uint8_t *kbase = (const uint8_t *)p.k;
-    const uint8_t *vbase = (const uint8_t *)p.v;
-    const size_t row_bytes = (size_t)p.hkv * D * EB;     // bytes per cache row (all kv heads)
-    const size_t head_off = (size_t)kvh * D * EB;
+    while (pos < hi) {
+        const int u_in = grp * p.wpg + wave;  // unit within the sequence: kvh * nhb + hb
+        const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
+        const int n = max(0, min(p.seq_len[b], p.max_seq_len));
+        const int seg_tiles = (int)min((int64_t)(Tb - t_off), hi - pos);
+        const bool whole = (t_off == 0) && (seg_tiles == Tb);
+        const int t_begin = t_off * kTile;
+        const int t_end = min(n, (t_off + seg_tiles) * kTile);
 
-    f32x4_t acc[DT];
+        const int hloc = hb * kHeadBlock + c;
+        const bool hvalid = hloc < p.group;
+        const int h = kvh * p.group + hloc;
+        const size_t orow = ((size_t)b * p.hq + h) * D;  // output row of head h
+
+        // q operand (B of q.k^T): column c = head hloc, k-slots of lane group g.
+        u32x4_t qop[KSTEPS];
+        {
+            const uint16_t *qrow = (const uint16_t *)p.q + orow;
 #pragma unroll
-    for (int i = 0; i < DT; i++) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-        // ---- locate the tile's first row (a 32-token tile never straddles a 32/64 block)
-        int64_t row0;
-        if constexpr (PAGED) {
-            const int blk = t0 / p.block_size;
-            row0 = (int64_t)p.block_table[(size_t)b * p.max_blocks + blk] * p.block_size + (t0 % p.block_size);
-        } else {
-            row0 = (int64_t)p.kv_start[b] + t0;
+            for (int kk = 0; kk < KSTEPS; kk++)
+                qop[kk] = hvalid ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
         }
-        const int last = t_end - 1 - t0;  // last valid tile-relative token (>= 0)
 
-        // ---- K: rows 16*half + c, 16-byte loads at element offsets 4E*L + E*g
-        u32x4_t kraw[2][KLOADS];
-#pragma unroll
-        for (int half = 0; half < 2; half++) {
-            const int tok = min(16 * half + c, last);
-            const uint8_t *src = kbase + (size_t)(row0 + tok) * row_bytes + head_off;
-#pragma unroll
-            for (int L = 0; L < KLOADS; L++)
-                kraw[half][L] = *(const u32x4_t *)(src + (size_t)(4 * E * L + E * g) * EB);
-        }
-        // ---- V: tokens pv_token(g, j), elements DT*c .. DT*c+DT-1
-        uint32_t vraw[8][VDW];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int tok = min(pv_token(g, j), last);
-            const uint8_t *src = vbase + (size_t)(row0 + tok) * row_bytes + head_off + (size_t)DT * c * EB;
-            if constexpr (VDW == 4) {
-                u32x4_t x = *(const u32x4_t *)src;
-                vraw[j][0] = x[0]; vraw[j][1] = x[1]; vraw[j][2] = x[2]; vraw[j][3] = x[3];
-            } else if constexpr (VDW == 2) {
-                u32x2_t x = *(const u32x2_t *)src;
-                vraw[j][0] = x[0]; vraw[j][1] = x[1];
+        const uint8_t *kbase = (const uint8_t *)p.k + (size_t)kvh * D * EB;
+        const uint8_t *vbase = (const uint8_t *)p.v + (size_t)kvh * D * EB;
+        // lane 16g+i of a tile holds the k (i < 8) or v (i >= 8) scale of token pv_token(g, i & 7)
+        const float *sbase = nullptr;
+        if constexpr (SCALE == SC_TOKEN_HEAD) sbase = ((c & 8) ? p.v_scale : p.k_scale) + kvh;
+        const int32_t *btab = PAGED ? p.block_table + (size_t)b * p.max_blocks : nullptr;
+        const int64_t kv0 = PAGED ? 0 : (int64_t)p.kv_start[b];
+
+        // first cache row of the tile starting at token t0 (wave-uniform; a 32-token tile never
+        // straddles a 32/64-token block)
+        auto tile_row = [&](int t0) -> int64_t {
+            if constexpr (PAGED) return (int64_t)btab[t0 / p.block_size] * p.block_size + (t0 % p.block_size);
+            else return kv0 + t0;
+        };
+        auto issue = [&](TileRaw<KLOADS, VDW> &r, int t0) {
+            const int64_t row = tile_row(t0);
+            const uint8_t *kt = kbase + (size_t)row * row_bytes;
+            const uint8_t *vt = vbase + (size_t)row * row_bytes;
+            const float *st = nullptr;
+            if constexpr (SCALE == SC_TOKEN_HEAD) st = sbase + (size_t)row * p.hkv;
+            const int last = t_end - 1 - t0;
+            if (last >= kTile - 1) {
+                load_tile<D, KVT, SCALE>(r, kt, vt, st, full);
             } else {
-                vraw[j][0] = *(const uint32_t *)src;
+                LaneOffsets<KLOADS> part;
+                lane_offsets<D, KVT>(part, g, c, row_bytes, p.hkv, last);
+                load_tile<D, KVT, SCALE>(r, kt, vt, st, part);
             }
-        }
-        // ---- per-token scales of the lane's 8 score slots
-        float ksc[8], vsc[8];
-        if constexpr (SCALE == SC_TOKEN_HEAD) {
+        };
+
+        f32x4_t acc[DT];
+#pragma unroll
+        for (int i = 0; i < DT; i++) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_run = 0.0f;
+
+        auto compute = [&](const TileRaw<KLOADS, VDW> &r, int t0) {
+            const int last = t_end - 1 - t0;  // last valid tile-relative token (>= 0)
+            // ---- per-token scales of the lane's 8 score slots, through LDS
+            float ksc[8], vsc[8];
+            if constexpr (SCALE == SC_TOKEN_HEAD) {
+                sh_scale[lane] = r.sc;
+                __builtin_amdgcn_wave_barrier();
+                const float4 k0 = *(const float4 *)&sh_scale[16 * g + 0];
+                const float4 k1 = *(const float4 *)&sh_scale[16 * g + 4];
+                const float4 v0 = *(const float4 *)&sh_scale[16 * g + 8];
+                const float4 v1 = *(const float4 *)&sh_scale[16 * g + 12];
+                __builtin_amdgcn_wave_barrier();
+                ksc[0] = k0.x; ksc[1] = k0.y; ksc[2] = k0.z; ksc[3] = k0.w;
+                ksc[4] = k1.x; ksc[5] = k1.y; ksc[6] = k1.z; ksc[7] = k1.w;
+                vsc[0] = v0.x; vsc[1] = v0.y; vsc[2] = v0.z; vsc[3] = v0.w;
+                vsc[4] = v1.x; vsc[5] = v1.y; vsc[6] = v1.z; vsc[7] = v1.w;
+            }
+
+            // ---- scores: S[token][head] = K . q over two 16-token halves
+            f32x4_t sacc[2];
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+                sacc[half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; kk++) {
+                    u32x4_t a;
+                    if constexpr (KVT == KV_FP8) {
+                        const u32x4_t wv = r.k[half][kk / 2];
+                        const uint32_t w0 = wv[2 * (kk % 2)], w1 = wv[2 * (kk % 2) + 1];
+                        a = u32x4_t{cvt_fp8x2<QT, false>(w0), cvt_fp8x2<QT, true>(w0),
+                                    cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
+                    } else {
+                        a = r.k[half][kk];
+                    }
+                    sacc[half] = mfma_qk<QT>(a, qop[kk], sacc[half]);
+                }
+            }
+
+            // ---- online softmax (log2 units)
+            float s[8];
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                const int tok = min(pv_token(g, j), last);
-                const size_t si = (size_t)(row0 + tok) * p.hkv + kvh;
-                ksc[j] = p.k_scale[si];
-                vsc[j] = p.v_scale[si];
+                float x = sacc[j >> 2][j & 3];
+                if constexpr (SCALE == SC_TOKEN_HEAD) x *= ksc[j] * p.qk_scale;
+                else x *= qk_scale;
+                s[j] = x;
             }
-        }
+            if (last < kTile - 1) {
+#pragma unroll
+                for (int j = 0; j < 8; j++) s[j] = (pv_token(g, j) <= last) ? s[j] : -INFINITY;
+            }
+            float mt = s[0];
+#pragma unroll
+            for (int j = 1; j < 8; j++) mt = fmaxf(mt, s[j]);
+            mt = fmaxf(mt, shfl_xor_f(mt, 16));
+            mt = fmaxf(mt, shfl_xor_f(mt, 32));
+            // rescale only when some head's running max grows (wave-uniform branch)
+            if (__any(mt > m_run)) {
+                const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < DT; i++) acc[i] *= alpha;
+                m_run = m_new;
+            }
+            float pj[8], psum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                pj[j] = __builtin_amdgcn_exp2f(s[j] - m_run);
+                psum += pj[j];
+            }
+            l_run += psum;
 
-        // ---- scores: S[token][head] = K . q over two 16-token halves
-        f32x4_t sacc[2];
-#pragma unroll
-        for (int half = 0; half < 2; half++) {
-            sacc[half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; kk++) {
-                u32x4_t a;
-                if constexpr (KVT == KV_FP8) {
-                    const u32x4_t w = kraw[half][kk / 2];
-                    const uint32_t w0 = w[2 * (kk % 2)], w1 = w[2 * (kk % 2) + 1];
-                    a = u32x4_t{cvt_fp8x2<QT, false>(w0), cvt_fp8x2<QT, true>(w0),
-                                cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
-                } else {
-                    a = kraw[half][kk];
-                }
-                sacc[half] = mfma_qk<QT>(a, qop[kk], sacc[half]);
-            }
-        }
-
-        // ---- online softmax (log2 units)
-        float s[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            float x = sacc[j >> 2][j & 3];
-            if constexpr (SCALE == SC_TOKEN_HEAD) x *= ksc[j] * p.qk_scale;
-            else x *= qk_scale;
-            s[j] = (pv_token(g, j) <= last) ? x : -INFINITY;
-        }
-        float mt = s[0];
-#pragma unroll
-        for (int j = 1; j < 8; j++) mt = fmaxf(mt, s[j]);
-        mt = fmaxf(mt, shfl_xor_f(mt, 16));
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        const float m_new = fmaxf(m_run, mt);           // finite: token 0 of the tile is valid
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float pj[8], psum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            pj[j] = __builtin_amdgcn_exp2f(s[j] - m_new);
-            psum += pj[j];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < DT; i++) acc[i] *= alpha;
-
-        // ---- p.V
-        if constexpr (KVT == KV_BF16) {
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const uint32_t h0 = f32_to_bf16_bits(pj[2 * u]), h1 = f32_to_bf16_bits(pj[2 * u + 1]);
-                const float r0 = pj[2 * u] - __builtin_bit_cast(float, h0 << 16);
-                const float r1 = pj[2 * u + 1] - __builtin_bit_cast(float, h1 << 16);
-                hi[u] = h0 | (h1 << 16);
-                lo[u] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-            }
-            const u32x4_t phi = {hi[0], hi[1], hi[2], hi[3]}, plo = {lo[0], lo[1], lo[2], lo[3]};
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) {
-                uint32_t a[4];
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    a[u] = __builtin_amdgcn_perm(vraw[2 * u + 1][dt >> 1], vraw[2 * u][dt >> 1],
-                                                 (dt & 1) ? 0x07060302u : 0x05040100u);
-                const u32x4_t av = {a[0], a[1], a[2], a[3]};
-                acc[dt] = mfma_bf16(av, phi, acc[dt]);
-                acc[dt] = mfma_bf16(av, plo, acc[dt]);
-            }
-        } else {
-            uint32_t pp[4];
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                float p0 = pj[2 * u], p1 = pj[2 * u + 1];
-                if constexpr (SCALE == SC_TOKEN_HEAD) { p0 *= vsc[2 * u]; p1 *= vsc[2 * u + 1]; }
-                pp[u] = pack_f16(p0, p1);
-            }
-            const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
-            if constexpr (KVT == KV_FP8) {
-                uint32_t a[DT][4];
+            // ---- p.V
+            if constexpr (KVT == KV_BF16) {
+                uint32_t hi2[4], lo2[4];
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
-#pragma unroll
-                    for (int w = 0; w < VDW; w++) {
-                        const uint32_t x = __builtin_amdgcn_perm(vraw[2 * u + 1][w], vraw[2 * u][w], 0x05010400u);
-                        const uint32_t y = __builtin_amdgcn_perm(vraw[2 * u + 1][w], vraw[2 * u][w], 0x07030602u);
-                        a[4 * w + 0][u] = cvt_fp8x2<KV_F16, false>(x);
-                        a[4 * w + 1][u] = cvt_fp8x2<KV_F16, true>(x);
-                        a[4 * w + 2][u] = cvt_fp8x2<KV_F16, false>(y);
-                        a[4 * w + 3][u] = cvt_fp8x2<KV_F16, true>(y);
-                    }
+                    const uint32_t h0 = f32_to_bf16_bits(pj[2 * u]), h1 = f32_to_bf16_bits(pj[2 * u + 1]);
+                    const float r0 = pj[2 * u] - __builtin_bit_cast(float, h0 << 16);
+                    const float r1 = pj[2 * u + 1] - __builtin_bit_cast(float, h1 << 16);
+                    hi2[u] = h0 | (h1 << 16);
+                    lo2[u] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
                 }
-#pragma unroll
-                for (int dt = 0; dt < DT; dt++)
-                    acc[dt] = mfma_f16(u32x4_t{a[dt][0], a[dt][1], a[dt][2], a[dt][3]}, pop, acc[dt]);
-            } else {
+                const u32x4_t phi = {hi2[0], hi2[1], hi2[2], hi2[3]}, plo = {lo2[0], lo2[1], lo2[2], lo2[3]};
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) {
                     uint32_t a[4];
 #pragma unroll
                     for (int u = 0; u < 4; u++)
-                        a[u] = __builtin_amdgcn_perm(vraw[2 * u + 1][dt >> 1], vraw[2 * u][dt >> 1],
+                        a[u] = __builtin_amdgcn_perm(r.v[2 * u + 1][dt >> 1], r.v[2 * u][dt >> 1],
                                                      (dt & 1) ? 0x07060302u : 0x05040100u);
-                    acc[dt] = mfma_f16(u32x4_t{a[0], a[1], a[2], a[3]}, pop, acc[dt]);
+                    const u32x4_t av = {a[0], a[1], a[2], a[3]};
+                    acc[dt] = mfma_bf16(av, phi, acc[dt]);
+                    acc[dt] = mfma_bf16(av, plo, acc[dt]);
+                }
+            } else {
+                uint32_t pp[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    float p0 = pj[2 * u], p1 = pj[2 * u + 1];
+                    if constexpr (SCALE == SC_TOKEN_HEAD) { p0 *= vsc[2 * u]; p1 *= vsc[2 * u + 1]; }
+                    pp[u] = pack_f16(p0, p1);
+                }
+                const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
+                if constexpr (KVT == KV_FP8) {
+#pragma unroll
+                    for (int wd = 0; wd < VDW; wd++) {
+                        uint32_t a[4][4];
+#pragma unroll
+                        for (int u = 0; u < 4; u++) {
+                            const uint32_t x = __builtin_amdgcn_perm(r.v[2 * u + 1][wd], r.v[2 * u][wd], 0x05010400u);
+                            const uint32_t y = __builtin_amdgcn_perm(r.v[2 * u + 1][wd], r.v[2 * u][wd], 0x07030602u);
+                            a[0][u] = cvt_fp8x2<KV_F16, false>(x);
+                            a[1][u] = cvt_fp8x2<KV_F16, true>(x);
+                            a[2][u] = cvt_fp8x2<KV_F16, false>(y);
+                            a[3][u] = cvt_fp8x2<KV_F16, true>(y);
+                        }
+#pragma unroll
+                        for (int k = 0; k < 4; k++)
+                            acc[4 * wd + k] = mfma_f16(u32x4_t{a[k][0], a[k][1], a[k][2], a[k][3]}, pop, acc[4 * wd + k]);
+                    }
+                } else {
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        uint32_t a[4];
+#pragma unroll
+                        for (int u = 0; u < 4; u++)
+                            a[u] = __builtin_amdgcn_perm(r.v[2 * u + 1][dt >> 1], r.v[2 * u][dt >> 1],
+                                                         (dt & 1) ? 0x07060302u : 0x05040100u);
+                        acc[dt] = mfma_f16(u32x4_t{a[0], a[1], a[2], a[3]}, pop, acc[dt]);
+                    }
                 }
             }
-        }
-    }
+        };
 
-    // ---- finish: total running sum over the four lane groups of head c
-    float l_tot = l_run + shfl_xor_f(l_run, 16);
-    l_tot += shfl_xor_f(l_tot, 32);
-    if (!hvalid) return;
-    if constexpr (SCALE == SC_TENSOR) {
-#pragma unroll
-        for (int i = 0; i < DT; i++) acc[i] *= tensor_v;
-    }
-    // lane (g, c) holds d = DT*(4g + r) + dt in acc[dt][r]
-    if (nsp == 1) {
-        const float inv = 1.0f / l_tot;
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            float v[DT];
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) v[dt] = acc[dt][r] * inv;
-            store_row_chunk<DT>(p.out, p.out_dtype, orow + DT * (4 * g + r), v);
+        // ---- tile loop: two register sets, the next tile's loads in flight while computing
+        TileRaw<KLOADS, VDW> ra, rb;
+        int t0 = t_begin;
+        issue(ra, t0);
+        while (true) {
+            if (t0 + kTile < t_end) issue(rb, t0 + kTile);
+            compute(ra, t0);
+            t0 += kTile;
+            if (t0 >= t_end) break;
+            if (t0 + kTile < t_end) issue(ra, t0 + kTile);
+            compute(rb, t0);
+            t0 += kTile;
+            if (t0 >= t_end) break;
         }
-        if (p.lse && g == 0) p.lse[(size_t)b * p.hq + h] = (m_run + __log2f(l_tot)) * kLn2;
-    } else {
-        const size_t slot = ((size_t)b * p.hq + h) * p.nsplit + split;
-        float *dst = p.ws_acc + slot * D;
+
+        // ---- segment result: total running sum over the four lane groups of head c
+        float l_tot = l_run + shfl_xor_f(l_run, 16);
+        l_tot += shfl_xor_f(l_tot, 32);
+        if constexpr (SCALE == SC_TENSOR) {
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-#pragma unroll
-            for (int dt = 0; dt < DT; dt += 4)
-                *(float4 *)(dst + DT * (4 * g + r) + dt) =
-                    make_float4(acc[dt][r], acc[dt + 1][r], acc[dt + 2][r], acc[dt + 3][r]);
+            for (int i = 0; i < DT; i++) acc[i] *= tensor_v;
         }
-        if (g == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
+        // lane (g, c) holds d = DT*(4g + r) + dt in acc[dt][r]
+        if (whole) {
+            if (hvalid) {
+                const float inv = 1.0f / l_tot;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    float v[DT];
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) v[dt] = acc[dt][r] * inv;
+                    store_row_chunk<DT>(p.out, p.out_dtype, orow + DT * (4 * g + r), v);
+                }
+                if (p.lse && g == 0) p.lse[(size_t)b * p.hq + h] = (m_run + log2f(l_tot)) * kLn2;
+            }
+        } else {
+            // slot 0: the workgroup's first segment; slot 1: its last (a middle one is always whole)
+            const size_t slot = (((size_t)wg * 2 + (seg_index == 0 ? 0 : 1)) * p.wpg + wave) * kHeadBlock + c;
+            float *dst = p.ws_acc + slot * D;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+#pragma unroll
+                for (int dt = 0; dt < DT; dt += 4)
+                    *(float4 *)(dst + DT * (4 * g + r) + dt) =
+                        make_float4(acc[dt][r], acc[dt + 1][r], acc[dt + 2][r], acc[dt + 3][r]);
+            }
+            if (g == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
+        }
+
+        // ---- next segment: next unit group of this sequence, else the next non-empty sequence
+        pos += seg_tiles;
+        seg_index++;
+        t_off = 0;
+        if (++grp == groups) {
+            grp = 0;
+            do {
+                b++;
+            } while (pos < hi && (Tb = seq_tiles(p, b)) == 0);
+        }
     }
 }
 
 // ---------------------------------------------------------------- combine kernel
 //
 // Grid: x = q head, y = sequence.  Block: 64 lanes, D/64 output elements per lane.
-// Log-sum-exp merge of the sequence's splits in split order:
+// For a unit cut by workgroup boundaries, merges its pieces -- slot 1 (or 0) of the first
+// workgroup, slot 0 of the later ones -- by log-sum-exp:
 //   M = max_i m_i, w_i = 2^(m_i - M), out = sum_i w_i acc_i / sum_i w_i l_i.
+// Also writes out = 0, lse = -inf for empty sequences.  Pieces are reduced in a fixed order:
+// deterministic.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     constexpr int PER = D / 64;
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const int S = p.split_tokens;
-    int n = p.seq_len[b];
-    n = max(0, min(n, p.max_seq_len));
-    const int nsp = (n + S - 1) / S;
-    if (nsp <= 1) return;  // written by the partition kernel
-    const size_t slot0 = ((size_t)b * p.hq + h) * p.nsplit;
+    const size_t obase = ((size_t)b * p.hq + h) * D + PER * lane;
+    const int Tb = seq_tiles(p, b);
+    if (Tb == 0) {
+#pragma unroll
+        for (int k = 0; k < PER; k++) {
+            if (p.out_dtype == 0) ((float *)p.out)[obase + k] = 0.0f;
+            else ((uint16_t *)p.out)[obase + k] = 0;
+        }
+        if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = -INFINITY;
+        return;
+    }
+    const int64_t TT = total_seq_tiles(p, lane) * p.groups;
+    const int64_t Pb = tiles_before(p, b, lane);
+    const int kvh = h / p.group, hloc = h % p.group;
+    const int u_in = kvh * p.nhb + hloc / kHeadBlock;
+    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = hloc % kHeadBlock;
+    const int64_t U0 = Pb * p.groups + (int64_t)grp * Tb;
+    const Split sp = make_split(TT, p.nparts);
+    const int64_t wlo = split_owner(sp, U0), whi = split_owner(sp, U0 + Tb - 1);
+    if (wlo == whi) return;  // finished by the partition kernel
+    const int np = (int)(whi - wlo + 1);
+    const int first_slot = split_lo(sp, wlo) == U0 ? 0 : 1;
+    auto slot_of = [&](int i) -> size_t {
+        return (((size_t)(wlo + i) * 2 + (i == 0 ? first_slot : 0)) * p.wpg + wave) * kHeadBlock + c;
+    };
+    // max and weight sum, pieces spread over lanes
     float M = -INFINITY;
-    for (int i = 0; i < nsp; i++) M = fmaxf(M, p.ws_ml[slot0 + i].x);
-    float L = 0.0f, o[PER];
+    for (int i = lane; i < np; i += 64) M = fmaxf(M, p.ws_ml[slot_of(i)].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor_f(M, off));
+    float L = 0.0f;
+    for (int i = lane; i < np; i += 64) {
+        const float2 ml = p.ws_ml[slot_of(i)];
+        L += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += shfl_xor_f(L, off);
+    // weighted accumulators, pieces in order
+    float o[PER];
 #pragma unroll
     for (int k = 0; k < PER; k++) o[k] = 0.0f;
-    for (int i = 0; i < nsp; i++) {
-        const float2 ml = p.ws_ml[slot0 + i];
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        L += w * ml.y;
-        const float *src = p.ws_acc + (slot0 + i) * D + PER * lane;
+#pragma unroll 4
+    for (int i = 0; i < np; i++) {
+        const size_t slot = slot_of(i);
+        const float wt = __builtin_amdgcn_exp2f(p.ws_ml[slot].x - M);
+        const float *src = p.ws_acc + slot * D + PER * lane;
 #pragma unroll
-        for (int k = 0; k < PER; k++) o[k] += w * src[k];
+        for (int k = 0; k < PER; k++) o[k] += wt * src[k];
     }
     const float inv = 1.0f / L;
-    const size_t base = ((size_t)b * p.hq + h) * D + PER * lane;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
         const float v = o[k] * inv;
-        if (p.out_dtype == 0) ((float *)p.out)[base + k] = v;
-        else if (p.out_dtype == 1) ((_Float16 *)p.out)[base + k] = (_Float16)v;
-        else ((uint16_t *)p.out)[base + k] = (uint16_t)f32_to_bf16_bits(v);
+        if (p.out_dtype == 0) ((float *)p.out)[obase + k] = v;
+        else if (p.out_dtype == 1) ((_Float16 *)p.out)[obase + k] = (_Float16)v;
+        else ((uint16_t *)p.out)[obase + k] = (uint16_t)f32_to_bf16_bits(v);
     }
-    if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = (M + __log2f(L)) * kLn2;
+    if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = (M + log2f(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------- E4M3 decode (diagnostic)
@@ -452,7 +682,7 @@ __global__ void fp8_decode_kernel(const uint8_t *in, float *out, int n) {
 // ---------------------------------------------------------------- host-side dispatch
 template <int D, int KVT, int QT, int SCALE>
 static hipError_t launch_p(const Params &p, hipStream_t stream) {
-    dim3 grid(p.nsplit, p.hkv * p.nhb, p.batch), block(64);
+    dim3 grid(p.nparts), block(64 * p.wpg);
     if (p.block_table)
         hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true>), grid, block, 0, stream, p);
     else

@@ -67,6 +67,12 @@ typedef enum {
 /*
  * fd_decode_attention -- one flash-decoding step (split-KV partition + log-sum-exp combine).
  *
+ * Work split: every (sequence, kv head, block of <= 16 query heads) "unit" owns
+ * ceil(seq_len / 32) tiles of 32 tokens; the units' tiles are concatenated and cut into
+ * `num_partitions` equal ranges, one per wave of the partition kernel, so long and short
+ * sequences are balanced without any host-side knowledge of seq_len.  A unit cut by a range
+ * boundary leaves partial (max, sum, accumulator) states that the combine kernel merges.
+ *
  *   q            [batch][num_q_heads][head_dim], q_dtype (FD_F16 or FD_BF16), contiguous.
  *   k_cache,     paged mode:      [num_blocks][block_size][num_kv_heads][head_dim]
  *   v_cache      contiguous mode: [rows][num_kv_heads][head_dim]
@@ -77,7 +83,8 @@ typedef enum {
  *   kv_start     [batch] int32 first row of each sequence (contiguous mode), or NULL.
  *                Exactly one of block_table / kv_start must be given.
  *   seq_len      [batch] int32, 0 <= seq_len[b] <= max_seq_len (device memory).
- *   max_seq_len  host-side upper bound of seq_len; sizes the grid and the workspace only.
+ *   max_seq_len  host-side upper bound of seq_len (<= 2^24); sizes the grid and the workspace
+ *                only.
  *                Paged mode needs max_seq_len <= max_blocks_per_seq * block_size.
  *   block_size   32 or 64 in paged mode; ignored (pass 0) in contiguous mode.
  *   scale_mode   FD_SCALE_NONE for f16/bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 KV.
@@ -87,11 +94,11 @@ typedef enum {
  *   out          [batch][num_q_heads][head_dim] in out_dtype (FD_F32, FD_F16 or FD_BF16).
  *   lse          optional [batch][num_q_heads] fp32 natural-log sum of exp(scores); NULL = skip.
  *                An empty sequence (seq_len 0) yields out = 0 and lse = -inf.
- *   workspace    device scratch of at least fd_workspace_bytes(...) bytes, 256-byte aligned
- *                (may be NULL when that size is 0).  Contents need no initialisation and are
- *                clobbered; one workspace must not be shared by calls that may overlap.
- *   num_splits   0 = automatic split of each sequence's KV range (sized for 256 CUs);
- *                > 0 forces at most that many splits per sequence (testing and tuning).
+ *   workspace    device scratch of at least fd_workspace_bytes(...) bytes, 256-byte aligned.
+ *                Contents need no initialisation and are clobbered; one workspace must not be
+ *                shared by calls that may overlap.
+ *   num_partitions  0 = automatic (2048 partitions: 8 waves per CU on 256 CUs); > 0 forces
+ *                that many (testing and tuning).  Capped by the number of tiles the sizes allow.
  *   stream       HIP stream to enqueue on (0 = null stream).
  *
  * Device-side contract (not checked; violating it is undefined): seq_len[b] <= max_seq_len,
@@ -111,25 +118,23 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
                         float softmax_scale,
                         void *out, int out_dtype, float *lse,
                         void *workspace, size_t workspace_bytes,
-                        int num_splits, hipStream_t stream);
+                        int num_partitions, hipStream_t stream);
 
 /*
- * fd_workspace_bytes -- workspace size fd_decode_attention needs for these sizes (0 when no
- * sequence can be split).  The same arguments must be passed to fd_decode_attention.
- * Returns (size_t)-1 for arguments fd_decode_attention would reject as invalid.
+ * fd_workspace_bytes -- workspace size fd_decode_attention needs for these sizes (partial
+ * states: 2 slots x 16 heads x (head_dim + 2) fp32 per partition).  The same arguments must
+ * be passed to fd_decode_attention.  Returns (size_t)-1 for arguments fd_decode_attention
+ * would reject as invalid.
  */
 size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                          int max_seq_len, int block_size, int kv_dtype, int num_splits);
+                          int max_seq_len, int block_size, int kv_dtype, int num_partitions);
 
 /*
- * fd_plan_splits -- the split plan fd_decode_attention will use for these sizes: returns the
- * maximum number of splits per sequence and stores the split length in tokens (a multiple
- * of 32) in *split_tokens when non-NULL.  Returns -1 for invalid sizes.  Host-only; for
- * tests and tuning.
+ * fd_plan_partitions -- the number of partitions (partition-kernel waves) fd_decode_attention
+ * will use for these sizes, or -1 for invalid sizes.  Host-only; for tests and tuning.
  */
-int fd_plan_splits(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                   int max_seq_len, int block_size, int kv_dtype, int num_splits,
-                   int *split_tokens);
+int fd_plan_partitions(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                       int max_seq_len, int block_size, int kv_dtype, int num_partitions);
 
 /*
  * fd_fp8_e4m3_decode -- diagnostic: decodes n E4M3 bytes with the exact hardware conversions the

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_splits", "fd_status_string",
+    for n in ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
               "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events"):
         assert n in names
     assert set(names) == set(fd.EXPORTS)
@@ -45,18 +45,23 @@ def test_version_and_status_strings():
 
 
 def test_plan_and_workspace_sizes():
-    n, S = fd.plan_splits(32, 64, 8, 128, 32768, 64, "fp8_e4m3")
-    assert S % 32 == 0 and n == -(-32768 // S) and 256 <= S <= 4096
-    assert fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3") >= 32 * 64 * n * 128 * 4
-    n1, S1 = fd.plan_splits(2, 4, 1, 64, 100, 0, "f16")
-    assert n1 == 1 and fd.workspace_bytes(2, 4, 1, 64, 100, 0, "f16") == 0
-    n7, S7 = fd.plan_splits(4, 128, 1, 128, 131072, 64, "fp8_e4m3", num_splits=7)
-    assert n7 <= 7 and S7 * n7 >= 131072
-    assert fd.plan_splits(1, 1, 1, 128, 0)[0] == 1
+    W = fd.plan_partitions(32, 64, 8, 128, 32768, 64, "fp8_e4m3")
+    assert W == 256                       # 8 kv heads -> 8 waves per workgroup, 2048 waves
+    assert fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3") >= W * 8 * 2 * 16 * 130 * 4
+    assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3") == 256   # 8 head blocks
+    assert fd.plan_partitions(64, 6, 3, 128, 4096, 64, "fp8_e4m3") == 2048 // 3   # 3 waves per group
+    assert fd.plan_partitions(2, 6, 3, 128, 4096, 64, "fp8_e4m3") == 2 * 128      # capped by tiles
+    # tiny step: capped by its tile count (2 sequences x 1 unit x 4 tiles)
+    assert fd.plan_partitions(2, 4, 1, 64, 100, 0, "f16") == 8
+    assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3", num_partitions=7) == 7
+    assert fd.plan_partitions(1, 1, 1, 128, 0) == 1
+    assert fd.workspace_bytes(1, 1, 1, 128, 0) > 0
     with pytest.raises(fd.FdError):
-        fd.plan_splits(2, 6, 4, 128, 100)          # 6 q heads on 4 kv heads
+        fd.plan_partitions(2, 6, 4, 128, 100)          # 6 q heads on 4 kv heads
     with pytest.raises(fd.FdError):
         fd.workspace_bytes(0, 4, 1, 128, 100)
+    with pytest.raises(fd.FdError):
+        fd.plan_partitions(1, 1, 1, 128, (1 << 24) + 1)
 
 
 # A valid argument set with fake (never dereferenced) device pointers; each test perturbs one.
@@ -66,7 +71,7 @@ def good_args(**kw):
              head_dim=128, block_size=64, kv_dtype=fd.FD_FP8_E4M3, q_dtype=fd.FD_BF16,
              scale_mode=fd.FD_SCALE_PER_TOKEN_HEAD, k_scale=0x6000, v_scale=0x7000,
              softmax_scale=0.088, out=0x8000, out_dtype=fd.FD_F32, lse=None, workspace=0x10000,
-             workspace_bytes_=1 << 30, num_splits=0, stream=None)
+             workspace_bytes_=1 << 30, num_partitions=0, stream=None)
     a.update(kw)
     return a
 
@@ -92,7 +97,8 @@ BAD = [
     (dict(kv_dtype=fd.FD_BF16), fd.FD_ERR_INVALID_ARG),          # bf16 KV with a scale mode
     (dict(kv_dtype=fd.FD_F16, scale_mode=0, q_dtype=fd.FD_BF16), fd.FD_ERR_UNSUPPORTED),
     (dict(softmax_scale=float("nan")), fd.FD_ERR_INVALID_ARG),
-    (dict(num_splits=-2), fd.FD_ERR_INVALID_ARG),
+    (dict(num_partitions=-2), fd.FD_ERR_INVALID_ARG),
+    (dict(max_seq_len=(1 << 24) + 32, max_blocks_per_seq=(1 << 19) + 1), fd.FD_ERR_INVALID_ARG),
     (dict(head_dim=96), fd.FD_ERR_UNSUPPORTED),
     (dict(block_size=16, max_blocks_per_seq=16), fd.FD_ERR_UNSUPPORTED),
     (dict(max_blocks_per_seq=0), fd.FD_ERR_INVALID_ARG),

@@ -51,11 +51,11 @@ def run_gpu(case, **kw):
     return out, lse
 
 
-def check_case(name, case, seqs=None, num_splits=0, out_dtype="f32"):
+def check_case(name, case, seqs=None, num_partitions=0, out_dtype="f32"):
     print(f"[{name}] lens={case.seq_lens[:8]}{'...' if case.batch > 8 else ''} G={case.group} "
           f"D={case.d} kv={case.kv_dtype} scale={case.scale_mode} bs={case.block_size} "
-          f"splits={num_splits}", flush=True)
-    out, lse = run_gpu(case, num_splits=num_splits, out_dtype=out_dtype)
+          f"partitions={num_partitions}", flush=True)
+    out, lse = run_gpu(case, num_partitions=num_partitions, out_dtype=out_dtype)
     prob = oracle.Problem.from_case(case)
     ref, ref_lse = oracle.decode_attention(prob, seqs=seqs)
     compare(name, out, ref, case.kv_dtype, seqs)
@@ -109,10 +109,10 @@ SMALL = [
 
 
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
-@pytest.mark.parametrize("splits", [0, 1, 2, 7])
-def test_small_shapes(name, kw, splits):
+@pytest.mark.parametrize("parts", [0, 1, 2, 7, 100000])
+def test_small_shapes(name, kw, parts):
     case = workloads.custom_case(seed=3, device="cuda", **kw)
-    check_case(f"{name}/s{splits}", case, num_splits=splits)
+    check_case(f"{name}/p{parts}", case, num_partitions=parts)
 
 
 @pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 4095])
@@ -121,16 +121,27 @@ def test_length_edges(n):
     case = workloads.custom_case(seed=n, device="cuda", batch=3, hq=16, hkv=2, d=128, seq_lens=lens,
                                  kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64,
                                  max_seq_len=max(lens + [1]))
-    for splits in (0, 3):
-        check_case(f"len{n}/s{splits}", case, num_splits=splits)
+    for parts in (0, 3):
+        check_case(f"len{n}/p{parts}", case, num_partitions=parts)
 
 
-def test_max_splits_one_tile_each():
-    case = workloads.custom_case(seed=9, device="cuda", batch=2, hq=8, hkv=1, d=128,
-                                 seq_lens=[32 * 40 + 3, 200], kv="fp8_e4m3", q="bf16",
+def test_more_partitions_than_tiles():
+    # 3 partitions per tile on average: many idle waves, every unit cut into one-tile pieces
+    case = workloads.custom_case(seed=9, device="cuda", batch=3, hq=8, hkv=1, d=128,
+                                 seq_lens=[32 * 40 + 3, 200, 0], kv="fp8_e4m3", q="bf16",
                                  scale="token_head", block_size=64)
-    nmax = -(-case.max_seq_len // 32)
-    check_case("maxsplits", case, num_splits=nmax)
+    tiles = sum(-(-n // 32) for n in case.seq_lens)
+    check_case("overpartitioned", case, num_partitions=3 * tiles)
+    check_case("one_tile_each", case, num_partitions=tiles)
+
+
+@pytest.mark.parametrize("parts", [1, 5, 64, 333, 2048])
+def test_ragged_mix_partition_counts(parts):
+    lens = [0, 1, 5000, 33, 0, 64, 2047, 12000, 31, 0, 700, 96]
+    case = workloads.custom_case(seed=21, device="cuda", batch=len(lens), hq=32, hkv=8, d=128,
+                                 seq_lens=lens, kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=32)
+    check_case(f"ragged_mix/p{parts}", case, num_partitions=parts)
 
 
 def test_peaky_scores():
@@ -138,7 +149,7 @@ def test_peaky_scores():
                                  seq_lens=[3000, 700], kv="fp8_e4m3", q="bf16", scale="token_head",
                                  block_size=64)
     case.q.mul_(4.0)
-    check_case("peaky_q4", case, num_splits=0)
+    check_case("peaky_q4", case, num_partitions=0)
 
 
 @pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
