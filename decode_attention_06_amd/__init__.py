@@ -20,7 +20,7 @@ FD_SCALE_NONE, FD_SCALE_PER_TENSOR, FD_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 DTYPE_CODES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8_e4m3": FD_FP8_E4M3}
 SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head": FD_SCALE_PER_TOKEN_HEAD}
 EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
-           "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events")
+           "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe")
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.fd_version.argtypes = []
         L.fd_fp8_e4m3_decode.restype = i32
         L.fd_fp8_e4m3_decode.argtypes = [vp, vp, i32, vp]
+        L.fd_hbm_read_probe.restype = i32
+        L.fd_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.fd_set_profile_events.restype = i32
         L.fd_set_profile_events.argtypes = [vp, vp]
         _lib = L
@@ -191,3 +193,19 @@ def set_profile_events(begin=None, end=None):
     st = lib().fd_set_profile_events(bp, ep)
     if st != FD_OK:
         raise FdError(st, "fd_set_profile_events")
+
+
+def hbm_read_probe(buf, out, blocks: int, stream=None):
+    """Diagnostic: stream-read GPU tensor ``buf`` (uint8, 16-byte multiple) once; ``out`` is a
+    uint32 GPU tensor of at least blocks*256 elements."""
+    import torch
+
+    _require_cuda(buf=buf, out=out)
+    nbytes = buf.numel() * buf.element_size()
+    if out.numel() < blocks * 256:
+        raise ValueError("out too small")
+    if stream is None:
+        stream = torch.cuda.current_stream(buf.device).cuda_stream
+    st = lib().fd_hbm_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, stream)
+    if st != FD_OK:
+        raise FdError(st, "fd_hbm_read_probe")

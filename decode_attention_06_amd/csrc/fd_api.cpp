@@ -180,6 +180,11 @@ int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end) 
     return FD_OK;
 }
 
+int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, hipStream_t stream) {
+    if (!buf || !out || blocks <= 0 || (bytes & 15) || ((uintptr_t)buf & 15)) return FD_ERR_INVALID_ARG;
+    return fd::launch_read_probe(buf, bytes / 16, out, blocks, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
+}
+
 int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream) {
     if (n < 0 || (n > 0 && (!in || !out))) return FD_ERR_INVALID_ARG;
     return fd::launch_fp8_decode(in, out, n, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;

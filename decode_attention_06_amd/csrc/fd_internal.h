@@ -43,5 +43,6 @@ hipError_t launch_partition(const Params &p, int kv_dtype, int q_dtype, int scal
                             hipStream_t stream);
 hipError_t launch_combine(const Params &p, hipStream_t stream);
 hipError_t launch_fp8_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
+hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, hipStream_t stream);
 
 }  // namespace fd

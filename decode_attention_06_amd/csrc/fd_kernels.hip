@@ -565,7 +565,7 @@ void partition_kernel(Params p) {
                 }
                 if (p.lse && g == 0) p.lse[(size_t)b * p.hq + h] = (m_run + log2f(l_tot)) * kLn2;
             }
-        } else {
+        } else if (hvalid) {
             // slot 0: the workgroup's first segment; slot 1: its last (a middle one is always whole)
             const size_t slot = (((size_t)wg * 2 + (seg_index == 0 ? 0 : 1)) * p.wpg + wave) * kHeadBlock + c;
             float *dst = p.ws_acc + slot * D;
@@ -594,32 +594,54 @@ void partition_kernel(Params p) {
 
 // ---------------------------------------------------------------- combine kernel
 //
-// Grid: x = q head, y = sequence.  Block: 64 lanes, D/64 output elements per lane.
-// For a unit cut by workgroup boundaries, merges its pieces -- slot 1 (or 0) of the first
-// workgroup, slot 0 of the later ones -- by log-sum-exp:
-//   M = max_i m_i, w_i = 2^(m_i - M), out = sum_i w_i acc_i / sum_i w_i l_i.
-// Also writes out = 0, lse = -inf for empty sequences.  Pieces are reduced in a fixed order:
-// deterministic.
+// Grid: x = q head, y = sequence.  Block: one wave.  For a unit cut by workgroup boundaries,
+// merges its pieces -- slot 1 (or 0) of the first workgroup, slot 0 of the later ones -- by
+// log-sum-exp:  M = max_i m_i, w_i = 2^(m_i - M), out = sum_i w_i acc_i / sum_i w_i l_i.
+// Lane (j = lane / 8, k = lane % 8) accumulates pieces j, j+8, ... over output elements
+// [k*D/8, (k+1)*D/8); the eight partial sums are then added by a fixed butterfly.  Also writes
+// out = 0, lse = -inf for empty sequences.  Fixed order throughout: deterministic.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(Params p) {
-    constexpr int PER = D / 64;
+    constexpr int PER = D / 8;  // output elements per lane
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const size_t obase = ((size_t)b * p.hq + h) * D + PER * lane;
+    const int j = lane >> 3, k = lane & 7;
+    const int kvh = h / p.group, hloc = h % p.group;
+    const int u_in = kvh * p.nhb + hloc / kHeadBlock;
+    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = hloc % kHeadBlock;
+    const size_t obase = ((size_t)b * p.hq + h) * D + PER * k;
+
+    auto store = [&](const float *v) {
+        if (p.out_dtype == 0) {
+            float *o = (float *)p.out + obase;
+#pragma unroll
+            for (int i = 0; i < PER; i += 4) *(float4 *)(o + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+        } else {
+            uint32_t w[PER / 2];
+#pragma unroll
+            for (int i = 0; i < PER / 2; i++) {
+                if (p.out_dtype == 1) w[i] = pack_f16(v[2 * i], v[2 * i + 1]);
+                else w[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
+            }
+            uint16_t *o = (uint16_t *)p.out + obase;
+#pragma unroll
+            for (int i = 0; i < PER / 2; i += 4) *(u32x4_t *)(o + 2 * i) = u32x4_t{w[i], w[i + 1], w[i + 2], w[i + 3]};
+        }
+    };
+
+    // wave-wide reductions first, with every lane active
+    const int64_t TT = total_seq_tiles(p, lane) * p.groups;
+    const int64_t Pb = tiles_before(p, b, lane);
     const int Tb = seq_tiles(p, b);
     if (Tb == 0) {
+        if (j == 0) {
+            float z[PER];
 #pragma unroll
-        for (int k = 0; k < PER; k++) {
-            if (p.out_dtype == 0) ((float *)p.out)[obase + k] = 0.0f;
-            else ((uint16_t *)p.out)[obase + k] = 0;
+            for (int i = 0; i < PER; i++) z[i] = 0.0f;
+            store(z);
         }
         if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = -INFINITY;
         return;
     }
-    const int64_t TT = total_seq_tiles(p, lane) * p.groups;
-    const int64_t Pb = tiles_before(p, b, lane);
-    const int kvh = h / p.group, hloc = h % p.group;
-    const int u_in = kvh * p.nhb + hloc / kHeadBlock;
-    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = hloc % kHeadBlock;
     const int64_t U0 = Pb * p.groups + (int64_t)grp * Tb;
     const Split sp = make_split(TT, p.nparts);
     const int64_t wlo = split_owner(sp, U0), whi = split_owner(sp, U0 + Tb - 1);
@@ -629,7 +651,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     auto slot_of = [&](int i) -> size_t {
         return (((size_t)(wlo + i) * 2 + (i == 0 ? first_slot : 0)) * p.wpg + wave) * kHeadBlock + c;
     };
-    // max and weight sum, pieces spread over lanes
+    // M and L with the pieces spread over lanes
     float M = -INFINITY;
     for (int i = lane; i < np; i += 64) M = fmaxf(M, p.ws_ml[slot_of(i)].x);
 #pragma unroll
@@ -641,27 +663,31 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) L += shfl_xor_f(L, off);
-    // weighted accumulators, pieces in order
+    // weighted accumulators: lane group j takes pieces j, j+8, ...
     float o[PER];
 #pragma unroll
-    for (int k = 0; k < PER; k++) o[k] = 0.0f;
-#pragma unroll 4
-    for (int i = 0; i < np; i++) {
+    for (int i = 0; i < PER; i++) o[i] = 0.0f;
+    for (int i = j; i < np; i += 8) {
         const size_t slot = slot_of(i);
         const float wt = __builtin_amdgcn_exp2f(p.ws_ml[slot].x - M);
-        const float *src = p.ws_acc + slot * D + PER * lane;
+        const float *src = p.ws_acc + slot * D + PER * k;
 #pragma unroll
-        for (int k = 0; k < PER; k++) o[k] += wt * src[k];
+        for (int e = 0; e < PER; e += 4) {
+            const float4 x = *(const float4 *)(src + e);
+            o[e] += wt * x.x; o[e + 1] += wt * x.y; o[e + 2] += wt * x.z; o[e + 3] += wt * x.w;
+        }
     }
-    const float inv = 1.0f / L;
 #pragma unroll
-    for (int k = 0; k < PER; k++) {
-        const float v = o[k] * inv;
-        if (p.out_dtype == 0) ((float *)p.out)[obase + k] = v;
-        else if (p.out_dtype == 1) ((_Float16 *)p.out)[obase + k] = (_Float16)v;
-        else ((uint16_t *)p.out)[obase + k] = (uint16_t)f32_to_bf16_bits(v);
+    for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < PER; e++) o[e] += shfl_xor_f(o[e], off);
+    if (j == 0) {
+        const float inv = 1.0f / L;
+#pragma unroll
+        for (int e = 0; e < PER; e++) o[e] *= inv;
+        store(o);
+        if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = (M + log2f(L)) * kLn2;
     }
-    if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = (M + log2f(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------- E4M3 decode (diagnostic)
@@ -677,6 +703,23 @@ __global__ void fp8_decode_kernel(const uint8_t *in, float *out, int n) {
     const float fb = __builtin_bit_cast(float, (bb & 0xFFFF) << 16);
     out[2 * i] = fh;
     out[2 * i + 1] = fb;
+}
+
+// ---------------------------------------------------------------- HBM read probe (diagnostic)
+// Streams `n16` 16-byte words with coalesced 128-bit loads (four independent loads in flight per
+// lane per iteration, grid-stride) and folds them with XOR so the loads cannot be dropped.
+// The measured rate is the read bandwidth a plain stream reaches on this device.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t *__restrict__ in, size_t n16,
+                                                         uint32_t *__restrict__ out) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    u32x4_t acc = {0, 0, 0, 0};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4_t a = in[i], b = in[i + stride], c = in[i + 2 * stride], d = in[i + 3 * stride];
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n16; i += stride) acc ^= in[i];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
 // ---------------------------------------------------------------- host-side dispatch
@@ -711,6 +754,11 @@ hipError_t launch_combine(const Params &p, hipStream_t stream) {
     dim3 grid(p.hq, p.batch), block(64);
     if (p.d == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, stream, p);
     else hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, hipStream_t stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4_t *)in, n16, out);
     return hipGetLastError();
 }
 

@@ -153,6 +153,16 @@ int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream)
  */
 int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end);
 
+/*
+ * fd_hbm_read_probe -- diagnostic: reads `bytes` (a multiple of 16) from the device buffer `buf`
+ * (16-byte aligned) with coalesced 128-bit loads, `blocks` workgroups of 256 lanes striding over
+ * it, and writes one XOR fold per lane to out[blocks * 256] (uint32).  Timing it gives the read
+ * bandwidth a plain stream reaches on the device, the practical ceiling for the attention
+ * kernels' KV reads.  Asynchronous on `stream`.  Returns FD_OK, FD_ERR_INVALID_ARG or
+ * FD_ERR_LAUNCH.
+ */
+int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, hipStream_t stream);
+
 /* fd_status_string -- static, NUL-terminated name of a status code (never NULL). */
 const char *fd_status_string(int status);
 

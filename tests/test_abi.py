@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
-              "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events"):
+              "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe"):
         assert n in names
     assert set(names) == set(fd.EXPORTS)
 
@@ -113,6 +113,13 @@ def test_bad_arguments_rejected_before_launch(change, expect):
     # valid-but-fake pointers: if validation let this through, the launch would fail with
     # FD_ERR_LAUNCH (no GPU here) -- the test needs the specific host-side code instead.
     assert fd.decode_attention_raw(**good_args(**change)) == expect
+
+
+def test_read_probe_rejects_bad_arguments():
+    L = fd.lib()
+    assert L.fd_hbm_read_probe(None, 16, 0x1000, 1, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_hbm_read_probe(0x1000, 15, 0x2000, 1, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_hbm_read_probe(0x1000, 16, 0x2000, 0, None) == fd.FD_ERR_INVALID_ARG
 
 
 def test_fp8_decode_rejects_bad_count():
