@@ -57,8 +57,11 @@ Plan make_plan(int batch, int hq, int hkv, int max_seq_len, int num_partitions) 
     return pl;
 }
 
+// Workspace: [ml slots][acc slots]; one slot pair per partition per unit of a group per head.
+size_t ws_slots(const Plan &pl) { return (size_t)pl.nparts * 2 * pl.wpg * fd::kHeadBlock; }
+
 size_t ws_bytes(const Plan &pl, int head_dim) {
-    const size_t slots = (size_t)pl.nparts * 2 * pl.wpg * fd::kHeadBlock;
+    const size_t slots = ws_slots(pl);
     return align256(slots * sizeof(float) * 2) + slots * head_dim * sizeof(float);
 }
 
@@ -162,7 +165,7 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     p.out_dtype = out_dtype;
     p.qk_scale = (float)((double)softmax_scale * 1.4426950408889634074);  // log2(e)
     {
-        const size_t slots = (size_t)pl.nparts * 2 * pl.wpg * fd::kHeadBlock;
+        const size_t slots = ws_slots(pl);
         p.ws_ml = (float2 *)workspace;
         p.ws_acc = (float *)((char *)workspace + align256(slots * sizeof(float) * 2));
     }

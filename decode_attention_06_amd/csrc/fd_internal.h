@@ -12,6 +12,8 @@ constexpr int kTile = 32;
 constexpr int kHeadBlock = 16;
 // Most waves (units of one sequence) a partition workgroup runs side by side.
 constexpr int kMaxWavesPerGroup = 8;
+// Largest batch whose per-sequence tile prefix sums a partition workgroup keeps in LDS.
+constexpr int kLdsBatch = 4096;
 
 struct Params {
     const void *q;

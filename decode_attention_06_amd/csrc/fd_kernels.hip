@@ -93,6 +93,22 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Scalar load of a wave-uniform int32 the kernel never writes (seq_len, block table, kv start):
+// through the constant address space, so it is an s_load, independent of the vector-memory
+// counter that the KV prefetch uses.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t *ptr, size_t i) {
+    return *((const __attribute__((address_space(4))) int32_t *)ptr + i);
+}
+
+// Wave-uniform copies (the value is the same in every lane; this keeps it in scalar registers
+// so that loads addressed by it are scalar loads, counted apart from the KV vector loads).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Element index (within a head_dim row) of MFMA k-slot (group g, step kk, position j) of the
 // q.k^T contraction.  E = elements per 16-byte load of K; each lane loads 16 bytes at element
 // offset 4E*L + E*g for L = 0 .. D/(4E)-1, so one load instruction covers 4E contiguous
@@ -150,6 +166,13 @@ __device__ __forceinline__ int seq_tiles(const Params &p, int b) {
     return (n + kTile - 1) / kTile;
 }
 
+// Same, for a wave-uniform b (scalar load).
+__device__ __forceinline__ int seq_tiles_u(const Params &p, int b) {
+    int n = ld_uniform(p.seq_len, b);
+    n = max(0, min(n, p.max_seq_len));
+    return (n + kTile - 1) / kTile;
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -200,10 +223,11 @@ __device__ __forceinline__ int64_t tiles_before(const Params &p, int b, int lane
 
 // ---------------------------------------------------------------- split-KV partition kernel
 //
-// Grid: W waves (one 64-lane workgroup each).  Each wave walks its tile range unit by unit
-// ("segments"): for each segment it computes the unnormalised softmax state of the segment's
-// tokens for the head block's heads and writes either the final output (whole unit) or a
-// partial state (m, l, acc) to its workspace slot.
+// Grid: W workgroups of wpg waves.  Workgroup w takes tile range w of the balanced split; wave i
+// runs unit i of each unit group in it.  The range is one stream of tiles that crosses unit and
+// sequence boundaries ("segments"): per segment a wave accumulates the unnormalised softmax state
+// of the segment's tokens for its head block and writes either the final output (whole unit) or
+// a partial state (m, l, acc) to its workspace slot.
 //
 // Per 32-token tile a lane loads: K -- 16 bytes x KLOADS from each of its two token rows
 // (16*half + c); V -- one DT-element chunk of each of its 8 token rows pv_token(g, j); and, with
@@ -228,54 +252,71 @@ struct TileRaw {
     float sc;
 };
 
-// Byte offsets of a lane's loads relative to the tile's first row of its kv head.
-template <int KLOADS>
+// Lane-dependent byte offsets of a full tile's loads (the rest of each address is wave-uniform
+// and folded into the scalar base pointer):
+//   K  row 16*half + c, elements 4E*L + E*g:      k = c*row_bytes + E*g*EB   (+16*half*row_bytes + 4E*L*EB)
+//   V  row pv_token(g, j), elements DT*c ..:      v = 4g*row_bytes + DT*c*EB  (+ (j < 4 ? j : 12 + j)*row_bytes)
+//   scale of token pv_token(g, c & 7), in floats: s = pv_token(g, c & 7) * hkv
 struct LaneOffsets {
-    uint32_t k[2][KLOADS];
-    uint32_t v[8];
-    uint32_t s;  // in floats, relative to the tile's first row of the scale array
+    uint32_t k, v, s;
 };
 
 template <int D, int KVT>
-__device__ __forceinline__ void lane_offsets(LaneOffsets<Geometry<D, KVT>::KLOADS> &o, int g, int c,
-                                             uint32_t row_bytes, int hkv, int last) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int g, int c, uint32_t row_bytes, int hkv) {
+    using G = Geometry<D, KVT>;
+    LaneOffsets o;
+    o.k = (uint32_t)c * row_bytes + (uint32_t)(G::E * g * G::EB);
+    o.v = (uint32_t)(4 * g) * row_bytes + (uint32_t)(G::DT * c * G::EB);
+    o.s = (uint32_t)pv_token(g, c & 7) * (uint32_t)hkv;
+    return o;
+}
+
+template <int VDW>
+__device__ __forceinline__ void load_v_chunk(uint32_t (&dst)[VDW], const uint8_t *src) {
+    if constexpr (VDW == 4) {
+        const u32x4_t x = *(const u32x4_t *)src;
+        dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+    } else if constexpr (VDW == 2) {
+        const u32x2_t x = *(const u32x2_t *)src;
+        dst[0] = x[0]; dst[1] = x[1];
+    } else {
+        dst[0] = *(const uint32_t *)src;
+    }
+}
+
+// Full tile: 32 valid tokens.
+template <int D, int KVT, int SCALE>
+__device__ __forceinline__ void load_tile(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
+                                          const uint8_t *kt, const uint8_t *vt, const float *st,
+                                          const LaneOffsets &o, uint32_t row_bytes) {
+    using G = Geometry<D, KVT>;
+#pragma unroll
+    for (int half = 0; half < 2; half++)
+#pragma unroll
+        for (int L = 0; L < G::KLOADS; L++)
+            r.k[half][L] = *(const u32x4_t *)(kt + (size_t)(16 * half) * row_bytes + 4 * G::E * L * G::EB + o.k);
+#pragma unroll
+    for (int j = 0; j < 8; j++) load_v_chunk<G::VDW>(r.v[j], vt + (size_t)(j < 4 ? j : 12 + j) * row_bytes + o.v);
+    if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[o.s];
+}
+
+// Partial last tile: tokens past `last` are clamped to `last` (valid rows; masked later).
+template <int D, int KVT, int SCALE>
+__device__ __forceinline__ void load_tile_part(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
+                                               const uint8_t *kt, const uint8_t *vt, const float *st,
+                                               int g, int c, uint32_t row_bytes, int hkv, int last) {
     using G = Geometry<D, KVT>;
 #pragma unroll
     for (int half = 0; half < 2; half++) {
         const uint32_t tok = (uint32_t)min(16 * half + c, last);
 #pragma unroll
         for (int L = 0; L < G::KLOADS; L++)
-            o.k[half][L] = tok * row_bytes + (uint32_t)(4 * G::E * L + G::E * g) * G::EB;
+            r.k[half][L] = *(const u32x4_t *)(kt + tok * row_bytes + (uint32_t)(4 * G::E * L + G::E * g) * G::EB);
     }
 #pragma unroll
     for (int j = 0; j < 8; j++)
-        o.v[j] = (uint32_t)min(pv_token(g, j), last) * row_bytes + (uint32_t)(G::DT * c * G::EB);
-    o.s = (uint32_t)min(pv_token(g, c & 7), last) * (uint32_t)hkv;
-}
-
-template <int D, int KVT, int SCALE>
-__device__ __forceinline__ void load_tile(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
-                                          const uint8_t *kt, const uint8_t *vt, const float *st,
-                                          const LaneOffsets<Geometry<D, KVT>::KLOADS> &o) {
-    using G = Geometry<D, KVT>;
-#pragma unroll
-    for (int half = 0; half < 2; half++)
-#pragma unroll
-        for (int L = 0; L < G::KLOADS; L++) r.k[half][L] = *(const u32x4_t *)(kt + o.k[half][L]);
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint8_t *src = vt + o.v[j];
-        if constexpr (G::VDW == 4) {
-            const u32x4_t x = *(const u32x4_t *)src;
-            r.v[j][0] = x[0]; r.v[j][1] = x[1]; r.v[j][2] = x[2]; r.v[j][3] = x[3];
-        } else if constexpr (G::VDW == 2) {
-            const u32x2_t x = *(const u32x2_t *)src;
-            r.v[j][0] = x[0]; r.v[j][1] = x[1];
-        } else {
-            r.v[j][0] = *(const uint32_t *)src;
-        }
-    }
-    if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[o.s];
+        load_v_chunk<G::VDW>(r.v[j], vt + (uint32_t)min(pv_token(g, j), last) * row_bytes + (uint32_t)(G::DT * c * G::EB));
+    if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[(uint32_t)min(pv_token(g, c & 7), last) * (uint32_t)hkv];
 }
 
 template <int D, int KVT, int QT, int SCALE, bool PAGED>
@@ -284,47 +325,36 @@ void partition_kernel(Params p) {
     using G = Geometry<D, KVT>;
     constexpr int EB = G::EB, E = G::E, KSTEPS = G::KSTEPS, KLOADS = G::KLOADS, DT = G::DT, VDW = G::VDW;
     __shared__ float sh_scale_all[kMaxWavesPerGroup][64];
+    __shared__ int sh_prefix[kLdsBatch + 1];  // tiles of the sequences before b (b <= batch)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     float *sh_scale = sh_scale_all[wave];
     const int c = lane & 15, g = lane >> 4;
     const int64_t wg = blockIdx.x, W = gridDim.x;
     const int groups = p.groups;  // unit groups per sequence
+    const bool lds_prefix = p.batch <= kLdsBatch;
 
-    // ---- this workgroup's tile range [lo, hi) in the concatenation of all unit groups
-    const int64_t TT = total_seq_tiles(p, lane) * groups;
+    // ---- per-sequence tile prefix sums, once per workgroup (then every lookup is an LDS read)
+    if (lds_prefix) {
+        if (wave == 0) {
+            int base = 0;
+            for (int b0 = 0; b0 < p.batch; b0 += 64) {
+                const int bb = b0 + lane;
+                const int t = bb < p.batch ? seq_tiles(p, bb) : 0;
+                const int incl = wave_incl_scan(t, lane);
+                if (bb < p.batch) sh_prefix[bb] = base + incl - t;
+                base += __shfl(incl, 63, 64);
+            }
+            if (lane == 0) sh_prefix[p.batch] = base;
+        }
+        __syncthreads();
+    }
+
+    // ---- this workgroup's tile range [lo, hi) of the concatenation of all unit groups
+    const int64_t TT = uni(lds_prefix ? (int64_t)sh_prefix[p.batch] * groups : total_seq_tiles(p, lane) * groups);
     const Split sp = make_split(TT, W);
     const int64_t lo = split_lo(sp, wg), hi = split_lo(sp, wg + 1);
-    if (lo >= hi) return;
-
-    // ---- locate lo: sequence b with P_b * groups <= lo < (P_b + T_b) * groups
-    int b = 0, Tb = 0;
-    int64_t Pb = 0;
-    {
-        int64_t base = 0;
-        for (int b0 = 0; b0 < p.batch; b0 += 64) {
-            const int bb = b0 + lane;
-            const int t = bb < p.batch ? seq_tiles(p, bb) : 0;
-            const int incl = wave_incl_scan(t, lane);
-            const int64_t excl = base + incl - t;
-            const bool here = t > 0 && excl * groups <= lo && (excl + t) * groups > lo;
-            const uint64_t mask = __ballot(here);
-            if (mask) {
-                const int src = __builtin_ctzll(mask);
-                b = b0 + src;
-                Tb = __shfl(t, src, 64);
-                Pb = base + __shfl(incl, src, 64) - Tb;
-                break;
-            }
-            base += __shfl(incl, 63, 64);
-        }
-    }
-    if (Tb == 0) return;  // unreachable: some sequence owns tile lo
-    const int64_t rel = lo - Pb * groups;
-    int grp = (int)(rel / Tb);     // unit group within the sequence
-    int t_off = (int)(rel % Tb);   // first tile of the segment within the unit
-    int64_t pos = lo;
-    int seg_index = 0;
+    if (lo >= hi) return;  // every wave of the workgroup takes this branch together
 
     float tensor_k = 1.0f, tensor_v = 1.0f;
     if constexpr (SCALE == SC_TENSOR) {
@@ -333,152 +363,245 @@ void partition_kernel(Params p) {
     }
     const float qk_scale = p.qk_scale * tensor_k;
     const uint32_t row_bytes = (uint32_t)p.hkv * D * EB;  // bytes per cache row (all kv heads)
-    LaneOffsets<KLOADS> full;
-    lane_offsets<D, KVT>(full, g, c, row_bytes, p.hkv, kTile - 1);
+    const LaneOffsets lofs = lane_offsets<D, KVT>(g, c, row_bytes, p.hkv);
 
-    while (pos < hi) {
-        const int u_in = grp * p.wpg + wave;  // unit within the sequence: kvh * nhb + hb
-        const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
-        const int n = max(0, min(p.seq_len[b], p.max_seq_len));
-        const int seg_tiles = (int)min((int64_t)(Tb - t_off), hi - pos);
-        const bool whole = (t_off == 0) && (seg_tiles == Tb);
-        const int t_begin = t_off * kTile;
-        const int t_end = min(n, (t_off + seg_tiles) * kTile);
+    // ---- tile cursor.  Every wave of the workgroup walks the same tiles (its own unit of each
+    // unit group), so the cursor is identical across the waves.
+    int64_t pos = lo;
+    int b = 0, Tb = 0, grp = 0, tt = 0, seg = 0, seg_start = 0, n = 0;
 
-        const int hloc = hb * kHeadBlock + c;
-        const bool hvalid = hloc < p.group;
-        const int h = kvh * p.group + hloc;
-        const size_t orow = ((size_t)b * p.hq + h) * D;  // output row of head h
-
-        // q operand (B of q.k^T): column c = head hloc, k-slots of lane group g.
-        u32x4_t qop[KSTEPS];
-        {
-            const uint16_t *qrow = (const uint16_t *)p.q + orow;
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; kk++)
-                qop[kk] = hvalid ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
-        }
-
-        const uint8_t *kbase = (const uint8_t *)p.k + (size_t)kvh * D * EB;
-        const uint8_t *vbase = (const uint8_t *)p.v + (size_t)kvh * D * EB;
-        // lane 16g+i of a tile holds the k (i < 8) or v (i >= 8) scale of token pv_token(g, i & 7)
-        const float *sbase = nullptr;
-        if constexpr (SCALE == SC_TOKEN_HEAD) sbase = ((c & 8) ? p.v_scale : p.k_scale) + kvh;
-        const int32_t *btab = PAGED ? p.block_table + (size_t)b * p.max_blocks : nullptr;
-        const int64_t kv0 = PAGED ? 0 : (int64_t)p.kv_start[b];
-
-        // first cache row of the tile starting at token t0 (wave-uniform; a 32-token tile never
-        // straddles a 32/64-token block)
-        auto tile_row = [&](int t0) -> int64_t {
-            if constexpr (PAGED) return (int64_t)btab[t0 / p.block_size] * p.block_size + (t0 % p.block_size);
-            else return kv0 + t0;
-        };
-        auto issue = [&](TileRaw<KLOADS, VDW> &r, int t0) {
-            const int64_t row = tile_row(t0);
-            const uint8_t *kt = kbase + (size_t)row * row_bytes;
-            const uint8_t *vt = vbase + (size_t)row * row_bytes;
-            const float *st = nullptr;
-            if constexpr (SCALE == SC_TOKEN_HEAD) st = sbase + (size_t)row * p.hkv;
-            const int last = t_end - 1 - t0;
-            if (last >= kTile - 1) {
-                load_tile<D, KVT, SCALE>(r, kt, vt, st, full);
-            } else {
-                LaneOffsets<KLOADS> part;
-                lane_offsets<D, KVT>(part, g, c, row_bytes, p.hkv, last);
-                load_tile<D, KVT, SCALE>(r, kt, vt, st, part);
+    // place the cursor on global tile `at`
+    auto locate = [&](int64_t at) {
+        if (lds_prefix) {  // largest b with P_b * groups <= at; it owns a tile, so T_b > 0
+            int lo = 0, hi2 = p.batch;
+            while (hi2 - lo > 1) {
+                const int mid = (lo + hi2) >> 1;
+                if ((int64_t)sh_prefix[mid] * groups <= at) lo = mid;
+                else hi2 = mid;
             }
-        };
+            b = uni(lo);
+            const int64_t Pb = sh_prefix[b];
+            Tb = uni(sh_prefix[b + 1] - sh_prefix[b]);
+            const int64_t rel = at - Pb * groups;
+            grp = uni((int)(rel / Tb));
+            tt = uni((int)(rel % Tb));
+            n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
+            return;
+        }
+        int64_t base = 0;
+        Tb = 0;
+        for (int b0 = 0; b0 < p.batch; b0 += 64) {
+            const int bb = b0 + lane;
+            const int t = bb < p.batch ? seq_tiles(p, bb) : 0;
+            const int incl = wave_incl_scan(t, lane);
+            const int64_t excl = base + incl - t;
+            const bool here = t > 0 && excl * groups <= at && (excl + t) * groups > at;
+            const uint64_t mask = __ballot(here);
+            if (mask) {
+                const int src = __builtin_ctzll(mask);
+                b = uni(b0 + src);
+                Tb = uni(__shfl(t, src, 64));
+                const int64_t Pb = base + uni(__shfl(incl, src, 64)) - Tb;
+                const int64_t rel = at - Pb * groups;
+                grp = uni((int)(rel / Tb));
+                tt = uni((int)(rel % Tb));
+                break;
+            }
+            base += uni(__shfl(incl, 63, 64));
+        }
+        n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
+    };
+    struct Desc {
+        int64_t row0;             // first cache row of the tile
+        int b, u_in, t0, last;    // sequence, unit in sequence, first token, last valid token in tile
+        int seg;                  // segment index within the workgroup's range
+        bool first, lastseg, whole;
+    };
+    auto describe = [&](Desc &d) {
+        d.b = b;
+        d.u_in = grp * p.wpg + wave;
+        d.t0 = tt * kTile;
+        d.last = min(n - d.t0, kTile) - 1;
+        if constexpr (PAGED)
+            d.row0 = (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + d.t0 / p.block_size) *
+                         p.block_size + (d.t0 % p.block_size);
+        else
+            d.row0 = (int64_t)ld_uniform(p.kv_start, b) + d.t0;
+        d.seg = seg;
+        d.first = (tt == seg_start);
+        d.lastseg = (tt + 1 == Tb) || (pos + 1 == hi);
+        d.whole = (seg_start == 0) && (tt + 1 == Tb);
+    };
+    // advance the cursor one tile (crossing units and sequences); false at the end of the range
+    auto advance = [&](Desc &d) -> bool {
+        if (++pos == hi) return false;
+        if (++tt == Tb) {
+            tt = 0;
+            seg++;
+            seg_start = 0;
+            if (++grp == groups) {
+                grp = 0;
+                do {
+                    b++;
+                } while ((Tb = lds_prefix ? uni(sh_prefix[b + 1] - sh_prefix[b]) : seq_tiles_u(p, b)) == 0);
+                n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
+            }
+        }
+        describe(d);
+        return true;
+    };
 
-        f32x4_t acc[DT];
+    // ---- per-segment state
+    u32x4_t qop[KSTEPS];
+    f32x4_t acc[DT];
+    float m_run = -INFINITY, l_run = 0.0f;
+    auto begin_segment = [&](const Desc &d) {
+        const int kvh = d.u_in / p.nhb, hb = d.u_in % p.nhb;
+        const int hloc = hb * kHeadBlock + c;
+        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)d.b * p.hq + kvh * p.group + hloc) * D;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++)
+            qop[kk] = hloc < p.group ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < DT; i++) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        float m_run = -INFINITY, l_run = 0.0f;
+        m_run = -INFINITY;
+        l_run = 0.0f;
+    };
 
-        auto compute = [&](const TileRaw<KLOADS, VDW> &r, int t0) {
-            const int last = t_end - 1 - t0;  // last valid tile-relative token (>= 0)
-            // ---- per-token scales of the lane's 8 score slots, through LDS
-            float ksc[8], vsc[8];
-            if constexpr (SCALE == SC_TOKEN_HEAD) {
-                sh_scale[lane] = r.sc;
-                __builtin_amdgcn_wave_barrier();
-                const float4 k0 = *(const float4 *)&sh_scale[16 * g + 0];
-                const float4 k1 = *(const float4 *)&sh_scale[16 * g + 4];
-                const float4 v0 = *(const float4 *)&sh_scale[16 * g + 8];
-                const float4 v1 = *(const float4 *)&sh_scale[16 * g + 12];
-                __builtin_amdgcn_wave_barrier();
-                ksc[0] = k0.x; ksc[1] = k0.y; ksc[2] = k0.z; ksc[3] = k0.w;
-                ksc[4] = k1.x; ksc[5] = k1.y; ksc[6] = k1.z; ksc[7] = k1.w;
-                vsc[0] = v0.x; vsc[1] = v0.y; vsc[2] = v0.z; vsc[3] = v0.w;
-                vsc[4] = v1.x; vsc[5] = v1.y; vsc[6] = v1.z; vsc[7] = v1.w;
+    auto issue = [&](TileRaw<KLOADS, VDW> &r, const Desc &d) {
+        const int kvh = d.u_in / p.nhb;
+        const uint8_t *kt = (const uint8_t *)p.k + (size_t)kvh * D * EB + (size_t)d.row0 * row_bytes;
+        const uint8_t *vt = (const uint8_t *)p.v + (size_t)kvh * D * EB + (size_t)d.row0 * row_bytes;
+        const float *st = nullptr;
+        // lane 16g+i holds the k (i < 8) or v (i >= 8) scale of token pv_token(g, i & 7)
+        if constexpr (SCALE == SC_TOKEN_HEAD) st = ((c & 8) ? p.v_scale : p.k_scale) + kvh + (size_t)d.row0 * p.hkv;
+        if (d.last >= kTile - 1) load_tile<D, KVT, SCALE>(r, kt, vt, st, lofs, row_bytes);
+        else load_tile_part<D, KVT, SCALE>(r, kt, vt, st, g, c, row_bytes, p.hkv, d.last);
+    };
+
+    auto compute = [&](const TileRaw<KLOADS, VDW> &r, const Desc &d) {
+        const int last = d.last;  // last valid tile-relative token (>= 0)
+        // ---- per-token scales of the lane's 8 score slots, through LDS
+        float ksc[8], vsc[8];
+        if constexpr (SCALE == SC_TOKEN_HEAD) {
+            sh_scale[lane] = r.sc;
+            __builtin_amdgcn_wave_barrier();
+            const float4 k0 = *(const float4 *)&sh_scale[16 * g + 0];
+            const float4 k1 = *(const float4 *)&sh_scale[16 * g + 4];
+            const float4 v0 = *(const float4 *)&sh_scale[16 * g + 8];
+            const float4 v1 = *(const float4 *)&sh_scale[16 * g + 12];
+            __builtin_amdgcn_wave_barrier();
+            ksc[0] = k0.x; ksc[1] = k0.y; ksc[2] = k0.z; ksc[3] = k0.w;
+            ksc[4] = k1.x; ksc[5] = k1.y; ksc[6] = k1.z; ksc[7] = k1.w;
+            vsc[0] = v0.x; vsc[1] = v0.y; vsc[2] = v0.z; vsc[3] = v0.w;
+            vsc[4] = v1.x; vsc[5] = v1.y; vsc[6] = v1.z; vsc[7] = v1.w;
+        }
+
+        // ---- scores: S[token][head] = K . q over two 16-token halves
+        f32x4_t sacc[2];
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            sacc[half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++) {
+                u32x4_t a;
+                if constexpr (KVT == KV_FP8) {
+                    const u32x4_t wv = r.k[half][kk / 2];
+                    const uint32_t w0 = wv[2 * (kk % 2)], w1 = wv[2 * (kk % 2) + 1];
+                    a = u32x4_t{cvt_fp8x2<QT, false>(w0), cvt_fp8x2<QT, true>(w0),
+                                cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
+                } else {
+                    a = r.k[half][kk];
+                }
+                sacc[half] = mfma_qk<QT>(a, qop[kk], sacc[half]);
             }
+        }
 
-            // ---- scores: S[token][head] = K . q over two 16-token halves
-            f32x4_t sacc[2];
+        // ---- online softmax (log2 units)
+        float s[8];
 #pragma unroll
-            for (int half = 0; half < 2; half++) {
-                sacc[half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 8; j++) {
+            float x = sacc[j >> 2][j & 3];
+            if constexpr (SCALE == SC_TOKEN_HEAD) x *= ksc[j] * p.qk_scale;
+            else x *= qk_scale;
+            s[j] = x;
+        }
+        if (last < kTile - 1) {
 #pragma unroll
-                for (int kk = 0; kk < KSTEPS; kk++) {
-                    u32x4_t a;
-                    if constexpr (KVT == KV_FP8) {
-                        const u32x4_t wv = r.k[half][kk / 2];
-                        const uint32_t w0 = wv[2 * (kk % 2)], w1 = wv[2 * (kk % 2) + 1];
-                        a = u32x4_t{cvt_fp8x2<QT, false>(w0), cvt_fp8x2<QT, true>(w0),
-                                    cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
-                    } else {
-                        a = r.k[half][kk];
+            for (int j = 0; j < 8; j++) s[j] = (pv_token(g, j) <= last) ? s[j] : -INFINITY;
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int j = 1; j < 8; j++) mt = fmaxf(mt, s[j]);
+        mt = fmaxf(mt, shfl_xor_f(mt, 16));
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        // rescale only when some head's running max grows (wave-uniform branch)
+        if (__any(mt > m_run)) {
+            const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DT; i++) acc[i] *= alpha;
+            m_run = m_new;
+        }
+        float pj[8], psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            pj[j] = __builtin_amdgcn_exp2f(s[j] - m_run);
+            psum += pj[j];
+        }
+        l_run += psum;
+
+        // ---- p.V
+        if constexpr (KVT == KV_BF16) {
+            uint32_t hi2[4], lo2[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t h0 = f32_to_bf16_bits(pj[2 * u]), h1 = f32_to_bf16_bits(pj[2 * u + 1]);
+                const float r0 = pj[2 * u] - __builtin_bit_cast(float, h0 << 16);
+                const float r1 = pj[2 * u + 1] - __builtin_bit_cast(float, h1 << 16);
+                hi2[u] = h0 | (h1 << 16);
+                lo2[u] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+            }
+            const u32x4_t phi = {hi2[0], hi2[1], hi2[2], hi2[3]}, plo = {lo2[0], lo2[1], lo2[2], lo2[3]};
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                uint32_t a[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    a[u] = __builtin_amdgcn_perm(r.v[2 * u + 1][dt >> 1], r.v[2 * u][dt >> 1],
+                                                 (dt & 1) ? 0x07060302u : 0x05040100u);
+                const u32x4_t av = {a[0], a[1], a[2], a[3]};
+                acc[dt] = mfma_bf16(av, phi, acc[dt]);
+                acc[dt] = mfma_bf16(av, plo, acc[dt]);
+            }
+        } else {
+            uint32_t pp[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                float p0 = pj[2 * u], p1 = pj[2 * u + 1];
+                if constexpr (SCALE == SC_TOKEN_HEAD) { p0 *= vsc[2 * u]; p1 *= vsc[2 * u + 1]; }
+                pp[u] = pack_f16(p0, p1);
+            }
+            const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
+            if constexpr (KVT == KV_FP8) {
+#pragma unroll
+                for (int wd = 0; wd < VDW; wd++) {
+                    uint32_t a[4][4];
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        const uint32_t x = __builtin_amdgcn_perm(r.v[2 * u + 1][wd], r.v[2 * u][wd], 0x05010400u);
+                        const uint32_t y = __builtin_amdgcn_perm(r.v[2 * u + 1][wd], r.v[2 * u][wd], 0x07030602u);
+                        a[0][u] = cvt_fp8x2<KV_F16, false>(x);
+                        a[1][u] = cvt_fp8x2<KV_F16, true>(x);
+                        a[2][u] = cvt_fp8x2<KV_F16, false>(y);
+                        a[3][u] = cvt_fp8x2<KV_F16, true>(y);
                     }
-                    sacc[half] = mfma_qk<QT>(a, qop[kk], sacc[half]);
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        acc[4 * wd + k] = mfma_f16(u32x4_t{a[k][0], a[k][1], a[k][2], a[k][3]}, pop, acc[4 * wd + k]);
                 }
-            }
-
-            // ---- online softmax (log2 units)
-            float s[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                float x = sacc[j >> 2][j & 3];
-                if constexpr (SCALE == SC_TOKEN_HEAD) x *= ksc[j] * p.qk_scale;
-                else x *= qk_scale;
-                s[j] = x;
-            }
-            if (last < kTile - 1) {
-#pragma unroll
-                for (int j = 0; j < 8; j++) s[j] = (pv_token(g, j) <= last) ? s[j] : -INFINITY;
-            }
-            float mt = s[0];
-#pragma unroll
-            for (int j = 1; j < 8; j++) mt = fmaxf(mt, s[j]);
-            mt = fmaxf(mt, shfl_xor_f(mt, 16));
-            mt = fmaxf(mt, shfl_xor_f(mt, 32));
-            // rescale only when some head's running max grows (wave-uniform branch)
-            if (__any(mt > m_run)) {
-                const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < DT; i++) acc[i] *= alpha;
-                m_run = m_new;
-            }
-            float pj[8], psum = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                pj[j] = __builtin_amdgcn_exp2f(s[j] - m_run);
-                psum += pj[j];
-            }
-            l_run += psum;
-
-            // ---- p.V
-            if constexpr (KVT == KV_BF16) {
-                uint32_t hi2[4], lo2[4];
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const uint32_t h0 = f32_to_bf16_bits(pj[2 * u]), h1 = f32_to_bf16_bits(pj[2 * u + 1]);
-                    const float r0 = pj[2 * u] - __builtin_bit_cast(float, h0 << 16);
-                    const float r1 = pj[2 * u + 1] - __builtin_bit_cast(float, h1 << 16);
-                    hi2[u] = h0 | (h1 << 16);
-                    lo2[u] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-                }
-                const u32x4_t phi = {hi2[0], hi2[1], hi2[2], hi2[3]}, plo = {lo2[0], lo2[1], lo2[2], lo2[3]};
+            } else {
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) {
                     uint32_t a[4];
@@ -486,109 +609,76 @@ void partition_kernel(Params p) {
                     for (int u = 0; u < 4; u++)
                         a[u] = __builtin_amdgcn_perm(r.v[2 * u + 1][dt >> 1], r.v[2 * u][dt >> 1],
                                                      (dt & 1) ? 0x07060302u : 0x05040100u);
-                    const u32x4_t av = {a[0], a[1], a[2], a[3]};
-                    acc[dt] = mfma_bf16(av, phi, acc[dt]);
-                    acc[dt] = mfma_bf16(av, plo, acc[dt]);
-                }
-            } else {
-                uint32_t pp[4];
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    float p0 = pj[2 * u], p1 = pj[2 * u + 1];
-                    if constexpr (SCALE == SC_TOKEN_HEAD) { p0 *= vsc[2 * u]; p1 *= vsc[2 * u + 1]; }
-                    pp[u] = pack_f16(p0, p1);
-                }
-                const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
-                if constexpr (KVT == KV_FP8) {
-#pragma unroll
-                    for (int wd = 0; wd < VDW; wd++) {
-                        uint32_t a[4][4];
-#pragma unroll
-                        for (int u = 0; u < 4; u++) {
-                            const uint32_t x = __builtin_amdgcn_perm(r.v[2 * u + 1][wd], r.v[2 * u][wd], 0x05010400u);
-                            const uint32_t y = __builtin_amdgcn_perm(r.v[2 * u + 1][wd], r.v[2 * u][wd], 0x07030602u);
-                            a[0][u] = cvt_fp8x2<KV_F16, false>(x);
-                            a[1][u] = cvt_fp8x2<KV_F16, true>(x);
-                            a[2][u] = cvt_fp8x2<KV_F16, false>(y);
-                            a[3][u] = cvt_fp8x2<KV_F16, true>(y);
-                        }
-#pragma unroll
-                        for (int k = 0; k < 4; k++)
-                            acc[4 * wd + k] = mfma_f16(u32x4_t{a[k][0], a[k][1], a[k][2], a[k][3]}, pop, acc[4 * wd + k]);
-                    }
-                } else {
-#pragma unroll
-                    for (int dt = 0; dt < DT; dt++) {
-                        uint32_t a[4];
-#pragma unroll
-                        for (int u = 0; u < 4; u++)
-                            a[u] = __builtin_amdgcn_perm(r.v[2 * u + 1][dt >> 1], r.v[2 * u][dt >> 1],
-                                                         (dt & 1) ? 0x07060302u : 0x05040100u);
-                        acc[dt] = mfma_f16(u32x4_t{a[0], a[1], a[2], a[3]}, pop, acc[dt]);
-                    }
+                    acc[dt] = mfma_f16(u32x4_t{a[0], a[1], a[2], a[3]}, pop, acc[dt]);
                 }
             }
-        };
-
-        // ---- tile loop: two register sets, the next tile's loads in flight while computing
-        TileRaw<KLOADS, VDW> ra, rb;
-        int t0 = t_begin;
-        issue(ra, t0);
-        while (true) {
-            if (t0 + kTile < t_end) issue(rb, t0 + kTile);
-            compute(ra, t0);
-            t0 += kTile;
-            if (t0 >= t_end) break;
-            if (t0 + kTile < t_end) issue(ra, t0 + kTile);
-            compute(rb, t0);
-            t0 += kTile;
-            if (t0 >= t_end) break;
         }
+    };
 
-        // ---- segment result: total running sum over the four lane groups of head c
+    // ---- segment result: total running sum over the four lane groups of head c
+    auto finalize = [&](const Desc &d) {
+        const int kvh = d.u_in / p.nhb, hb = d.u_in % p.nhb;
+        const int hloc = hb * kHeadBlock + c;
+        const bool hvalid = hloc < p.group;
+        const int h = kvh * p.group + hloc;
         float l_tot = l_run + shfl_xor_f(l_run, 16);
         l_tot += shfl_xor_f(l_tot, 32);
-        if constexpr (SCALE == SC_TENSOR) {
+        f32x4_t o[DT];
 #pragma unroll
-            for (int i = 0; i < DT; i++) acc[i] *= tensor_v;
-        }
-        // lane (g, c) holds d = DT*(4g + r) + dt in acc[dt][r]
-        if (whole) {
+        for (int i = 0; i < DT; i++) o[i] = (SCALE == SC_TENSOR) ? acc[i] * tensor_v : acc[i];
+        // lane (g, c) holds d = DT*(4g + r) + dt in o[dt][r]
+        if (d.whole) {
             if (hvalid) {
+                const size_t orow = ((size_t)d.b * p.hq + h) * D;
                 const float inv = 1.0f / l_tot;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     float v[DT];
 #pragma unroll
-                    for (int dt = 0; dt < DT; dt++) v[dt] = acc[dt][r] * inv;
+                    for (int dt = 0; dt < DT; dt++) v[dt] = o[dt][r] * inv;
                     store_row_chunk<DT>(p.out, p.out_dtype, orow + DT * (4 * g + r), v);
                 }
-                if (p.lse && g == 0) p.lse[(size_t)b * p.hq + h] = (m_run + log2f(l_tot)) * kLn2;
+                if (p.lse && g == 0) p.lse[(size_t)d.b * p.hq + h] = (m_run + log2f(l_tot)) * kLn2;
             }
         } else if (hvalid) {
-            // slot 0: the workgroup's first segment; slot 1: its last (a middle one is always whole)
-            const size_t slot = (((size_t)wg * 2 + (seg_index == 0 ? 0 : 1)) * p.wpg + wave) * kHeadBlock + c;
+            // slot 0: the range's first segment; slot 1: its last (a middle one is always whole)
+            const size_t slot = (((size_t)wg * 2 + (d.seg == 0 ? 0 : 1)) * p.wpg + wave) * kHeadBlock + c;
             float *dst = p.ws_acc + slot * D;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
 #pragma unroll
                 for (int dt = 0; dt < DT; dt += 4)
                     *(float4 *)(dst + DT * (4 * g + r) + dt) =
-                        make_float4(acc[dt][r], acc[dt + 1][r], acc[dt + 2][r], acc[dt + 3][r]);
+                        make_float4(o[dt][r], o[dt + 1][r], o[dt + 2][r], o[dt + 3][r]);
             }
             if (g == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
         }
+    };
 
-        // ---- next segment: next unit group of this sequence, else the next non-empty sequence
-        pos += seg_tiles;
-        seg_index++;
-        t_off = 0;
-        if (++grp == groups) {
-            grp = 0;
-            do {
-                b++;
-            } while (pos < hi && (Tb = seq_tiles(p, b)) == 0);
-        }
+    // ---- start
+    locate(lo);
+    seg_start = tt;
+
+    // ---- tile stream: two register sets; the next tile's loads (possibly of the next unit or
+    // sequence) are in flight while the current one is computed
+    TileRaw<KLOADS, VDW> ra, rb;
+    Desc da, db;
+    describe(da);
+    issue(ra, da);
+    begin_segment(da);
+    for (;;) {
+        bool more = advance(db);
+        if (more) issue(rb, db);
+        compute(ra, da);
+        if (da.lastseg) finalize(da);
+        if (!more) break;
+        if (db.first) begin_segment(db);
+        more = advance(da);
+        if (more) issue(ra, da);
+        compute(rb, db);
+        if (db.lastseg) finalize(db);
+        if (!more) break;
+        if (da.first) begin_segment(da);
     }
 }
 
@@ -646,8 +736,10 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     const Split sp = make_split(TT, p.nparts);
     const int64_t wlo = split_owner(sp, U0), whi = split_owner(sp, U0 + Tb - 1);
     if (wlo == whi) return;  // finished by the partition kernel
+    // pieces: the ranges wlo..whi in order (never empty: with fewer tiles than workgroups every
+    // non-empty range holds one tile and split_owner(t) = t)
     const int np = (int)(whi - wlo + 1);
-    const int first_slot = split_lo(sp, wlo) == U0 ? 0 : 1;
+    const int first_slot = split_lo(sp, wlo) == U0 ? 0 : 1;  // unit began inside wlo's range
     auto slot_of = [&](int i) -> size_t {
         return (((size_t)(wlo + i) * 2 + (i == 0 ? first_slot : 0)) * p.wpg + wave) * kHeadBlock + c;
     };

@@ -69,9 +69,9 @@ typedef enum {
  *
  * Work split: every (sequence, kv head, block of <= 16 query heads) "unit" owns
  * ceil(seq_len / 32) tiles of 32 tokens; the units' tiles are concatenated and cut into
- * `num_partitions` equal ranges, one per wave of the partition kernel, so long and short
- * sequences are balanced without any host-side knowledge of seq_len.  A unit cut by a range
- * boundary leaves partial (max, sum, accumulator) states that the combine kernel merges.
+ * `num_partitions` equal ranges, one per partition workgroup, so long and short sequences are
+ * balanced without any host-side knowledge of seq_len.  A unit cut by a range boundary leaves
+ * partial (max, sum, accumulator) states that the combine kernel merges in a fixed order.
  *
  *   q            [batch][num_q_heads][head_dim], q_dtype (FD_F16 or FD_BF16), contiguous.
  *   k_cache,     paged mode:      [num_blocks][block_size][num_kv_heads][head_dim]
@@ -122,7 +122,7 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
 
 /*
  * fd_workspace_bytes -- workspace size fd_decode_attention needs for these sizes (partial
- * states: 2 slots x 16 heads x (head_dim + 2) fp32 per partition).  The same arguments must
+ * states: 2 slots x 16 heads x (head_dim + 2) fp32 per partition and unit of a group).  The same arguments must
  * be passed to fd_decode_attention.  Returns (size_t)-1 for arguments fd_decode_attention
  * would reject as invalid.
  */
