@@ -452,20 +452,28 @@ void partition_kernel(Params p) {
     };
 
     // ---- per-segment state
-    u32x4_t qop[KSTEPS];
+    u32x4_t qop[KSTEPS], qnext[KSTEPS];  // q operand of the current segment / of the next one
     f32x4_t acc[DT];
     float m_run = -INFINITY, l_run = 0.0f;
-    auto begin_segment = [&](const Desc &d) {
+    // q operand (B of q.k^T) of segment d's unit: column c = head hloc, k-slots of lane group g
+    auto load_q = [&](u32x4_t (&dst)[KSTEPS], const Desc &d) {
         const int kvh = d.u_in / p.nhb, hb = d.u_in % p.nhb;
         const int hloc = hb * kHeadBlock + c;
         const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)d.b * p.hq + kvh * p.group + hloc) * D;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; kk++)
-            qop[kk] = hloc < p.group ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
+            dst[kk] = hloc < p.group ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
+    };
+    auto reset_state = [&]() {
 #pragma unroll
         for (int i = 0; i < DT; i++) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;
         l_run = 0.0f;
+    };
+    auto next_segment = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) qop[kk] = qnext[kk];
+        reset_state();
     };
 
     auto issue = [&](TileRaw<KLOADS, VDW> &r, const Desc &d) {
@@ -661,24 +669,32 @@ void partition_kernel(Params p) {
 
     // ---- tile stream: two register sets; the next tile's loads (possibly of the next unit or
     // sequence) are in flight while the current one is computed
+    // (a new segment's q operand is loaded together with its first tile)
     TileRaw<KLOADS, VDW> ra, rb;
     Desc da, db;
     describe(da);
     issue(ra, da);
-    begin_segment(da);
+    load_q(qop, da);
+    reset_state();
     for (;;) {
         bool more = advance(db);
-        if (more) issue(rb, db);
+        if (more) {
+            issue(rb, db);
+            if (db.first) load_q(qnext, db);
+        }
         compute(ra, da);
         if (da.lastseg) finalize(da);
         if (!more) break;
-        if (db.first) begin_segment(db);
+        if (db.first) next_segment();
         more = advance(da);
-        if (more) issue(ra, da);
+        if (more) {
+            issue(ra, da);
+            if (da.first) load_q(qnext, da);
+        }
         compute(rb, db);
         if (db.lastseg) finalize(db);
         if (!more) break;
-        if (da.first) begin_segment(da);
+        if (da.first) next_segment();
     }
 }
 
