@@ -22,11 +22,19 @@ inline long cdiv(long a, long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
+    bool wide;   // wide-group kernel (32-head blocks, LDS-shared tiles)
+    int hb;      // heads per head block
     int nhb;     // head blocks per kv head
     int wpg;     // waves per partition workgroup (units processed side by side)
     int groups;  // unit groups per sequence
     int nparts;  // partition workgroups
 };
+
+// Groups of 64+ query heads per kv head with E4M3 KV and head_dim 128 take the wide-group
+// kernel: 32 heads per wave, and 2 or 4 waves of one kv head share every K/V tile through LDS.
+bool use_wide(int group, int head_dim, int kv_dtype) {
+    return kv_dtype == FD_FP8_E4M3 && head_dim == 128 && group % 64 == 0;
+}
 
 bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
     if (batch <= 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0) return false;
@@ -37,18 +45,27 @@ bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
 }
 
 // Units per sequence (kv head x head block) are grouped `wpg` at a time, wpg the largest
-// divisor of their count up to 8; workgroup w of the partition kernel takes tiles
-// [w*q + min(w, r), ...) of the concatenation of all unit groups (TT tiles of 32 tokens).
-// The workgroup count is capped by the largest TT the sizes allow.
-Plan make_plan(int batch, int hq, int hkv, int max_seq_len, int num_partitions) {
+// divisor of their count up to 8 (wide kernel: 4 or 2 head blocks of one kv head); workgroup w
+// of the partition kernel takes tiles [w*q + min(w, r), ...) of the concatenation of all unit
+// groups (TT tiles of 32 tokens).  The workgroup count is capped by the largest TT the sizes allow.
+Plan make_plan(int batch, int hq, int hkv, int head_dim, int kv_dtype, int max_seq_len, int num_partitions) {
     Plan pl;
     const int group = hq / hkv;
-    pl.nhb = (int)cdiv(group, fd::kHeadBlock);
-    const long ups = (long)hkv * pl.nhb;
-    pl.wpg = 1;
-    for (int d = fd::kMaxWavesPerGroup; d >= 1; d--)
-        if (ups % d == 0) { pl.wpg = d; break; }
-    pl.groups = (int)(ups / pl.wpg);
+    pl.wide = use_wide(group, head_dim, kv_dtype);
+    if (pl.wide) {
+        pl.hb = fd::kWideHeadBlock;
+        pl.nhb = group / pl.hb;
+        pl.wpg = pl.nhb % 4 == 0 ? 4 : 2;
+        pl.groups = hkv * pl.nhb / pl.wpg;
+    } else {
+        pl.hb = fd::kHeadBlock;
+        pl.nhb = (int)cdiv(group, pl.hb);
+        const long ups = (long)hkv * pl.nhb;
+        pl.wpg = 1;
+        for (int d = fd::kMaxWavesPerGroup; d >= 1; d--)
+            if (ups % d == 0) { pl.wpg = d; break; }
+        pl.groups = (int)(ups / pl.wpg);
+    }
     const long tt_max = (long)batch * pl.groups * cdiv(max_seq_len, fd::kTile);
     long W = num_partitions > 0 ? num_partitions : kDefaultWaves / pl.wpg;
     if (W > tt_max) W = tt_max;
@@ -58,7 +75,7 @@ Plan make_plan(int batch, int hq, int hkv, int max_seq_len, int num_partitions) 
 }
 
 // Workspace: [ml slots][acc slots]; one slot pair per partition per unit of a group per head.
-size_t ws_slots(const Plan &pl) { return (size_t)pl.nparts * 2 * pl.wpg * fd::kHeadBlock; }
+size_t ws_slots(const Plan &pl) { return (size_t)pl.nparts * 2 * pl.wpg * pl.hb; }
 
 size_t ws_bytes(const Plan &pl, int head_dim) {
     const size_t slots = ws_slots(pl);
@@ -85,18 +102,16 @@ const char *fd_status_string(int status) {
 int fd_plan_partitions(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
                        int block_size, int kv_dtype, int num_partitions) {
     (void)block_size;
-    (void)kv_dtype;
     if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_partitions < 0) return -1;
-    return make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_partitions).nparts;
+    return make_plan(batch, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len, num_partitions).nparts;
 }
 
 size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
                           int block_size, int kv_dtype, int num_partitions) {
     (void)block_size;
-    (void)kv_dtype;
     if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_partitions < 0)
         return (size_t)-1;
-    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_partitions);
+    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len, num_partitions);
     return ws_bytes(pl, head_dim);
 }
 
@@ -133,7 +148,7 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
         if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
         if ((long)max_seq_len > (long)max_blocks_per_seq * block_size) return FD_ERR_INVALID_ARG;
     }
-    const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, max_seq_len, num_partitions);
+    const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len, num_partitions);
     const size_t need = ws_bytes(pl, head_dim);
     if (!workspace || workspace_bytes < need) return FD_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255) return FD_ERR_WORKSPACE;
@@ -158,6 +173,7 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     p.max_blocks = block_table ? max_blocks_per_seq : 0;
     p.max_seq_len = max_seq_len;
     p.group = num_q_heads / num_kv_heads;
+    p.hb = pl.hb;
     p.nhb = pl.nhb;
     p.wpg = pl.wpg;
     p.groups = pl.groups;
@@ -171,7 +187,9 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     }
 
     if (t_prof_begin) (void)hipEventRecord(t_prof_begin, stream);
-    if (fd::launch_partition(p, kv_dtype, q_dtype, scale_mode, stream) != hipSuccess) return FD_ERR_LAUNCH;
+    const hipError_t perr = pl.wide ? fd::launch_wide_partition(p, q_dtype, scale_mode, stream)
+                                    : fd::launch_partition(p, kv_dtype, q_dtype, scale_mode, stream);
+    if (perr != hipSuccess) return FD_ERR_LAUNCH;
     if (t_prof_end) (void)hipEventRecord(t_prof_end, stream);
     if (fd::launch_combine(p, stream) != hipSuccess) return FD_ERR_LAUNCH;
     return FD_OK;

@@ -1,0 +1,191 @@
+// fd_device.h -- gfx950 device helpers shared by the flash-decoding kernels: vector types,
+// MFMA wrappers, E4M3 conversion, wave-uniform loads, output stores and the balanced split of a
+// step's KV tiles over partition workgroups.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fd_internal.h"
+
+namespace fd {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+enum { KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3 };
+enum { SC_NONE = 0, SC_TENSOR = 1, SC_TOKEN_HEAD = 2 };
+
+constexpr float kLn2 = 0.69314718055994530942f;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// ---------------------------------------------------------------- small helpers
+template <int QT>
+__device__ __forceinline__ f32x4_t mfma_qk(u32x4_t a, u32x4_t b, f32x4_t c) {
+    if constexpr (QT == KV_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two E4M3 bytes (bytes 0,1 or 2,3 of w) -> two values of type QT packed in one dword.
+// Exact: every E4M3 value is representable in f16 and bf16.
+template <int QT, bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t w) {
+    if constexpr (QT == KV_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    f16x2_t v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Scalar load of a wave-uniform int32 the kernel never writes (seq_len, block table, kv start):
+// through the constant address space, so it is an s_load, independent of the vector-memory
+// counter that the KV prefetch uses.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t *ptr, size_t i) {
+    return *((const __attribute__((address_space(4))) int32_t *)ptr + i);
+}
+
+// Wave-uniform copies (the value is the same in every lane; this keeps it in scalar registers
+// so that loads addressed by it are scalar loads, counted apart from the KV vector loads).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// 32x32x16 MFMA (one wave): A = 32 rows x 16 k, B = 16 k x 32 columns, C 32 x 32.
+// Lane l holds A[l % 32][8*(l/32) + 0..7] and B[8*(l/32) + 0..7][l % 32]; C register r of lane l
+// is C[8*(r/4) + 4*(l/32) + r%4][l % 32].
+template <int QT>
+__device__ __forceinline__ f32x16_t mfma32_qk(u32x4_t a, u32x4_t b, f32x16_t c) {
+    if constexpr (QT == KV_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32_f16(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Store DT consecutive output elements starting at element `d0` of row `dst`.
+template <int DT>
+__device__ __forceinline__ void store_row_chunk(void *out, int out_dtype, size_t base, const float *v) {
+    if (out_dtype == 0) {
+        float *o = (float *)out + base;
+#pragma unroll
+        for (int i = 0; i < DT; i += 4) *(float4 *)(o + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    } else if (out_dtype == 1) {
+        uint32_t w[DT / 2];
+#pragma unroll
+        for (int i = 0; i < DT / 2; i++) w[i] = pack_f16(v[2 * i], v[2 * i + 1]);
+        uint16_t *o = (uint16_t *)out + base;
+        if constexpr (DT == 8) *(u32x4_t *)o = u32x4_t{w[0], w[1], w[2], w[3]};
+        else *(u32x2_t *)o = u32x2_t{w[0], w[1]};
+    } else {
+        uint32_t w[DT / 2];
+#pragma unroll
+        for (int i = 0; i < DT / 2; i++)
+            w[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
+        uint16_t *o = (uint16_t *)out + base;
+        if constexpr (DT == 8) *(u32x4_t *)o = u32x4_t{w[0], w[1], w[2], w[3]};
+        else *(u32x2_t *)o = u32x2_t{w[0], w[1]};
+    }
+}
+
+// ---------------------------------------------------------------- work split helpers
+//
+// Balanced split of one step's KV work.  A *unit* is (sequence b, kv head, head block): the
+// G <= 16 query heads of one head block that share one kv head.  The units of a sequence are
+// taken in groups of `wpg` by the `wpg` waves of one workgroup (wave i takes unit grp*wpg + i),
+// so the waves of a workgroup stream the same token rows of the cache at the same time.
+// Unit group (b, grp) owns T_b = ceil(seq_len[b] / 32) tiles; groups are concatenated
+// sequence-major into TT tiles, and workgroup w of W takes tiles [lo_w, lo_{w+1}) with
+// lo_w = w*q + min(w, r), q = TT / W, r = TT % W: every workgroup gets the same amount of KV
+// (up to one tile) whatever the length mix.  A group cut by workgroup boundaries leaves one
+// partial state per piece: slot 0 of a workgroup holds its first piece, slot 1 its last one.
+
+__device__ __forceinline__ int seq_tiles(const Params &p, int b) {
+    int n = p.seq_len[b];
+    n = max(0, min(n, p.max_seq_len));
+    return (n + kTile - 1) / kTile;
+}
+
+// Same, for a wave-uniform b (scalar load).
+__device__ __forceinline__ int seq_tiles_u(const Params &p, int b) {
+    int n = ld_uniform(p.seq_len, b);
+    n = max(0, min(n, p.max_seq_len));
+    return (n + kTile - 1) / kTile;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+struct Split {
+    int64_t q, r;
+};
+
+__device__ __forceinline__ Split make_split(int64_t TT, int64_t W) { return Split{TT / W, TT % W}; }
+
+__device__ __forceinline__ int64_t split_lo(const Split &s, int64_t w) { return w * s.q + min(w, s.r); }
+
+// Workgroup whose range holds tile t (0 <= t < TT).
+__device__ __forceinline__ int64_t split_owner(const Split &s, int64_t t) {
+    const int64_t big = s.r * (s.q + 1);
+    return t < big ? t / (s.q + 1) : s.r + (t - big) / s.q;
+}
+
+// Total tiles over all sequences (one unit group each); every lane gets the same value.
+__device__ __forceinline__ int64_t total_seq_tiles(const Params &p, int lane) {
+    int64_t tot = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        int t = b < p.batch ? seq_tiles(p, b) : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+        tot += t;
+    }
+    return tot;
+}
+
+
+}  // namespace fd

@@ -8,8 +8,10 @@ namespace fd {
 
 // Tokens per wave tile: two 16-row MFMA blocks for q.k^T, one 32-deep MFMA step for p.V.
 constexpr int kTile = 32;
-// Heads per MFMA column block (a GQA group wider than this takes several head blocks).
+// Heads per MFMA column block (a GQA group wider than this takes several head blocks): 16 for
+// the 16x16x32 partition kernel, 32 for the wide-group kernel (32x32x16 MFMA, LDS-shared tiles).
 constexpr int kHeadBlock = 16;
+constexpr int kWideHeadBlock = 32;
 // Most waves (units of one sequence) a partition workgroup runs side by side.
 constexpr int kMaxWavesPerGroup = 8;
 // Largest batch whose per-sequence tile prefix sums a partition workgroup keeps in LDS.
@@ -26,13 +28,14 @@ struct Params {
     const float *v_scale;
     void *out;
     float *lse;
-    float *ws_acc;   // [nparts][2][wpg][kHeadBlock][d]  unnormalised partial outputs
-    float2 *ws_ml;   // [nparts][2][wpg][kHeadBlock]     (running max in log2 units, running sum)
+    float *ws_acc;   // [nparts][2][wpg][hb][d]  unnormalised partial outputs
+    float2 *ws_ml;   // [nparts][2][wpg][hb]     (running max in log2 units, running sum)
     int batch, hq, hkv, d;
     int block_size, max_blocks;
     int max_seq_len;  // host bound; seq_len values above it are clamped (never read past it)
     int group;        // hq / hkv
-    int nhb;          // head blocks per kv head: ceil(group / kHeadBlock)
+    int hb;           // heads per head block (kHeadBlock or kWideHeadBlock)
+    int nhb;          // head blocks per kv head: ceil(group / hb)
     int wpg;          // waves per partition workgroup = units per unit group (divides hkv*nhb)
     int groups;       // unit groups per sequence: hkv * nhb / wpg
     int nparts;       // partition workgroups (equal shares of the step's tiles)
@@ -44,6 +47,9 @@ struct Params {
 hipError_t launch_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode,
                             hipStream_t stream);
 hipError_t launch_combine(const Params &p, hipStream_t stream);
+// Wide-group variant (defined in fd_wide.hip): E4M3 KV, head_dim 128, hb = kWideHeadBlock,
+// wpg 2 or 4 head blocks of one kv head per workgroup.
+hipError_t launch_wide_partition(const Params &p, int q_dtype, int scale_mode, hipStream_t stream);
 hipError_t launch_fp8_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
 hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, hipStream_t stream);
 

@@ -32,82 +32,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "fd_internal.h"
+#include "fd_device.h"
 
 namespace fd {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-
-enum { KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3 };
-enum { SC_NONE = 0, SC_TENSOR = 1, SC_TOKEN_HEAD = 2 };
-
-constexpr float kLn2 = 0.69314718055994530942f;
-
-// ---------------------------------------------------------------- small helpers
-template <int QT>
-__device__ __forceinline__ f32x4_t mfma_qk(u32x4_t a, u32x4_t b, f32x4_t c) {
-    if constexpr (QT == KV_BF16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// Two E4M3 bytes (bytes 0,1 or 2,3 of w) -> two values of type QT packed in one dword.
-// Exact: every E4M3 value is representable in f16 and bf16.
-template <int QT, bool HI>
-__device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t w) {
-    if constexpr (QT == KV_BF16)
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-    else
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even
-    return u >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-    f16x2_t v = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
-
-// Scalar load of a wave-uniform int32 the kernel never writes (seq_len, block table, kv start):
-// through the constant address space, so it is an s_load, independent of the vector-memory
-// counter that the KV prefetch uses.
-__device__ __forceinline__ int32_t ld_uniform(const int32_t *ptr, size_t i) {
-    return *((const __attribute__((address_space(4))) int32_t *)ptr + i);
-}
-
-// Wave-uniform copies (the value is the same in every lane; this keeps it in scalar registers
-// so that loads addressed by it are scalar loads, counted apart from the KV vector loads).
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uni(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 // Element index (within a head_dim row) of MFMA k-slot (group g, step kk, position j) of the
 // q.k^T contraction.  E = elements per 16-byte load of K; each lane loads 16 bytes at element
@@ -122,104 +49,6 @@ __device__ __forceinline__ int qk_elem(int g, int kk) {
 // Tile-relative token of k-slot j (0..7) of lane group g in the p.V contraction; equals the
 // token whose score sits in C slot (j & 3) of half (j >> 2) of the q.k^T result.
 __device__ __forceinline__ int pv_token(int g, int j) { return (j < 4) ? 4 * g + j : 12 + 4 * g + j; }
-
-// Store DT consecutive output elements starting at element `d0` of row `dst`.
-template <int DT>
-__device__ __forceinline__ void store_row_chunk(void *out, int out_dtype, size_t base, const float *v) {
-    if (out_dtype == 0) {
-        float *o = (float *)out + base;
-#pragma unroll
-        for (int i = 0; i < DT; i += 4) *(float4 *)(o + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
-    } else if (out_dtype == 1) {
-        uint32_t w[DT / 2];
-#pragma unroll
-        for (int i = 0; i < DT / 2; i++) w[i] = pack_f16(v[2 * i], v[2 * i + 1]);
-        uint16_t *o = (uint16_t *)out + base;
-        if constexpr (DT == 8) *(u32x4_t *)o = u32x4_t{w[0], w[1], w[2], w[3]};
-        else *(u32x2_t *)o = u32x2_t{w[0], w[1]};
-    } else {
-        uint32_t w[DT / 2];
-#pragma unroll
-        for (int i = 0; i < DT / 2; i++)
-            w[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
-        uint16_t *o = (uint16_t *)out + base;
-        if constexpr (DT == 8) *(u32x4_t *)o = u32x4_t{w[0], w[1], w[2], w[3]};
-        else *(u32x2_t *)o = u32x2_t{w[0], w[1]};
-    }
-}
-
-// ---------------------------------------------------------------- work split helpers
-//
-// Balanced split of one step's KV work.  A *unit* is (sequence b, kv head, head block): the
-// G <= 16 query heads of one head block that share one kv head.  The units of a sequence are
-// taken in groups of `wpg` by the `wpg` waves of one workgroup (wave i takes unit grp*wpg + i),
-// so the waves of a workgroup stream the same token rows of the cache at the same time.
-// Unit group (b, grp) owns T_b = ceil(seq_len[b] / 32) tiles; groups are concatenated
-// sequence-major into TT tiles, and workgroup w of W takes tiles [lo_w, lo_{w+1}) with
-// lo_w = w*q + min(w, r), q = TT / W, r = TT % W: every workgroup gets the same amount of KV
-// (up to one tile) whatever the length mix.  A group cut by workgroup boundaries leaves one
-// partial state per piece: slot 0 of a workgroup holds its first piece, slot 1 its last one.
-
-__device__ __forceinline__ int seq_tiles(const Params &p, int b) {
-    int n = p.seq_len[b];
-    n = max(0, min(n, p.max_seq_len));
-    return (n + kTile - 1) / kTile;
-}
-
-// Same, for a wave-uniform b (scalar load).
-__device__ __forceinline__ int seq_tiles_u(const Params &p, int b) {
-    int n = ld_uniform(p.seq_len, b);
-    n = max(0, min(n, p.max_seq_len));
-    return (n + kTile - 1) / kTile;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
-struct Split {
-    int64_t q, r;
-};
-
-__device__ __forceinline__ Split make_split(int64_t TT, int64_t W) { return Split{TT / W, TT % W}; }
-
-__device__ __forceinline__ int64_t split_lo(const Split &s, int64_t w) { return w * s.q + min(w, s.r); }
-
-// Workgroup whose range holds tile t (0 <= t < TT).
-__device__ __forceinline__ int64_t split_owner(const Split &s, int64_t t) {
-    const int64_t big = s.r * (s.q + 1);
-    return t < big ? t / (s.q + 1) : s.r + (t - big) / s.q;
-}
-
-// Total tiles over all sequences (one unit group each); every lane gets the same value.
-__device__ __forceinline__ int64_t total_seq_tiles(const Params &p, int lane) {
-    int64_t tot = 0;
-    for (int b0 = 0; b0 < p.batch; b0 += 64) {
-        const int b = b0 + lane;
-        int t = b < p.batch ? seq_tiles(p, b) : 0;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
-        tot += t;
-    }
-    return tot;
-}
-
-// Tiles of the sequences before b; every lane gets the same value.
-__device__ __forceinline__ int64_t tiles_before(const Params &p, int b, int lane) {
-    int64_t tot = 0;
-    for (int b0 = 0; b0 < b; b0 += 64) {
-        int t = (b0 + lane < b) ? seq_tiles(p, b0 + lane) : 0;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
-        tot += t;
-    }
-    return tot;
-}
 
 // ---------------------------------------------------------------- split-KV partition kernel
 //
@@ -271,21 +100,29 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int g, int c, uint32_t row_b
     return o;
 }
 
-template <int VDW>
+// KV payload load.  NT: streaming (nontemporal) hint, used when every KV byte has exactly one
+// reader in the grid, so the stream does not displace lines that other loads still need.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_kv(const uint8_t *src) {
+    if constexpr (NT) return __builtin_nontemporal_load((const T *)src);
+    else return *(const T *)src;
+}
+
+template <int VDW, bool NT>
 __device__ __forceinline__ void load_v_chunk(uint32_t (&dst)[VDW], const uint8_t *src) {
     if constexpr (VDW == 4) {
-        const u32x4_t x = *(const u32x4_t *)src;
+        const u32x4_t x = ld_kv<NT, u32x4_t>(src);
         dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
     } else if constexpr (VDW == 2) {
-        const u32x2_t x = *(const u32x2_t *)src;
+        const u32x2_t x = ld_kv<NT, u32x2_t>(src);
         dst[0] = x[0]; dst[1] = x[1];
     } else {
-        dst[0] = *(const uint32_t *)src;
+        dst[0] = ld_kv<NT, uint32_t>(src);
     }
 }
 
 // Full tile: 32 valid tokens.
-template <int D, int KVT, int SCALE>
+template <int D, int KVT, int SCALE, bool NT>
 __device__ __forceinline__ void load_tile(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
                                           const uint8_t *kt, const uint8_t *vt, const float *st,
                                           const LaneOffsets &o, uint32_t row_bytes) {
@@ -294,14 +131,14 @@ __device__ __forceinline__ void load_tile(TileRaw<Geometry<D, KVT>::KLOADS, Geom
     for (int half = 0; half < 2; half++)
 #pragma unroll
         for (int L = 0; L < G::KLOADS; L++)
-            r.k[half][L] = *(const u32x4_t *)(kt + (size_t)(16 * half) * row_bytes + 4 * G::E * L * G::EB + o.k);
+            r.k[half][L] = ld_kv<NT, u32x4_t>(kt + (size_t)(16 * half) * row_bytes + 4 * G::E * L * G::EB + o.k);
 #pragma unroll
-    for (int j = 0; j < 8; j++) load_v_chunk<G::VDW>(r.v[j], vt + (size_t)(j < 4 ? j : 12 + j) * row_bytes + o.v);
+    for (int j = 0; j < 8; j++) load_v_chunk<G::VDW, NT>(r.v[j], vt + (size_t)(j < 4 ? j : 12 + j) * row_bytes + o.v);
     if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[o.s];
 }
 
 // Partial last tile: tokens past `last` are clamped to `last` (valid rows; masked later).
-template <int D, int KVT, int SCALE>
+template <int D, int KVT, int SCALE, bool NT>
 __device__ __forceinline__ void load_tile_part(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
                                                const uint8_t *kt, const uint8_t *vt, const float *st,
                                                int g, int c, uint32_t row_bytes, int hkv, int last) {
@@ -311,15 +148,15 @@ __device__ __forceinline__ void load_tile_part(TileRaw<Geometry<D, KVT>::KLOADS,
         const uint32_t tok = (uint32_t)min(16 * half + c, last);
 #pragma unroll
         for (int L = 0; L < G::KLOADS; L++)
-            r.k[half][L] = *(const u32x4_t *)(kt + tok * row_bytes + (uint32_t)(4 * G::E * L + G::E * g) * G::EB);
+            r.k[half][L] = ld_kv<NT, u32x4_t>(kt + tok * row_bytes + (uint32_t)(4 * G::E * L + G::E * g) * G::EB);
     }
 #pragma unroll
     for (int j = 0; j < 8; j++)
-        load_v_chunk<G::VDW>(r.v[j], vt + (uint32_t)min(pv_token(g, j), last) * row_bytes + (uint32_t)(G::DT * c * G::EB));
+        load_v_chunk<G::VDW, NT>(r.v[j], vt + (uint32_t)min(pv_token(g, j), last) * row_bytes + (uint32_t)(G::DT * c * G::EB));
     if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[(uint32_t)min(pv_token(g, c & 7), last) * (uint32_t)hkv];
 }
 
-template <int D, int KVT, int QT, int SCALE, bool PAGED>
+template <int D, int KVT, int QT, int SCALE, bool PAGED, bool NT>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
 void partition_kernel(Params p) {
     using G = Geometry<D, KVT>;
@@ -483,8 +320,8 @@ void partition_kernel(Params p) {
         const float *st = nullptr;
         // lane 16g+i holds the k (i < 8) or v (i >= 8) scale of token pv_token(g, i & 7)
         if constexpr (SCALE == SC_TOKEN_HEAD) st = ((c & 8) ? p.v_scale : p.k_scale) + kvh + (size_t)d.row0 * p.hkv;
-        if (d.last >= kTile - 1) load_tile<D, KVT, SCALE>(r, kt, vt, st, lofs, row_bytes);
-        else load_tile_part<D, KVT, SCALE>(r, kt, vt, st, g, c, row_bytes, p.hkv, d.last);
+        if (d.last >= kTile - 1) load_tile<D, KVT, SCALE, NT>(r, kt, vt, st, lofs, row_bytes);
+        else load_tile_part<D, KVT, SCALE, NT>(r, kt, vt, st, g, c, row_bytes, p.hkv, d.last);
     };
 
     auto compute = [&](const TileRaw<KLOADS, VDW> &r, const Desc &d) {
@@ -701,19 +538,22 @@ void partition_kernel(Params p) {
 // ---------------------------------------------------------------- combine kernel
 //
 // Grid: x = q head, y = sequence.  Block: one wave.  For a unit cut by workgroup boundaries,
-// merges its pieces -- slot 1 (or 0) of the first workgroup, slot 0 of the later ones -- by
-// log-sum-exp:  M = max_i m_i, w_i = 2^(m_i - M), out = sum_i w_i acc_i / sum_i w_i l_i.
-// Lane (j = lane / 8, k = lane % 8) accumulates pieces j, j+8, ... over output elements
-// [k*D/8, (k+1)*D/8); the eight partial sums are then added by a fixed butterfly.  Also writes
-// out = 0, lse = -inf for empty sequences.  Fixed order throughout: deterministic.
+// merges its pieces -- slot 1 (or 0) of the first workgroup, slot 0 of the later ones -- with the
+// log-sum-exp rule for two partial states (m_a, l_a, acc_a), (m_b, l_b, acc_b):
+//   M = max(m_a, m_b),  w = 2^(m - M),  l = w_a l_a + w_b l_b,  acc = w_a acc_a + w_b acc_b
+// (an empty state has m = -inf and weight 0), then out = acc / l, lse = (M + log2 l) ln 2.
+// Lane (j = lane / 8, k = lane % 8) folds pieces j, j+8, ... in order over output elements
+// [k*D/8, (k+1)*D/8), four pieces' loads in flight at a time; the eight lane-group states are
+// then merged by a fixed butterfly (both partners compute the same sums).  Also writes out = 0,
+// lse = -inf for empty sequences.  Fixed order throughout: deterministic.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     constexpr int PER = D / 8;  // output elements per lane
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int j = lane >> 3, k = lane & 7;
     const int kvh = h / p.group, hloc = h % p.group;
-    const int u_in = kvh * p.nhb + hloc / kHeadBlock;
-    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = hloc % kHeadBlock;
+    const int u_in = kvh * p.nhb + hloc / p.hb;
+    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = hloc % p.hb;
     const size_t obase = ((size_t)b * p.hq + h) * D + PER * k;
 
     auto store = [&](const float *v) {
@@ -734,10 +574,24 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
         }
     };
 
-    // wave-wide reductions first, with every lane active
-    const int64_t TT = total_seq_tiles(p, lane) * p.groups;
-    const int64_t Pb = tiles_before(p, b, lane);
-    const int Tb = seq_tiles(p, b);
+    // one pass over seq_len: tiles of all sequences, of those before b, and of b
+    int64_t tot = 0, bef = 0;
+    int mine = 0;
+#pragma unroll 4
+    for (int bb = lane; bb < p.batch; bb += 64) {
+        const int t = seq_tiles(p, bb);
+        tot += t;
+        bef += bb < b ? t : 0;
+        mine = bb == b ? t : mine;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        tot += __shfl_xor(tot, off, 64);
+        bef += __shfl_xor(bef, off, 64);
+        mine += __shfl_xor(mine, off, 64);
+    }
+    const int64_t TT = tot * p.groups, Pb = bef;
+    const int Tb = mine;
     if (Tb == 0) {
         if (j == 0) {
             float z[PER];
@@ -757,44 +611,59 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     const int np = (int)(whi - wlo + 1);
     const int first_slot = split_lo(sp, wlo) == U0 ? 0 : 1;  // unit began inside wlo's range
     auto slot_of = [&](int i) -> size_t {
-        return (((size_t)(wlo + i) * 2 + (i == 0 ? first_slot : 0)) * p.wpg + wave) * kHeadBlock + c;
+        return (((size_t)(wlo + i) * 2 + (i == 0 ? first_slot : 0)) * p.wpg + wave) * p.hb + c;
     };
-    // M and L with the pieces spread over lanes
-    float M = -INFINITY;
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, p.ws_ml[slot_of(i)].x);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor_f(M, off));
-    float L = 0.0f;
-    for (int i = lane; i < np; i += 64) {
-        const float2 ml = p.ws_ml[slot_of(i)];
-        L += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) L += shfl_xor_f(L, off);
-    // weighted accumulators: lane group j takes pieces j, j+8, ...
-    float o[PER];
+
+    // ---- this lane group's pieces j, j+8, ..., four at a time
+    float m = -INFINITY, l = 0.0f, o[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) o[i] = 0.0f;
-    for (int i = j; i < np; i += 8) {
-        const size_t slot = slot_of(i);
-        const float wt = __builtin_amdgcn_exp2f(p.ws_ml[slot].x - M);
-        const float *src = p.ws_acc + slot * D + PER * k;
+    for (int i0 = j; i0 < np; i0 += 32) {
+        float2 ml[4];
+        float4 x[4][PER / 4];
 #pragma unroll
-        for (int e = 0; e < PER; e += 4) {
-            const float4 x = *(const float4 *)(src + e);
-            o[e] += wt * x.x; o[e + 1] += wt * x.y; o[e + 2] += wt * x.z; o[e + 3] += wt * x.w;
+        for (int u = 0; u < 4; u++) {
+            const size_t slot = slot_of(min(i0 + 8 * u, np - 1));
+            ml[u] = p.ws_ml[slot];
+            const float *src = p.ws_acc + slot * D + PER * k;
+#pragma unroll
+            for (int e = 0; e < PER / 4; e++) x[u][e] = *(const float4 *)(src + 4 * e);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            if (i0 + 8 * u < np) {
+                const float mn = fmaxf(m, ml[u].x);  // finite: every piece holds a token
+                const float wa = __builtin_amdgcn_exp2f(m - mn), wb = __builtin_amdgcn_exp2f(ml[u].x - mn);
+                l = l * wa + ml[u].y * wb;
+#pragma unroll
+                for (int e = 0; e < PER / 4; e++) {
+                    o[4 * e + 0] = o[4 * e + 0] * wa + x[u][e].x * wb;
+                    o[4 * e + 1] = o[4 * e + 1] * wa + x[u][e].y * wb;
+                    o[4 * e + 2] = o[4 * e + 2] * wa + x[u][e].z * wb;
+                    o[4 * e + 3] = o[4 * e + 3] * wa + x[u][e].w * wb;
+                }
+                m = mn;
+            }
         }
     }
+    // ---- merge the eight lane-group states
 #pragma unroll
-    for (int off = 8; off < 64; off <<= 1)
+    for (int off = 8; off < 64; off <<= 1) {
+        const float mo = shfl_xor_f(m, off), lo = shfl_xor_f(l, off);
+        const float mn = fmaxf(m, mo);
+        const float wa = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        const float wb = mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+        l = l * wa + lo * wb;
 #pragma unroll
-        for (int e = 0; e < PER; e++) o[e] += shfl_xor_f(o[e], off);
+        for (int e = 0; e < PER; e++) o[e] = o[e] * wa + shfl_xor_f(o[e], off) * wb;
+        m = mn;
+    }
     if (j == 0) {
-        const float inv = 1.0f / L;
+        const float inv = 1.0f / l;
 #pragma unroll
         for (int e = 0; e < PER; e++) o[e] *= inv;
         store(o);
-        if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = (M + log2f(L)) * kLn2;
+        if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = (m + log2f(l)) * kLn2;
     }
 }
 
@@ -834,10 +703,15 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t *__restri
 template <int D, int KVT, int QT, int SCALE>
 static hipError_t launch_p(const Params &p, hipStream_t stream) {
     dim3 grid(p.nparts), block(64 * p.wpg);
-    if (p.block_table)
-        hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, false>), grid, block, 0, stream, p);
+    // with one head block per kv head every KV byte is read by one wave only: stream it
+    const bool nt = p.nhb == 1;
+    if (p.block_table) {
+        if (nt) hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, false>), grid, block, 0, stream, p);
+    } else {
+        if (nt) hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, false, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, false, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,489 @@
+// fd_wide.hip -- gfx950 partition kernel for wide query groups: 64 or more query heads per kv
+// head (MQA / wide GQA), E4M3 KV, head_dim 128.
+//
+// Method: the split-KV online-softmax recurrence of the 16-head partition kernel in
+// fd_kernels.hip (same pages: "SGLang Prefill 性能优化" section 2.2 for the block recurrence;
+// "从 SGLang Kernel源码到 GPU Trace：DeepSeek V4.1 Flash-Decode" sections 2.2 / 3.1 for the ragged,
+// block-wise KV walk and FP8 conversion right after the load; the ch.15 profiling page, sections
+// 15.11-15.13, for per-token scales, one kv head serving a query-head group, paged addressing and
+// split-K partials).  Same work split (unit groups concatenated into 32-token tiles, equal tile
+// ranges per workgroup) and the same partial-slot layout, so the same combine kernel finishes it.
+//
+// gfx950 design:
+//   * One workgroup runs WPG waves on WPG head blocks of 32 heads of ONE kv head: the K/V tile is
+//     the same for all of them, so it is fetched once per workgroup, straight into LDS by
+//     direct-to-LDS copies (global_load_lds_dwordx4: no VGPRs held while a copy is in flight),
+//     into a ring of NSLOT tiles with NSLOT-1 tiles in flight.  Every wave issues its share of each
+//     tile's copies.  Before reading a tile a wave waits for its own copies of it (an explicit
+//     vmcnt, which counts only what this wave issued), and one workgroup barrier per tile then
+//     publishes the tile and frees the slot read one tile earlier, which the next copies refill.
+//     LDS reads of the ring are issued as inline ds_read so the compiler does not add its own
+//     (conservative: every in-flight copy) waits for the direct-to-LDS writes.
+//   * q.k^T runs on v_mfma_f32_32x32x16_{bf16,f16}: A = K (32 tokens x 16 d, converted to q's
+//     type -- exact), B = q^T (16 d x 32 heads).  Lane (i = l % 32, hh = l / 32) takes
+//     d = 64 hh + 8 kk + 0..7 at k-step kk in both operands, so its K operand for all 8 k-steps is
+//     one 64-byte half row of token i: four 16-byte LDS reads.  In the ring, 16-byte chunk c of
+//     K row r is stored at chunk c ^ (r & 7), so the 8 lanes of each LDS read phase hit 8
+//     different bank groups.
+//   * p.V: O^T (128 d x 32 heads) = V^T . P^T, four 32-row d-tiles, two 16-token k-steps.  The
+//     score C tile holds, in lane l register r, token 8(r/4) + 4hh + r%4 of head i; registers
+//     8s..8s+7 are exactly the B operand (P^T) of k-step s when k-slot j of lane half hh means
+//     token 16s + 8(j/4) + 4hh + j%4, so P never moves between lanes.  The A operand (V^T) of lane
+//     (i, hh) for d-tile dt holds d = 4i + dt of those 8 tokens: one 4-byte LDS read per token
+//     row, then a byte permute and the hardware E4M3 -> f16 convert per token pair.
+//   * Softmax in log2 units with v_exp_f32, as in the 16-head kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fd_device.h"
+
+namespace fd {
+namespace {
+
+// Largest batch whose per-sequence tile prefix sums a wide workgroup keeps in LDS (the ring
+// takes most of the LDS; larger batches locate tiles with a wave scan of seq_len instead).
+constexpr int kWideLdsBatch = 1024;
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 field layout:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at bits 15:14).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int WPG, int SCALE>
+struct WideLayout {
+    static constexpr int ROWB = 128;                 // bytes of one token's K (or V) row, one kv head
+    static constexpr int KV_BYTES = kTile * ROWB;    // one tile of K (or V)
+    static constexpr int SC_BYTES = 256;             // per wave: 32 k then 32 v scales of a tile
+    static constexpr int SLOT = 2 * KV_BYTES + (SCALE == SC_TOKEN_HEAD ? WPG * SC_BYTES : 0);
+    static constexpr int OPS_KV = 8 / WPG;           // 1 KB copies per wave per tile
+    static constexpr int OPS = OPS_KV + (SCALE == SC_TOKEN_HEAD ? 1 : 0);
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// Direct-to-LDS copies: lane i moves 16 (or 4) bytes from its own global address to
+// dst + 16 i (dst + 4 i); dst is wave-uniform.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)dst, 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_void_t *)p; }
+
+// Four 16-byte LDS reads, complete on return.
+__device__ __forceinline__ void lds_read_4x16(u32x4_t (&r)[4], uint32_t a0, uint32_t a1, uint32_t a2,
+                                              uint32_t a3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
+// Four 16-byte LDS reads at a + 0, 32, 64, 96 bytes, complete on return.
+__device__ __forceinline__ void lds_read_4x16_s32(u32x4_t (&r)[4], uint32_t a) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:0\n\t"
+        "ds_read_b128 %1, %4 offset:32\n\t"
+        "ds_read_b128 %2, %4 offset:64\n\t"
+        "ds_read_b128 %3, %4 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a)
+        : "memory");
+}
+
+// Eight 4-byte LDS reads from rows {0, 1, 2, 3, 8, 9, 10, 11} (128-byte rows) past a.
+__device__ __forceinline__ void lds_read_v8(uint32_t (&w)[8], uint32_t a) {
+    asm volatile(
+        "ds_read_b32 %0, %8 offset:0\n\t"
+        "ds_read_b32 %1, %8 offset:128\n\t"
+        "ds_read_b32 %2, %8 offset:256\n\t"
+        "ds_read_b32 %3, %8 offset:384\n\t"
+        "ds_read_b32 %4, %8 offset:1024\n\t"
+        "ds_read_b32 %5, %8 offset:1152\n\t"
+        "ds_read_b32 %6, %8 offset:1280\n\t"
+        "ds_read_b32 %7, %8 offset:1408\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]),
+          "=&v"(w[7])
+        : "v"(a)
+        : "memory");
+}
+
+// Workgroup barrier that the compiler may not move memory operations across.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+}  // namespace
+
+template <int WPG, int NSLOT, int QT, int SCALE, bool PAGED>
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
+void wide_partition_kernel(Params p) {
+    using LY = WideLayout<WPG, SCALE>;
+    constexpr int D = 128;
+    static_assert(NSLOT >= 3, "the ring needs the slot being read, one being refilled and one in flight");
+    static_assert((NSLOT - 2) * LY::OPS < 64, "vmcnt field is 6 bits");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * LY::SLOT];
+    __shared__ int sh_prefix[kWideLdsBatch + 1];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 31, lh = lane >> 5;
+    const int64_t wg = blockIdx.x, W = gridDim.x;
+    const int groups = p.groups;
+    const bool lds_prefix = p.batch <= kWideLdsBatch;
+
+    // ---- per-sequence tile prefix sums, once per workgroup
+    if (lds_prefix) {
+        if (wave == 0) {
+            int base = 0;
+            for (int b0 = 0; b0 < p.batch; b0 += 64) {
+                const int bb = b0 + lane;
+                const int t = bb < p.batch ? seq_tiles(p, bb) : 0;
+                const int incl = wave_incl_scan(t, lane);
+                if (bb < p.batch) sh_prefix[bb] = base + incl - t;
+                base += __shfl(incl, 63, 64);
+            }
+            if (lane == 0) sh_prefix[p.batch] = base;
+        }
+        __syncthreads();
+    }
+
+    const int64_t TT = uni(lds_prefix ? (int64_t)sh_prefix[p.batch] * groups : total_seq_tiles(p, lane) * groups);
+    const Split sp = make_split(TT, W);
+    const int64_t lo = split_lo(sp, wg), hi = split_lo(sp, wg + 1);
+    if (lo >= hi) return;  // workgroup-uniform
+
+    float tensor_k = 1.0f, tensor_v = 1.0f;
+    if constexpr (SCALE == SC_TENSOR) {
+        tensor_k = p.k_scale[0];
+        tensor_v = p.v_scale[0];
+    }
+    const float qk_scale = p.qk_scale * tensor_k;
+    const uint32_t row_bytes = (uint32_t)p.hkv * D;  // bytes per cache row (all kv heads)
+
+    // ---- tile cursors: one issuing copies NSLOT-1 tiles ahead, one computing
+    struct Cursor {
+        int64_t pos;
+        int b, Tb, grp, tt, n;
+    };
+    auto locate = [&](Cursor &k, int64_t at) {
+        k.pos = at;
+        if (lds_prefix) {
+            int l0 = 0, h0 = p.batch;
+            while (h0 - l0 > 1) {
+                const int mid = (l0 + h0) >> 1;
+                if ((int64_t)sh_prefix[mid] * groups <= at) l0 = mid;
+                else h0 = mid;
+            }
+            k.b = uni(l0);
+            k.Tb = uni(sh_prefix[k.b + 1] - sh_prefix[k.b]);
+            const int64_t rel = at - (int64_t)sh_prefix[k.b] * groups;
+            k.grp = uni((int)(rel / k.Tb));
+            k.tt = uni((int)(rel % k.Tb));
+        } else {
+            int64_t base = 0;
+            for (int b0 = 0; b0 < p.batch; b0 += 64) {
+                const int bb = b0 + lane;
+                const int t = bb < p.batch ? seq_tiles(p, bb) : 0;
+                const int incl = wave_incl_scan(t, lane);
+                const int64_t excl = base + incl - t;
+                const bool here = t > 0 && excl * groups <= at && (excl + t) * groups > at;
+                const uint64_t mask = __ballot(here);
+                if (mask) {
+                    const int src = __builtin_ctzll(mask);
+                    k.b = uni(b0 + src);
+                    k.Tb = uni(__shfl(t, src, 64));
+                    const int64_t Pb = base + uni(__shfl(incl, src, 64)) - k.Tb;
+                    const int64_t rel = at - Pb * groups;
+                    k.grp = uni((int)(rel / k.Tb));
+                    k.tt = uni((int)(rel % k.Tb));
+                    break;
+                }
+                base += uni(__shfl(incl, 63, 64));
+            }
+        }
+        k.n = max(0, min(ld_uniform(p.seq_len, k.b), p.max_seq_len));
+    };
+    // one tile forward (crossing unit groups and sequences); false, unmoved, at the range end
+    auto step = [&](Cursor &k) -> bool {
+        if (k.pos + 1 >= hi) return false;
+        k.pos++;
+        if (++k.tt == k.Tb) {
+            k.tt = 0;
+            if (++k.grp == groups) {
+                k.grp = 0;
+                do {
+                    k.b++;
+                } while ((k.Tb = lds_prefix ? uni(sh_prefix[k.b + 1] - sh_prefix[k.b]) : seq_tiles_u(p, k.b)) == 0);
+                k.n = max(0, min(ld_uniform(p.seq_len, k.b), p.max_seq_len));
+            }
+        }
+        return true;
+    };
+    auto slot_of = [&](int64_t pos) -> int { return (int)((pos - lo) % NSLOT); };
+
+    // ---- copies of one tile into a ring slot (this wave's share)
+    auto issue = [&](const Cursor &k, int si) {
+        const int t0 = k.tt * kTile;
+        const int last = min(k.n - t0, kTile) - 1;  // rows past it repeat it (valid; masked later)
+        int64_t row0;
+        if constexpr (PAGED)
+            row0 = (int64_t)ld_uniform(p.block_table, (size_t)k.b * p.max_blocks + t0 / p.block_size) *
+                       p.block_size + (t0 % p.block_size);
+        else
+            row0 = (int64_t)ld_uniform(p.kv_start, k.b) + t0;
+        const int kvh = (k.grp * WPG) / p.nhb;
+        uint8_t *slot = ring + si * LY::SLOT;
+        const uint8_t *kb = (const uint8_t *)p.k + (size_t)kvh * D + (size_t)row0 * row_bytes;
+        const uint8_t *vb = (const uint8_t *)p.v + (size_t)kvh * D + (size_t)row0 * row_bytes;
+#pragma unroll
+        for (int u = 0; u < LY::OPS_KV; u++) {
+            const int o = wave * LY::OPS_KV + u;  // copies 0..3: K rows 8o..8o+7; 4..7: V rows
+            const int row = 8 * (o & 3) + (lane >> 3);
+            const uint32_t rc = (uint32_t)min(row, last);
+            if (o < 4)
+                copy16_to_lds(kb + rc * row_bytes + 16 * ((lane & 7) ^ (row & 7)), slot + o * 1024);
+            else
+                copy16_to_lds(vb + rc * row_bytes + 16 * (lane & 7), slot + LY::KV_BYTES + (o - 4) * 1024);
+        }
+        if constexpr (SCALE == SC_TOKEN_HEAD) {
+            const int t = min(lane & 31, last);
+            const float *sb = (lane < 32 ? p.k_scale : p.v_scale) + kvh + (size_t)(row0 + t) * p.hkv;
+            copy4_to_lds(sb, slot + 2 * LY::KV_BYTES + wave * LY::SC_BYTES);
+        }
+    };
+
+    // ---- per-lane LDS offsets within a slot
+    const uint32_t ring0 = lds_addr(ring);
+    uint32_t koff[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) koff[q] = li * LY::ROWB + 16 * ((4 * lh + q) ^ (li & 7));
+    const uint32_t voff = LY::KV_BYTES + (4 * lh) * LY::ROWB + 4 * li;
+    const uint32_t soff = 2 * LY::KV_BYTES + wave * LY::SC_BYTES + 16 * lh;
+
+    // ---- per-segment state
+    u32x4_t qop[8];
+    f32x16_t acc[4];
+    float m_run = -INFINITY, l_run = 0.0f;
+    auto load_q = [&](int b, int grp) {
+        const int u_in = grp * WPG + wave;
+        const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
+        const int head = kvh * p.group + hb * kWideHeadBlock + li;
+        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + 64 * lh;
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++) qop[kk] = *(const u32x4_t *)(qrow + 8 * kk);
+        // complete here (a drain, once per segment), so that no load is pending at the top of the
+        // tile loop and the compiler adds no wait on the in-flight tile copies there
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    };
+    auto reset_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][r] = 0.0f;
+        m_run = -INFINITY;
+        l_run = 0.0f;
+    };
+
+    auto compute = [&](int si, int last) {
+        const uint32_t sbase = ring0 + si * LY::SLOT;
+        u32x4_t kr[4];
+        lds_read_4x16(kr, sbase + koff[0], sbase + koff[1], sbase + koff[2], sbase + koff[3]);
+        float ksc[16], vsc[16];
+        if constexpr (SCALE == SC_TOKEN_HEAD) {
+            u32x4_t kv[4], vv[4];
+            lds_read_4x16_s32(kv, sbase + soff);
+            lds_read_4x16_s32(vv, sbase + soff + 128);
+            // element to a scalar first: a bit cast straight from a vector element reads
+            // element 0 with this compiler
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const uint32_t kw = kv[r >> 2][r & 3], vw = vv[r >> 2][r & 3];
+                ksc[r] = __builtin_bit_cast(float, kw);
+                vsc[r] = __builtin_bit_cast(float, vw);
+            }
+        }
+        // ---- scores S[token][head]
+        f32x16_t S;
+#pragma unroll
+        for (int r = 0; r < 16; r++) S[r] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++) {
+            const uint32_t w0 = kr[kk >> 1][2 * (kk & 1)], w1 = kr[kk >> 1][2 * (kk & 1) + 1];
+            const u32x4_t a = {cvt_fp8x2<QT, false>(w0), cvt_fp8x2<QT, true>(w0),
+                               cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
+            S = mfma32_qk<QT>(a, qop[kk], S);
+        }
+        // ---- online softmax (log2 units); lane holds tokens 8(r/4) + 4lh + r%4 of head li
+        float s[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) s[r] = (SCALE == SC_TOKEN_HEAD) ? S[r] * (ksc[r] * p.qk_scale) : S[r] * qk_scale;
+        if (last < kTile - 1) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (8 * (r >> 2) + 4 * lh + (r & 3) > last) s[r] = -INFINITY;
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; r++) mt = fmaxf(mt, s[r]);
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        if (__any(mt > m_run)) {
+            const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[i] *= alpha;
+            m_run = m_new;
+        }
+        float pj[16], psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            pj[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
+            psum += pj[r];
+        }
+        l_run += psum;
+        // ---- p.V, two 16-token k-steps
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            uint32_t pp[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                float p0 = pj[8 * ks + 2 * u], p1 = pj[8 * ks + 2 * u + 1];
+                if constexpr (SCALE == SC_TOKEN_HEAD) {
+                    p0 *= vsc[8 * ks + 2 * u];
+                    p1 *= vsc[8 * ks + 2 * u + 1];
+                }
+                pp[u] = pack_f16(p0, p1);
+            }
+            const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
+            uint32_t w[8];
+            lds_read_v8(w, sbase + voff + 16 * ks * LY::ROWB);
+            uint32_t a[4][4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t x = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x05010400u);
+                const uint32_t y = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x07030602u);
+                a[0][u] = cvt_fp8x2<KV_F16, false>(x);
+                a[1][u] = cvt_fp8x2<KV_F16, true>(x);
+                a[2][u] = cvt_fp8x2<KV_F16, false>(y);
+                a[3][u] = cvt_fp8x2<KV_F16, true>(y);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++)
+                acc[dt] = mfma32_f16(u32x4_t{a[dt][0], a[dt][1], a[dt][2], a[dt][3]}, pop, acc[dt]);
+        }
+    };
+
+    // ---- segment result (lane (li, lh) holds d = 4i + dt, i = 8(r/4) + 4lh + r%4, in acc[dt][r])
+    auto finalize = [&](const Cursor &k, int seg, bool whole) {
+        const int u_in = k.grp * WPG + wave;
+        const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
+        const int head = kvh * p.group + hb * kWideHeadBlock + li;
+        const float l_tot = l_run + shfl_xor_f(l_run, 32);
+        if (whole) {
+            const size_t orow = ((size_t)k.b * p.hq + head) * D;
+            const float inv = ((SCALE == SC_TENSOR) ? tensor_v : 1.0f) / l_tot;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const float v[4] = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
+                store_row_chunk<4>(p.out, p.out_dtype, orow + 4 * (8 * (r >> 2) + 4 * lh + (r & 3)), v);
+            }
+            if (p.lse && lh == 0) p.lse[(size_t)k.b * p.hq + head] = (m_run + log2f(l_tot)) * kLn2;
+        } else {
+            // slot 0: the range's first segment; slot 1: its last (a middle one is always whole)
+            const size_t slot = (((size_t)wg * 2 + (seg == 0 ? 0 : 1)) * WPG + wave) * kWideHeadBlock + li;
+            float *dst = p.ws_acc + slot * D;
+            const float sv = (SCALE == SC_TENSOR) ? tensor_v : 1.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                *(float4 *)(dst + 4 * (8 * (r >> 2) + 4 * lh + (r & 3))) =
+                    make_float4(acc[0][r] * sv, acc[1][r] * sv, acc[2][r] * sv, acc[3][r] * sv);
+            if (lh == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
+        }
+    };
+
+    // ---- pipeline: copies of tiles lo .. lo+NSLOT-2 in flight before the first compute; each
+    // step waits for its tile, barriers, refills the slot freed by the previous tile (past the
+    // range end the issue cursor repeats its last tile, so every wave always has the same number
+    // of copies in flight) and computes.
+    Cursor ic, cc;
+    locate(ic, lo);
+    cc = ic;
+    issue(ic, 0);
+#pragma unroll
+    for (int k = 1; k <= NSLOT - 2; k++) {
+        step(ic);
+        issue(ic, k);
+    }
+    int seg = 0, seg_start = cc.tt;
+    bool stores_pending = false;
+    load_q(cc.b, cc.grp);
+    reset_state();
+    for (;;) {
+        // own copies of tile cc.pos done (the NSLOT-2 younger tiles may still be in flight); after
+        // stores, wait for everything (loads and stores need not retire in order)
+        if (stores_pending) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSLOT - 2) * LY::OPS));
+        stores_pending = false;
+        wg_barrier();
+        step(ic);
+        issue(ic, slot_of(cc.pos + NSLOT - 1));
+        const int t0 = cc.tt * kTile;
+        compute(slot_of(cc.pos), min(cc.n - t0, kTile) - 1);
+        const bool end_unit = cc.tt + 1 == cc.Tb;
+        if (end_unit || cc.pos + 1 == hi) {
+            finalize(cc, seg, seg_start == 0 && end_unit);
+            stores_pending = true;
+        }
+        if (!step(cc)) break;
+        if (cc.tt == 0) {  // a new unit group begins
+            seg++;
+            seg_start = 0;
+            load_q(cc.b, cc.grp);
+            reset_state();
+        }
+    }
+    // no copy may still be landing in LDS when the workgroup retires
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// ---------------------------------------------------------------- host-side dispatch
+template <int WPG, int QT, int SCALE>
+static hipError_t launch_w(const Params &p, hipStream_t stream) {
+    constexpr int NSLOT = WPG == 4 ? 6 : 3;  // tiles in flight per workgroup: NSLOT-1
+    dim3 grid(p.nparts), block(64 * WPG);
+    if (p.block_table)
+        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int WPG>
+static hipError_t launch_wq(const Params &p, int qt, int sc, hipStream_t stream) {
+    if (qt == KV_BF16) {
+        if (sc == SC_TENSOR) return launch_w<WPG, KV_BF16, SC_TENSOR>(p, stream);
+        return launch_w<WPG, KV_BF16, SC_TOKEN_HEAD>(p, stream);
+    }
+    if (sc == SC_TENSOR) return launch_w<WPG, KV_F16, SC_TENSOR>(p, stream);
+    return launch_w<WPG, KV_F16, SC_TOKEN_HEAD>(p, stream);
+}
+
+hipError_t launch_wide_partition(const Params &p, int q_dtype, int scale_mode, hipStream_t stream) {
+    if (p.d != 128 || p.hb != kWideHeadBlock || (p.wpg != 2 && p.wpg != 4) || p.nhb % p.wpg)
+        return hipErrorInvalidValue;
+    if (p.wpg == 4) return launch_wq<4>(p, q_dtype, scale_mode, stream);
+    return launch_wq<2>(p, q_dtype, scale_mode, stream);
+}
+
+}  // namespace fd

@@ -105,6 +105,19 @@ SMALL = [
                                    q="bf16", scale="token_head", paged=False, block_size=0)),
     ("g2_fp8_tok_bs32", dict(batch=2, hq=4, hkv=2, d=128, seq_lens=[1000, 2], kv="fp8_e4m3", q="bf16",
                              scale="token_head", block_size=32)),
+    # several head blocks per kv head (cached, shared loads) in contiguous mode
+    ("g32_bf16_contig", dict(batch=2, hq=64, hkv=2, d=128, seq_lens=[200, 1], kv="bf16", q="bf16",
+                             scale="none", paged=False, block_size=0)),
+    # wide-group kernel (E4M3, head_dim 128, group a multiple of 64): 2 and 4 waves per workgroup,
+    # both scale modes, both q types, paged and contiguous, two workgroups per kv head (G = 256)
+    ("wide_g64_tok", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[1000, 33, 4097], kv="fp8_e4m3",
+                          q="bf16", scale="token_head", block_size=64)),
+    ("wide_g128_tok_contig_f16q", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[300, 1], kv="fp8_e4m3",
+                                       q="f16", scale="token_head", paged=False, block_size=0)),
+    ("wide_g256_tensor_bs32", dict(batch=2, hq=256, hkv=1, d=128, seq_lens=[700, 64], kv="fp8_e4m3",
+                                   q="bf16", scale="tensor", block_size=32)),
+    ("wide_g64_tensor_f16q", dict(batch=2, hq=64, hkv=1, d=128, seq_lens=[2500, 95], kv="fp8_e4m3",
+                                  q="f16", scale="tensor", block_size=64)),
 ]
 
 
@@ -123,6 +136,25 @@ def test_length_edges(n):
                                  max_seq_len=max(lens + [1]))
     for parts in (0, 3):
         check_case(f"len{n}/p{parts}", case, num_partitions=parts)
+
+
+@pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 191, 192, 193, 4095])
+def test_wide_length_edges(n):
+    lens = [n, 7, n]
+    case = workloads.custom_case(seed=100 + n, device="cuda", batch=3, hq=128, hkv=1, d=128, seq_lens=lens,
+                                 kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64,
+                                 max_seq_len=max(lens + [1]))
+    for parts in (0, 3):
+        check_case(f"wide_len{n}/p{parts}", case, num_partitions=parts)
+
+
+def test_wide_ragged_mix():
+    lens = [0, 1, 5000, 33, 0, 64, 2047, 12000, 31, 0, 700, 96]
+    case = workloads.custom_case(seed=22, device="cuda", batch=len(lens), hq=128, hkv=2, d=128,
+                                 seq_lens=lens, kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=32)
+    for parts in (1, 7, 100, 1024):
+        check_case(f"wide_ragged/p{parts}", case, num_partitions=parts)
 
 
 def test_more_partitions_than_tiles():
