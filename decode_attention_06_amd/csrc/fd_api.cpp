@@ -11,9 +11,11 @@
 
 namespace {
 
-// Partition-kernel waves per step: 8 per CU on 256 CUs (two per SIMD), all resident at once,
-// each workgroup of `wpg` waves with an equal share of the step's KV tiles.
+// Partition-kernel waves per step, all resident at once, each workgroup of `wpg` waves with an
+// equal share of the step's KV tiles: 8 per CU on 256 CUs (two per SIMD; the 16-head kernel
+// needs up to 256 VGPRs), 12 per CU for the wide-group kernel (three per SIMD at 168 VGPRs).
 constexpr long kDefaultWaves = 2048;
+constexpr long kDefaultWavesWide = 3072;
 constexpr int kMaxSeqLen = 1 << 24;
 
 thread_local hipEvent_t t_prof_begin = nullptr, t_prof_end = nullptr;
@@ -67,7 +69,7 @@ Plan make_plan(int batch, int hq, int hkv, int head_dim, int kv_dtype, int max_s
         pl.groups = (int)(ups / pl.wpg);
     }
     const long tt_max = (long)batch * pl.groups * cdiv(max_seq_len, fd::kTile);
-    long W = num_partitions > 0 ? num_partitions : kDefaultWaves / pl.wpg;
+    long W = num_partitions > 0 ? num_partitions : (pl.wide ? kDefaultWavesWide : kDefaultWaves) / pl.wpg;
     if (W > tt_max) W = tt_max;
     if (W < 1) W = 1;
     pl.nparts = (int)W;

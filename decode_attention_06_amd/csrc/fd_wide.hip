@@ -41,8 +41,9 @@ namespace fd {
 namespace {
 
 // Largest batch whose per-sequence tile prefix sums a wide workgroup keeps in LDS (the ring
-// takes most of the LDS; larger batches locate tiles with a wave scan of seq_len instead).
-constexpr int kWideLdsBatch = 1024;
+// takes most of the LDS, and three workgroups of 4 waves or six of 2 share one CU's 160 KB;
+// larger batches locate tiles with a wave scan of seq_len instead).
+constexpr int kWideLdsBatch = 256;
 
 // s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 field layout:
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at bits 15:14).
@@ -99,6 +100,17 @@ __device__ __forceinline__ void lds_read_4x16_s32(u32x4_t (&r)[4], uint32_t a) {
         : "memory");
 }
 
+// Two 16-byte LDS reads at a + 0 and a + 32 bytes, complete on return.
+__device__ __forceinline__ void lds_read_2x16_s32(u32x4_t (&r)[2], uint32_t a) {
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:0\n\t"
+        "ds_read_b128 %1, %2 offset:32\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(a)
+        : "memory");
+}
+
 // Eight 4-byte LDS reads from rows {0, 1, 2, 3, 8, 9, 10, 11} (128-byte rows) past a.
 __device__ __forceinline__ void lds_read_v8(uint32_t (&w)[8], uint32_t a) {
     asm volatile(
@@ -127,7 +139,7 @@ __device__ __forceinline__ void wg_barrier() {
 }  // namespace
 
 template <int WPG, int NSLOT, int QT, int SCALE, bool PAGED>
-__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(3)))
 void wide_partition_kernel(Params p) {
     using LY = WideLayout<WPG, SCALE>;
     constexpr int D = 128;
@@ -230,7 +242,7 @@ void wide_partition_kernel(Params p) {
         }
         return true;
     };
-    auto slot_of = [&](int64_t pos) -> int { return (int)((pos - lo) % NSLOT); };
+    auto next_slot = [](int si) -> int { return si + 1 == NSLOT ? 0 : si + 1; };
 
     // ---- copies of one tile into a ring slot (this wave's share)
     auto issue = [&](const Cursor &k, int si) {
@@ -299,20 +311,18 @@ void wide_partition_kernel(Params p) {
         const uint32_t sbase = ring0 + si * LY::SLOT;
         u32x4_t kr[4];
         lds_read_4x16(kr, sbase + koff[0], sbase + koff[1], sbase + koff[2], sbase + koff[3]);
-        float ksc[16], vsc[16];
-        if constexpr (SCALE == SC_TOKEN_HEAD) {
-            u32x4_t kv[4], vv[4];
-            lds_read_4x16_s32(kv, sbase + soff);
-            lds_read_4x16_s32(vv, sbase + soff + 128);
-            // element to a scalar first: a bit cast straight from a vector element reads
-            // element 0 with this compiler
+        // per-token scales: element to a scalar before the bit cast (a bit cast straight from a
+        // vector element reads element 0 with this compiler)
+        auto read_scales = [&](float (&sc)[16], uint32_t at) {
+            u32x4_t raw[4];
+            lds_read_4x16_s32(raw, at);
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const uint32_t kw = kv[r >> 2][r & 3], vw = vv[r >> 2][r & 3];
-                ksc[r] = __builtin_bit_cast(float, kw);
-                vsc[r] = __builtin_bit_cast(float, vw);
+                const uint32_t w = raw[r >> 2][r & 3];
+                sc[r] = __builtin_bit_cast(float, w);
             }
-        }
+        };
+
         // ---- scores S[token][head]
         f32x16_t S;
 #pragma unroll
@@ -324,6 +334,8 @@ void wide_partition_kernel(Params p) {
                                cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
             S = mfma32_qk<QT>(a, qop[kk], S);
         }
+        float ksc[16];
+        if constexpr (SCALE == SC_TOKEN_HEAD) read_scales(ksc, sbase + soff);
         // ---- online softmax (log2 units); lane holds tokens 8(r/4) + 4lh + r%4 of head li
         float s[16];
 #pragma unroll
@@ -355,13 +367,24 @@ void wide_partition_kernel(Params p) {
         // ---- p.V, two 16-token k-steps
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
+            // v scales of this k-step's 8 tokens (registers 8ks .. 8ks+7)
+            float vsc[8];
+            if constexpr (SCALE == SC_TOKEN_HEAD) {
+                u32x4_t raw[2];
+                lds_read_2x16_s32(raw, sbase + soff + 128 + 64 * ks);
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const uint32_t w = raw[j >> 2][j & 3];
+                    vsc[j] = __builtin_bit_cast(float, w);
+                }
+            }
             uint32_t pp[4];
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 float p0 = pj[8 * ks + 2 * u], p1 = pj[8 * ks + 2 * u + 1];
                 if constexpr (SCALE == SC_TOKEN_HEAD) {
-                    p0 *= vsc[8 * ks + 2 * u];
-                    p1 *= vsc[8 * ks + 2 * u + 1];
+                    p0 *= vsc[2 * u];
+                    p1 *= vsc[2 * u + 1];
                 }
                 pp[u] = pack_f16(p0, p1);
             }
@@ -426,6 +449,7 @@ void wide_partition_kernel(Params p) {
         issue(ic, k);
     }
     int seg = 0, seg_start = cc.tt;
+    int slot_c = 0, slot_i = NSLOT - 1;  // ring slots of the computed tile and of the next copies
     bool stores_pending = false;
     load_q(cc.b, cc.grp);
     reset_state();
@@ -437,9 +461,11 @@ void wide_partition_kernel(Params p) {
         stores_pending = false;
         wg_barrier();
         step(ic);
-        issue(ic, slot_of(cc.pos + NSLOT - 1));
+        issue(ic, slot_i);
+        slot_i = next_slot(slot_i);
         const int t0 = cc.tt * kTile;
-        compute(slot_of(cc.pos), min(cc.n - t0, kTile) - 1);
+        compute(slot_c, min(cc.n - t0, kTile) - 1);
+        slot_c = next_slot(slot_c);
         const bool end_unit = cc.tt + 1 == cc.Tb;
         if (end_unit || cc.pos + 1 == hi) {
             finalize(cc, seg, seg_start == 0 && end_unit);
@@ -460,7 +486,9 @@ void wide_partition_kernel(Params p) {
 // ---------------------------------------------------------------- host-side dispatch
 template <int WPG, int QT, int SCALE>
 static hipError_t launch_w(const Params &p, hipStream_t stream) {
-    constexpr int NSLOT = WPG == 4 ? 6 : 3;  // tiles in flight per workgroup: NSLOT-1
+    // tiles in flight per workgroup: NSLOT-1; the ring is sized so that three workgroups fit
+    // in one CU's 160 KB of LDS
+    constexpr int NSLOT = WPG == 2 ? 3 : (SCALE == SC_TOKEN_HEAD ? 5 : 6);
     dim3 grid(p.nparts), block(64 * WPG);
     if (p.block_table)
         hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, true>), grid, block, 0, stream, p);
