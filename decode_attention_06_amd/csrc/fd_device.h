@@ -21,6 +21,12 @@ enum { KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3 };
 enum { SC_NONE = 0, SC_TENSOR = 1, SC_TOKEN_HEAD = 2 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// The running max m that the accumulator is scaled to moves only when a tile's max exceeds it
+// by more than this (log2 units): weights 2^(s - m) then stay <= 2^8, exact to represent in
+// fp32 and f16, and acc / l is unchanged (both carry the same reference m), while the rescale
+// of the accumulator is skipped on most tiles.
+constexpr float kRescaleSlack = 8.0f;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 // ---------------------------------------------------------------- small helpers

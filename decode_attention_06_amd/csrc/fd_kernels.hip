@@ -380,8 +380,8 @@ void partition_kernel(Params p) {
         for (int j = 1; j < 8; j++) mt = fmaxf(mt, s[j]);
         mt = fmaxf(mt, shfl_xor_f(mt, 16));
         mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        // rescale only when some head's running max grows (wave-uniform branch)
-        if (__any(mt > m_run)) {
+        // move the reference max only when some head exceeds it by more than kRescaleSlack
+        if (__any(mt > m_run + kRescaleSlack)) {  // wave-uniform; always taken on a segment's first tile
             const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;

@@ -349,7 +349,7 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
         for (int r = 1; r < 16; r++) mt = fmaxf(mt, s[r]);
         mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        if (__any(mt > m_run)) {
+        if (__any(mt > m_run + kRescaleSlack)) {  // wave-uniform; always taken on a segment's first tile
             const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
