@@ -40,6 +40,17 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _Append(ctypes.Structure):
+    _fields_ = [
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("kv_start", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("scale_mode", ctypes.c_int32),
+    ]
+
+
 def build(force: bool = False) -> str:
     """Compile liboracle.so with gcc (no fast-math: IEEE double semantics)."""
     with _lock:
@@ -72,6 +83,16 @@ def _load():
         lib.orc_decode_attention.restype = ctypes.c_int
         lib.orc_decode_attention.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.orc_f16_encode.restype = ctypes.c_uint16
+        lib.orc_f16_encode.argtypes = [ctypes.c_float]
+        lib.orc_bf16_encode.restype = ctypes.c_uint16
+        lib.orc_bf16_encode.argtypes = [ctypes.c_float]
+        lib.orc_quantize_row_e4m3.restype = ctypes.c_float
+        lib.orc_quantize_row_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+        lib.orc_kv_append.restype = ctypes.c_int
+        lib.orc_kv_append.argtypes = [ctypes.POINTER(_Append)]
         _lib = lib
     return _lib
 
@@ -180,3 +201,50 @@ def f16_to_double(bits: int) -> float:
 
 def bf16_to_double(bits: int) -> float:
     return _load().orc_bf16_to_double(bits)
+
+
+# ---------------------------------------------------------------- KV-cache append (oracle.c)
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code of the fp32 value x (clamped to +-448, ties to even)."""
+    return int(_load().orc_e4m3_encode(float(np.float32(x))))
+
+
+def f16_encode(x: float) -> int:
+    return int(_load().orc_f16_encode(float(np.float32(x))))
+
+
+def bf16_encode(x: float) -> int:
+    return int(_load().orc_bf16_encode(float(np.float32(x))))
+
+
+def quantize_row_e4m3(x, scale: float = 0.0):
+    """(bytes uint8[n], scale) for one fp32 row: scale = amax/448 unless a scale > 0 is given."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.shape[0], dtype=np.uint8)
+    sc = _load().orc_quantize_row_e4m3(x.ctypes.data, int(x.shape[0]), float(scale), out.ctypes.data)
+    return out, float(np.float32(sc))
+
+
+def kv_append(*, k_new, v_new, k_cache, v_cache, pos, kv_dtype, scale_mode="none", k_scale=None,
+              v_scale=None, block_table=None, kv_start=None, block_size=0):
+    """Host copies (k_cache, v_cache, k_scale, v_scale) after appending k_new / v_new
+    ([batch][hkv][d], any float dtype -- converted to fp32 exactly) at token pos[b] of each
+    sequence.  Caches are returned as raw bits (uint8 for E4M3, int16 for f16 / bf16)."""
+    def f32(t):
+        if hasattr(t, "detach"):
+            t = t.detach().float().cpu().numpy()
+        return np.ascontiguousarray(t, dtype=np.float32)
+    kn, vn = f32(k_new), f32(v_new)
+    batch, hkv, d = kn.shape
+    keep = dict(kn=kn, vn=vn, kc=_host(k_cache).copy(), vc=_host(v_cache).copy(),
+                ks=None if k_scale is None else _host(k_scale, np.float32).copy(),
+                vs=None if v_scale is None else _host(v_scale, np.float32).copy(),
+                bt=_host(block_table, np.int32), st=_host(kv_start, np.int32), pos=_host(pos, np.int32))
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+    bt = keep["bt"]
+    a = _Append(ptr(keep["kn"]), ptr(keep["vn"]), ptr(keep["kc"]), ptr(keep["vc"]), ptr(keep["ks"]),
+                ptr(keep["vs"]), ptr(bt), ptr(keep["st"]), ptr(keep["pos"]), batch, hkv, d,
+                block_size, 0 if bt is None else bt.shape[1], _DTYPE[kv_dtype], _SCALE[scale_mode])
+    if _load().orc_kv_append(ctypes.byref(a)) != 0:
+        raise ValueError("oracle rejected the append")
+    return keep["kc"], keep["vc"], keep["ks"], keep["vs"]

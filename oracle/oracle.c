@@ -237,3 +237,157 @@ int orc_decode_attention(const orc_problem *p, const uint8_t *seq_mask, double *
     free(jobs);
     return status;
 }
+
+/* ======================================================================================
+ * KV-cache append of the current token: the step that precedes the scan.
+ *
+ * Sources: [CH15] 15.9 (paged cache writes; its exercise 4 adds a single-token decode append),
+ * 15.11 (quantised KV with per-token k/v scales) and 15.18 (row-wise absmax -> scale ->
+ * quantise).  Readings: a row is one token's D values of one kv head; its scale is
+ * amax|x| / 448 (448 = largest E4M3 value; 1 when the row is all zeros); the quantised value is
+ * x / scale, clamped to [-448, 448], rounded to the nearest E4M3 value with ties to an even
+ * mantissa.  The decision is taken in fp32 -- scale and quotient are fp32 operations -- the
+ * precision the kernels quantise in; only the final rounding to E4M3 is done here by exact
+ * search.  f16 / bf16 caches store the fp32 value rounded to nearest-even.
+ * ====================================================================================== */
+
+/* Nearest finite E4M3 code to x (clamped to +-448), ties to the even code: a plain search over
+ * the 127 non-negative finite codes in exact double arithmetic.  NaN gives the NaN code 0x7F;
+ * the sign of x (including -0) goes to the sign bit. */
+uint8_t orc_e4m3_encode(float x) {
+    if (x != x) return 0x7F;
+    const int neg = signbit(x) ? 1 : 0;
+    double a = fabs((double)x);
+    if (a > 448.0) a = 448.0;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c <= 0x7E; c++) {
+        const double d = fabs(orc_e4m3_to_double((uint8_t)c) - a);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return (uint8_t)(best | (neg << 7));
+}
+
+/* Round a finite double to the nearest value with `mant` explicit significand bits and minimum
+ * normal exponent `emin` (IEEE round-to-nearest-even, gradual underflow), by exact scaling:
+ * the quantum at x's binade is 2^(e - mant); x / quantum is exact and rint() rounds half to even. */
+static double round_to_format(double x, int mant, int emin) {
+    if (x == 0.0 || x != x || isinf(x)) return x;
+    int e;
+    frexp(x, &e);  /* x = f * 2^e, 0.5 <= |f| < 1, so the binade exponent is e - 1 */
+    int be = e - 1;
+    if (be < emin) be = emin;
+    const double quantum = ldexp(1.0, be - mant);
+    return rint(x / quantum) * quantum;
+}
+
+/* fp32 -> IEEE binary16 bits, round to nearest even (overflow to infinity). */
+uint16_t orc_f16_encode(float x) {
+    const double r = round_to_format((double)x, 10, -14);
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (r != r) return 0x7E00;
+    const double a = fabs(r);
+    if (a >= 65536.0) return sign | 0x7C00;  /* 65520 and above round to infinity */
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    const int be = e - 1;
+    if (be < -14) return sign | (uint16_t)(a / ldexp(1.0, -24));           /* subnormal */
+    return sign | (uint16_t)((be + 15) << 10) | (uint16_t)((a / ldexp(1.0, be) - 1.0) * 1024.0);
+}
+
+/* fp32 -> bfloat16 bits, round to nearest even. */
+uint16_t orc_bf16_encode(float x) {
+    const double r = round_to_format((double)x, 7, -126);
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (r != r) return 0x7FC0;
+    const double a = fabs(r);
+    if (a >= ldexp(1.0, 128)) return sign | 0x7F80;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    const int be = e - 1;
+    if (be < -126) return sign | (uint16_t)(a / ldexp(1.0, -133));         /* subnormal */
+    return sign | (uint16_t)((be + 127) << 7) | (uint16_t)((a / ldexp(1.0, be) - 1.0) * 128.0);
+}
+
+/* One row, E4M3 ([CH15] 15.18): with scale_in > 0 use it (per-tensor scale), else scale =
+ * amax / 448 in fp32 (1 for an all-zero row).  byte[i] = encode(clamp(x[i] / scale, +-448)).
+ * Returns the scale used. */
+float orc_quantize_row_e4m3(const float *x, int n, float scale_in, uint8_t *out) {
+    float scale = scale_in;
+    if (!(scale_in > 0.0f)) {
+        float amax = 0.0f;
+        for (int i = 0; i < n; i++) {
+            const float a = fabsf(x[i]);
+            if (a > amax) amax = a;
+        }
+        scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    }
+    for (int i = 0; i < n; i++) {
+        float q = x[i] / scale;
+        if (q > 448.0f) q = 448.0f;
+        if (q < -448.0f) q = -448.0f;
+        out[i] = orc_e4m3_encode(q);
+    }
+    return scale;
+}
+
+typedef struct {
+    const float *k_new;         /* [batch][hkv][d] fp32 (f16 / bf16 inputs converted exactly)    */
+    const float *v_new;
+    void *k_cache;              /* rows of [hkv][d], kv_dtype                                      */
+    void *v_cache;
+    float *k_scale;             /* E4M3: [1] (per-tensor, read) or [rows][hkv] (per token, written) */
+    float *v_scale;
+    const int32_t *block_table; /* [batch][max_blocks] or NULL (contiguous mode)                  */
+    const int32_t *kv_start;    /* [batch] or NULL                                                 */
+    const int32_t *pos;         /* [batch] token index to write; < 0 skips the sequence           */
+    int32_t batch, hkv, d, block_size, max_blocks, kv_dtype, scale_mode;
+} orc_append;
+
+/* Write each sequence's new K and V rows into the row of token pos[b] (the [CH15] 15.26 paged
+ * address, or kv_start[b] + pos[b]).  Returns 0, or -1 on a bad argument. */
+int orc_kv_append(const orc_append *a) {
+    if (!a || a->batch <= 0 || a->hkv <= 0 || a->d <= 0) return -1;
+    if (!a->block_table && !a->kv_start) return -1;
+    if (a->block_table && a->block_size <= 0) return -1;
+    for (int b = 0; b < a->batch; b++) {
+        const int t = a->pos[b];
+        if (t < 0) continue;
+        int64_t row;
+        if (a->block_table) {
+            const int32_t page = a->block_table[(int64_t)b * a->max_blocks + t / a->block_size];
+            row = (int64_t)page * a->block_size + t % a->block_size;
+        } else {
+            row = (int64_t)a->kv_start[b] + t;
+        }
+        for (int g = 0; g < a->hkv; g++) {
+            for (int which = 0; which < 2; which++) {
+                const float *x = (which ? a->v_new : a->k_new) + ((size_t)b * a->hkv + g) * a->d;
+                void *cache = which ? a->v_cache : a->k_cache;
+                float *sc = which ? a->v_scale : a->k_scale;
+                const size_t base = ((size_t)row * a->hkv + g) * a->d;
+                if (a->kv_dtype == ORC_E4M3) {
+                    if (a->scale_mode == ORC_SCALE_TENSOR) {
+                        orc_quantize_row_e4m3(x, a->d, sc[0], (uint8_t *)cache + base);
+                    } else if (a->scale_mode == ORC_SCALE_TOKEN_HEAD) {
+                        sc[row * a->hkv + g] = orc_quantize_row_e4m3(x, a->d, 0.0f, (uint8_t *)cache + base);
+                    } else {
+                        return -1;
+                    }
+                } else if (a->kv_dtype == ORC_F16 || a->kv_dtype == ORC_BF16) {
+                    uint16_t *dst = (uint16_t *)cache + base;
+                    for (int i = 0; i < a->d; i++)
+                        dst[i] = a->kv_dtype == ORC_F16 ? orc_f16_encode(x[i]) : orc_bf16_encode(x[i]);
+                } else {
+                    return -1;
+                }
+            }
+        }
+    }
+    return 0;
+}
