@@ -62,6 +62,39 @@ def measured_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def kv_append_timing(fd, torch, case, target, stream, reps=50):
+    """fd_kv_append of one new token per sequence (bf16 rows, quantised into the cache): mean
+    launch duration over `reps` back-to-back calls.  Each call rewrites the last existing row of
+    every sequence (pos = seq_len - 1), always a valid row of the cache."""
+    dev = target.k_cache.device
+    g = torch.Generator(device=dev).manual_seed(1)
+    k_new = torch.randn((case.batch, case.hkv, case.d), generator=g, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((case.batch, case.hkv, case.d), generator=g, device=dev).to(torch.bfloat16)
+    pos = (target.seq_len.to(torch.int64) - 1).clamp(min=-1).to(torch.int32)
+
+    def call():
+        fd.kv_append(k_new, v_new, target.k_cache, target.v_cache, pos, kv_dtype=case.kv_dtype,
+                     block_table=target.block_table, kv_start=target.kv_start,
+                     block_size=case.block_size, scale_mode=case.scale_mode, k_scale=target.k_scale,
+                     v_scale=target.v_scale, stream=stream.cuda_stream)
+
+    for _ in range(3):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    rows = int((target.seq_len > 0).sum()) * case.hkv * 2
+    eb = {"fp8_e4m3": 1, "f16": 2, "bf16": 2}[case.kv_dtype]
+    moved = rows * case.d * (2 + eb) + (rows * 4 if case.scale_mode == "token_head" else 0)
+    us = a.elapsed_time(b) * 1e3 / reps
+    return {"us_per_call": round(us, 2), "rows": rows, "bytes_moved": moved,
+            "what": "fd_kv_append: one bf16 K and V row per (sequence, kv head) into the cache"}
+
+
 def read_probe(fd, torch, dev, stream, nbytes=4 << 30, reps=5):
     """The practical HBM read ceiling: a plain coalesced 128-bit streaming read of a 4 GiB buffer
     (fd_hbm_read_probe), best over a few grid sizes, mean of `reps` back-to-back reads each."""
@@ -209,6 +242,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+
+    result["kv_append"] = kv_append_timing(fd, torch, case, copies[0], stream)
 
     if not args.no_read_probe:
         result["read_probe"] = read_probe(fd, torch, dev, stream)

@@ -20,7 +20,8 @@ FD_SCALE_NONE, FD_SCALE_PER_TENSOR, FD_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 DTYPE_CODES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8_e4m3": FD_FP8_E4M3}
 SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head": FD_SCALE_PER_TOKEN_HEAD}
 EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
-           "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe")
+           "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe",
+           "fd_kv_append", "fd_fp8_e4m3_encode")
 
 _lock = threading.Lock()
 _lib = None
@@ -65,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.fd_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.fd_set_profile_events.restype = i32
         L.fd_set_profile_events.argtypes = [vp, vp]
+        L.fd_kv_append.restype = i32
+        L.fd_kv_append.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   vp, vp, vp]
+        L.fd_fp8_e4m3_encode.restype = i32
+        L.fd_fp8_e4m3_encode.argtypes = [vp, vp, i32, vp]
         _lib = L
         return L
 
@@ -180,6 +186,52 @@ def fp8_e4m3_decode(x, stream=None):
     st = lib().fd_fp8_e4m3_decode(x.data_ptr(), out.data_ptr(), x.numel(), stream)
     if st != FD_OK:
         raise FdError(st, "fd_fp8_e4m3_decode")
+    return out
+
+
+def kv_append_raw(k_new, v_new, new_dtype, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start,
+                  pos, batch, num_kv_heads, head_dim, block_size, kv_dtype, scale_mode, k_scale,
+                  v_scale, stream) -> int:
+    """Direct call of fd_kv_append with integer pointers/codes; returns the status."""
+    return lib().fd_kv_append(k_new, v_new, new_dtype, k_cache, v_cache, block_table, max_blocks_per_seq,
+                              kv_start, pos, batch, num_kv_heads, head_dim, block_size, kv_dtype,
+                              scale_mode, k_scale, v_scale, stream)
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, pos, *, kv_dtype: str, block_table=None, kv_start=None,
+              block_size: int = 0, scale_mode: str = "none", k_scale=None, v_scale=None, stream=None):
+    """Write the current token's K/V rows ``k_new``/``v_new`` ([batch][num_kv_heads][head_dim],
+    f32/f16/bf16 GPU tensors) into the cache at token ``pos[b]`` of each sequence (in place;
+    per-token E4M3 scales are written too).  Layouts and codes as ``include/fd.h``."""
+    import torch
+
+    _require_cuda(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, pos=pos,
+                  block_table=block_table, kv_start=kv_start, k_scale=k_scale, v_scale=v_scale)
+    batch, hkv, d = k_new.shape
+    new_code = {torch.float32: FD_F32, torch.float16: FD_F16, torch.bfloat16: FD_BF16}[k_new.dtype]
+    if v_new.dtype != k_new.dtype or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must have the same shape and dtype")
+    max_blocks = 0 if block_table is None else block_table.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(k_new.device).cuda_stream
+    st = kv_append_raw(_ptr(k_new), _ptr(v_new), new_code, _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                       max_blocks, _ptr(kv_start), _ptr(pos), batch, hkv, d, block_size,
+                       DTYPE_CODES[kv_dtype], SCALE_CODES[scale_mode], _ptr(k_scale), _ptr(v_scale), stream)
+    if st != FD_OK:
+        raise FdError(st, "fd_kv_append")
+
+
+def fp8_e4m3_encode(x, stream=None):
+    """Diagnostic: the E4M3 codes fd_kv_append stores for the fp32 quotients in GPU tensor x."""
+    import torch
+
+    _require_cuda(x=x)
+    out = torch.empty(x.numel(), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib().fd_fp8_e4m3_encode(x.data_ptr(), out.data_ptr(), x.numel(), stream)
+    if st != FD_OK:
+        raise FdError(st, "fd_fp8_e4m3_encode")
     return out
 
 

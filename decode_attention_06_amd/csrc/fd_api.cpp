@@ -208,6 +208,50 @@ int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, 
     return fd::launch_read_probe(buf, bytes / 16, out, blocks, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
 }
 
+int fd_kv_append(const void *k_new, const void *v_new, int new_dtype, void *k_cache, void *v_cache,
+                 const int32_t *block_table, int max_blocks_per_seq, const int32_t *kv_start,
+                 const int32_t *pos, int batch, int num_kv_heads, int head_dim, int block_size,
+                 int kv_dtype, int scale_mode, float *k_scale, float *v_scale, hipStream_t stream) {
+    if (!k_new || !v_new || !k_cache || !v_cache || !pos) return FD_ERR_INVALID_ARG;
+    if (batch <= 0 || batch > 65535 || num_kv_heads <= 0 || num_kv_heads > 4096) return FD_ERR_INVALID_ARG;
+    if ((block_table == nullptr) == (kv_start == nullptr)) return FD_ERR_INVALID_ARG;
+    if (new_dtype != FD_F32 && new_dtype != FD_F16 && new_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
+    if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
+    if (kv_dtype == FD_FP8_E4M3) {
+        if (scale_mode != FD_SCALE_PER_TENSOR && scale_mode != FD_SCALE_PER_TOKEN_HEAD) return FD_ERR_INVALID_ARG;
+        if (!k_scale || !v_scale) return FD_ERR_INVALID_ARG;
+    } else if (scale_mode != FD_SCALE_NONE) {
+        return FD_ERR_INVALID_ARG;
+    }
+    if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
+    if (block_table) {
+        if (block_size != 32 && block_size != 64) return FD_ERR_UNSUPPORTED;
+        if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
+    }
+    fd::AppendParams a;
+    memset(&a, 0, sizeof(a));
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.kv_start = kv_start;
+    a.pos = pos;
+    a.batch = batch;
+    a.hkv = num_kv_heads;
+    a.d = head_dim;
+    a.block_size = block_table ? block_size : 0;
+    a.max_blocks = block_table ? max_blocks_per_seq : 0;
+    return fd::launch_append(a, new_dtype, kv_dtype, scale_mode, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
+}
+
+int fd_fp8_e4m3_encode(const float *in, uint8_t *out, int n, hipStream_t stream) {
+    if (n < 0 || (n > 0 && (!in || !out))) return FD_ERR_INVALID_ARG;
+    return fd::launch_fp8_encode(in, out, n, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
+}
+
 int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream) {
     if (n < 0 || (n > 0 && (!in || !out))) return FD_ERR_INVALID_ARG;
     return fd::launch_fp8_decode(in, out, n, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;

@@ -43,6 +43,20 @@ struct Params {
     float qk_scale;   // softmax_scale * log2(e): scores are kept in log2 units
 };
 
+// KV-cache append of the current token (fd_append.hip).
+struct AppendParams {
+    const void *k_new;           // [batch][hkv][d], new dtype
+    const void *v_new;
+    void *k_cache;               // rows of [hkv][d]
+    void *v_cache;
+    float *k_scale;              // E4M3: [1] (per tensor, read) or [rows][hkv] (per token, written)
+    float *v_scale;
+    const int32_t *block_table;  // paged mode
+    const int32_t *kv_start;     // contiguous mode
+    const int32_t *pos;          // [batch] token index written; < 0 skips
+    int batch, hkv, d, block_size, max_blocks;
+};
+
 // Host-side launchers (defined in fd_kernels.hip).  Return hipSuccess or the launch error.
 hipError_t launch_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode,
                             hipStream_t stream);
@@ -52,5 +66,8 @@ hipError_t launch_combine(const Params &p, hipStream_t stream);
 hipError_t launch_wide_partition(const Params &p, int q_dtype, int scale_mode, hipStream_t stream);
 hipError_t launch_fp8_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
 hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, hipStream_t stream);
+// fd_append.hip: new_dtype 0 f32 / 1 f16 / 2 bf16; kv_dtype and scale_mode as the FD_ codes.
+hipError_t launch_append(const AppendParams &a, int new_dtype, int kv_dtype, int scale_mode, hipStream_t stream);
+hipError_t launch_fp8_encode(const float *in, uint8_t *out, int n, hipStream_t stream);
 
 }  // namespace fd

@@ -97,7 +97,9 @@ typedef enum {
  *   workspace    device scratch of at least fd_workspace_bytes(...) bytes, 256-byte aligned.
  *                Contents need no initialisation and are clobbered; one workspace must not be
  *                shared by calls that may overlap.
- *   num_partitions  0 = automatic (2048 partitions: 8 waves per CU on 256 CUs); > 0 forces
+ *   num_partitions  0 = automatic (one partition workgroup per `wpg` resident waves: 2048 waves,
+ *                8 per CU on 256 CUs, or 3072 for the wide-group kernel that E4M3 KV with
+ *                head_dim 128 and a multiple of 64 query heads per kv head uses); > 0 forces
  *                that many (testing and tuning).  Capped by the number of tiles the sizes allow.
  *   stream       HIP stream to enqueue on (0 = null stream).
  *
@@ -122,9 +124,9 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
 
 /*
  * fd_workspace_bytes -- workspace size fd_decode_attention needs for these sizes (partial
- * states: 2 slots x 16 heads x (head_dim + 2) fp32 per partition and unit of a group).  The same arguments must
- * be passed to fd_decode_attention.  Returns (size_t)-1 for arguments fd_decode_attention
- * would reject as invalid.
+ * states: 2 slots x 16 (wide-group kernel: 32) heads x (head_dim + 2) fp32 per partition and
+ * unit of a group).  The same arguments must be passed to fd_decode_attention.  Returns
+ * (size_t)-1 for arguments fd_decode_attention would reject as invalid.
  */
 size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                           int max_seq_len, int block_size, int kv_dtype, int num_partitions);
@@ -143,6 +145,43 @@ int fd_plan_partitions(int batch, int num_q_heads, int num_kv_heads, int head_di
  * Device pointers; asynchronous on `stream`.  Returns FD_OK, FD_ERR_INVALID_ARG or FD_ERR_LAUNCH.
  */
 int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
+
+/*
+ * fd_kv_append -- writes the current decode token's K and V rows of every sequence into its
+ * cache row, the step before the attention scan ("第 15 章 · GPU Profiling 与 LLM 推理优化实战",
+ * section 15.9: paged cache writes and the single-token decode append; 15.11: per-token k/v
+ * scales; 15.18: row-wise absmax -> scale -> quantise).  All pointers are device pointers owned
+ * by the caller; nothing is allocated; asynchronous on `stream`.
+ *   k_new, v_new  [batch][num_kv_heads][head_dim] in new_dtype (FD_F32, FD_F16 or FD_BF16).
+ *   k_cache, v_cache, block_table / kv_start, max_blocks_per_seq, block_size, kv_dtype,
+ *                scale_mode   as for fd_decode_attention (same layouts, same codes).
+ *   pos          [batch] int32: the token index each sequence's new row is written at (its length
+ *                before this step); a negative value leaves that sequence untouched.  The row is
+ *                block_table[b][pos / block_size] * block_size + pos % block_size (paged) or
+ *                kv_start[b] + pos (contiguous).
+ *   k_scale, v_scale  E4M3 only.  FD_SCALE_PER_TOKEN_HEAD: written, per (row, kv head), as
+ *                amax |row| / 448 in fp32 (1 for an all-zero row), and each value is stored as
+ *                the E4M3 code nearest to x / scale (ties to even).  FD_SCALE_PER_TENSOR: the
+ *                given k_scale[0] / v_scale[0] are used (not written); x / scale saturates at
+ *                +-448.  f16 / bf16 caches (scale_mode FD_SCALE_NONE) store x rounded to
+ *                nearest even.
+ * Device-side contract (not checked): the table entry of block pos / block_size is a valid block
+ * id and pos < max_blocks_per_seq * block_size (paged), the row exists (contiguous); inputs are
+ * finite.  Host-checked errors as for fd_decode_attention: FD_ERR_INVALID_ARG (null pointers,
+ * batch or heads <= 0, both or neither of block_table / kv_start, a dtype or scale_mode not
+ * allowed), FD_ERR_UNSUPPORTED (head_dim not 64 / 128, block_size not 32 / 64), FD_ERR_LAUNCH.
+ */
+int fd_kv_append(const void *k_new, const void *v_new, int new_dtype, void *k_cache, void *v_cache,
+                 const int32_t *block_table, int max_blocks_per_seq, const int32_t *kv_start,
+                 const int32_t *pos, int batch, int num_kv_heads, int head_dim, int block_size,
+                 int kv_dtype, int scale_mode, float *k_scale, float *v_scale, hipStream_t stream);
+
+/*
+ * fd_fp8_e4m3_encode -- diagnostic: out[i] = the E4M3 code fd_kv_append stores for the
+ * quotient in[i] (clamped to +-448, nearest E4M3 value, ties to even), n values, device
+ * pointers, asynchronous on `stream`.  Returns FD_OK, FD_ERR_INVALID_ARG or FD_ERR_LAUNCH.
+ */
+int fd_fp8_e4m3_encode(const float *in, uint8_t *out, int n, hipStream_t stream);
 
 /*
  * fd_set_profile_events -- diagnostic timing hook.  While set (non-NULL), every later

@@ -132,3 +132,42 @@ def test_read_probe_rejects_bad_arguments():
 
 def test_fp8_decode_rejects_bad_count():
     assert fd.lib().fd_fp8_e4m3_decode(None, None, -1, None) == fd.FD_ERR_INVALID_ARG
+
+
+def test_fp8_encode_rejects_bad_count():
+    assert fd.lib().fd_fp8_e4m3_encode(None, None, -1, None) == fd.FD_ERR_INVALID_ARG
+    assert fd.lib().fd_fp8_e4m3_encode(None, None, 5, None) == fd.FD_ERR_INVALID_ARG
+
+
+# fd_kv_append: a valid argument set with fake device pointers; each case perturbs one field.
+def good_append(**kw):
+    a = dict(k_new=0x1000, v_new=0x2000, new_dtype=fd.FD_BF16, k_cache=0x3000, v_cache=0x4000,
+             block_table=0x5000, max_blocks_per_seq=8, kv_start=None, pos=0x6000, batch=4,
+             num_kv_heads=2, head_dim=128, block_size=64, kv_dtype=fd.FD_FP8_E4M3,
+             scale_mode=fd.FD_SCALE_PER_TOKEN_HEAD, k_scale=0x7000, v_scale=0x8000, stream=None)
+    a.update(kw)
+    return a
+
+
+BAD_APPEND = [
+    (dict(k_new=None), fd.FD_ERR_INVALID_ARG),
+    (dict(v_cache=None), fd.FD_ERR_INVALID_ARG),
+    (dict(pos=None), fd.FD_ERR_INVALID_ARG),
+    (dict(batch=0), fd.FD_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), fd.FD_ERR_INVALID_ARG),
+    (dict(kv_start=0x9000), fd.FD_ERR_INVALID_ARG),            # both table and kv_start
+    (dict(block_table=None), fd.FD_ERR_INVALID_ARG),           # neither
+    (dict(new_dtype=fd.FD_FP8_E4M3), fd.FD_ERR_INVALID_ARG),   # new rows are f32/f16/bf16
+    (dict(kv_dtype=fd.FD_F32), fd.FD_ERR_INVALID_ARG),
+    (dict(scale_mode=fd.FD_SCALE_NONE), fd.FD_ERR_INVALID_ARG),  # E4M3 needs a scale mode
+    (dict(v_scale=None), fd.FD_ERR_INVALID_ARG),
+    (dict(kv_dtype=fd.FD_F16), fd.FD_ERR_INVALID_ARG),         # f16 cache with a scale mode
+    (dict(head_dim=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(block_size=16), fd.FD_ERR_UNSUPPORTED),
+    (dict(max_blocks_per_seq=0), fd.FD_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("change,expect", BAD_APPEND, ids=[str(sorted(c)) for c, _ in BAD_APPEND])
+def test_kv_append_bad_arguments_rejected_before_launch(change, expect):
+    assert fd.kv_append_raw(**good_append(**change)) == expect
