@@ -146,7 +146,7 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     }
     if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
     if (block_table) {
-        if (block_size != 32 && block_size != 64) return FD_ERR_UNSUPPORTED;
+        if (block_size != 16 && block_size != 32 && block_size != 64) return FD_ERR_UNSUPPORTED;
         if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
         if ((long)max_seq_len > (long)max_blocks_per_seq * block_size) return FD_ERR_INVALID_ARG;
     }
@@ -225,7 +225,7 @@ int fd_kv_append(const void *k_new, const void *v_new, int new_dtype, void *k_ca
     }
     if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
     if (block_table) {
-        if (block_size != 32 && block_size != 64) return FD_ERR_UNSUPPORTED;
+        if (block_size != 16 && block_size != 32 && block_size != 64) return FD_ERR_UNSUPPORTED;
         if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
     }
     fd::AppendParams a;

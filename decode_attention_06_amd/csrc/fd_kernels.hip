@@ -82,10 +82,11 @@ struct TileRaw {
 };
 
 // Lane-dependent byte offsets of a full tile's loads (the rest of each address is wave-uniform
-// and folded into the scalar base pointer):
-//   K  row 16*half + c, elements 4E*L + E*g:      k = c*row_bytes + E*g*EB   (+16*half*row_bytes + 4E*L*EB)
-//   V  row pv_token(g, j), elements DT*c ..:      v = 4g*row_bytes + DT*c*EB  (+ (j < 4 ? j : 12 + j)*row_bytes)
-//   scale of token pv_token(g, c & 7), in floats: s = pv_token(g, c & 7) * hkv
+// and folded into the scalar base pointer of the token's 16-row half -- the two halves of a tile
+// are 16 rows apart in one block, or in two blocks of 16 tokens):
+//   K  row c of half `half`, elements 4E*L + E*g:  k = c*row_bytes + E*g*EB   (+ 4E*L*EB)
+//   V  row 4g + (j & 3) of half j >> 2, elements DT*c ..:  v = 4g*row_bytes + DT*c*EB  (+ (j & 3)*row_bytes)
+//   scale of token pv_token(g, c & 7) (half (c & 7) >> 2), in floats: s = (4g + (c & 3)) * hkv
 struct LaneOffsets {
     uint32_t k, v, s;
 };
@@ -96,7 +97,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int g, int c, uint32_t row_b
     LaneOffsets o;
     o.k = (uint32_t)c * row_bytes + (uint32_t)(G::E * g * G::EB);
     o.v = (uint32_t)(4 * g) * row_bytes + (uint32_t)(G::DT * c * G::EB);
-    o.s = (uint32_t)pv_token(g, c & 7) * (uint32_t)hkv;
+    o.s = (uint32_t)(4 * g + (c & 3)) * (uint32_t)hkv;
     return o;
 }
 
@@ -121,42 +122,63 @@ __device__ __forceinline__ void load_v_chunk(uint32_t (&dst)[VDW], const uint8_t
     }
 }
 
+// First rows of a tile's two 16-token halves: K/V bytes of half 1 start h1 bytes (scales h1s
+// floats) after those of half 0 -- 16 rows, unless the cache has blocks of 16 tokens (B16).
+struct TileBase {
+    const uint8_t *k, *v;
+    const float *s;
+    int64_t h1, h1s;
+};
+
 // Full tile: 32 valid tokens.
-template <int D, int KVT, int SCALE, bool NT>
+template <int D, int KVT, int SCALE, bool NT, bool B16>
 __device__ __forceinline__ void load_tile(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
-                                          const uint8_t *kt, const uint8_t *vt, const float *st,
-                                          const LaneOffsets &o, uint32_t row_bytes) {
+                                          const TileBase &t, int c, const LaneOffsets &o, uint32_t row_bytes,
+                                          int hkv) {
     using G = Geometry<D, KVT>;
+    // offset of half 1: 16 rows in one block, or wherever the next 16-token block lies
+    const int64_t h1 = B16 ? t.h1 : (int64_t)16 * row_bytes;
+    const int64_t h1s = B16 ? t.h1s : (int64_t)16 * hkv;
 #pragma unroll
     for (int half = 0; half < 2; half++)
 #pragma unroll
         for (int L = 0; L < G::KLOADS; L++)
-            r.k[half][L] = ld_kv<NT, u32x4_t>(kt + (size_t)(16 * half) * row_bytes + 4 * G::E * L * G::EB + o.k);
+            r.k[half][L] = ld_kv<NT, u32x4_t>(t.k + (half ? h1 : 0) + 4 * G::E * L * G::EB + o.k);
 #pragma unroll
-    for (int j = 0; j < 8; j++) load_v_chunk<G::VDW, NT>(r.v[j], vt + (size_t)(j < 4 ? j : 12 + j) * row_bytes + o.v);
-    if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[o.s];
+    for (int j = 0; j < 8; j++)
+        load_v_chunk<G::VDW, NT>(r.v[j], t.v + (j < 4 ? 0 : h1) + (size_t)(j & 3) * row_bytes + o.v);
+    if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = t.s[((c & 4) ? h1s : 0) + o.s];
 }
 
 // Partial last tile: tokens past `last` are clamped to `last` (valid rows; masked later).
-template <int D, int KVT, int SCALE, bool NT>
+template <int D, int KVT, int SCALE, bool NT, bool B16>
 __device__ __forceinline__ void load_tile_part(TileRaw<Geometry<D, KVT>::KLOADS, Geometry<D, KVT>::VDW> &r,
-                                               const uint8_t *kt, const uint8_t *vt, const float *st,
-                                               int g, int c, uint32_t row_bytes, int hkv, int last) {
+                                               const TileBase &t, int g, int c, uint32_t row_bytes, int hkv,
+                                               int last) {
     using G = Geometry<D, KVT>;
+    // byte offset of tile-relative token `tok` (< 32) from the half-0 base
+    auto row_off = [&](int tok) -> int64_t {
+        if constexpr (!B16) return (uint32_t)tok * row_bytes;  // 32-bit: a tile spans < 2^32 bytes
+        return tok < 16 ? (int64_t)tok * row_bytes : t.h1 + (int64_t)(tok - 16) * row_bytes;
+    };
 #pragma unroll
     for (int half = 0; half < 2; half++) {
-        const uint32_t tok = (uint32_t)min(16 * half + c, last);
+        const int64_t off = row_off(min(16 * half + c, last));
 #pragma unroll
         for (int L = 0; L < G::KLOADS; L++)
-            r.k[half][L] = ld_kv<NT, u32x4_t>(kt + tok * row_bytes + (uint32_t)(4 * G::E * L + G::E * g) * G::EB);
+            r.k[half][L] = ld_kv<NT, u32x4_t>(t.k + off + (uint32_t)(4 * G::E * L + G::E * g) * G::EB);
     }
 #pragma unroll
     for (int j = 0; j < 8; j++)
-        load_v_chunk<G::VDW, NT>(r.v[j], vt + (uint32_t)min(pv_token(g, j), last) * row_bytes + (uint32_t)(G::DT * c * G::EB));
-    if constexpr (SCALE == SC_TOKEN_HEAD) r.sc = st[(uint32_t)min(pv_token(g, c & 7), last) * (uint32_t)hkv];
+        load_v_chunk<G::VDW, NT>(r.v[j], t.v + row_off(min(pv_token(g, j), last)) + (uint32_t)(G::DT * c * G::EB));
+    if constexpr (SCALE == SC_TOKEN_HEAD) {
+        const int tok = min(pv_token(g, c & 7), last);
+        if constexpr (!B16) r.sc = t.s[(uint32_t)tok * (uint32_t)hkv];
+        else r.sc = t.s[tok < 16 ? (int64_t)tok * hkv : t.h1s + (int64_t)(tok - 16) * hkv];
+    }
 }
 
-template <int D, int KVT, int QT, int SCALE, bool PAGED, bool NT>
+template <int D, int KVT, int QT, int SCALE, bool PAGED, bool NT, bool B16>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
 void partition_kernel(Params p) {
     using G = Geometry<D, KVT>;
@@ -249,7 +271,7 @@ void partition_kernel(Params p) {
         n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
     };
     struct Desc {
-        int64_t row0;             // first cache row of the tile
+        int64_t row0, row1;       // first cache rows of the tile's two 16-token halves
         int b, u_in, t0, last;    // sequence, unit in sequence, first token, last valid token in tile
         int seg;                  // segment index within the workgroup's range
         bool first, lastseg, whole;
@@ -259,11 +281,19 @@ void partition_kernel(Params p) {
         d.u_in = grp * p.wpg + wave;
         d.t0 = tt * kTile;
         d.last = min(n - d.t0, kTile) - 1;
-        if constexpr (PAGED)
+        if constexpr (PAGED) {
             d.row0 = (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + d.t0 / p.block_size) *
                          p.block_size + (d.t0 % p.block_size);
-        else
+            // blocks of 16 tokens: the second half sits in the next block (if the tile reaches it)
+            if constexpr (B16)
+                d.row1 = d.last < 16 ? d.row0 + 16
+                                     : (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 + 16) / 16) * 16;
+            else
+                d.row1 = d.row0 + 16;
+        } else {
             d.row0 = (int64_t)ld_uniform(p.kv_start, b) + d.t0;
+            d.row1 = d.row0 + 16;
+        }
         d.seg = seg;
         d.first = (tt == seg_start);
         d.lastseg = (tt + 1 == Tb) || (pos + 1 == hi);
@@ -315,13 +345,16 @@ void partition_kernel(Params p) {
 
     auto issue = [&](TileRaw<KLOADS, VDW> &r, const Desc &d) {
         const int kvh = d.u_in / p.nhb;
-        const uint8_t *kt = (const uint8_t *)p.k + (size_t)kvh * D * EB + (size_t)d.row0 * row_bytes;
-        const uint8_t *vt = (const uint8_t *)p.v + (size_t)kvh * D * EB + (size_t)d.row0 * row_bytes;
-        const float *st = nullptr;
+        TileBase t;
+        t.k = (const uint8_t *)p.k + (size_t)kvh * D * EB + (size_t)d.row0 * row_bytes;
+        t.v = (const uint8_t *)p.v + (size_t)kvh * D * EB + (size_t)d.row0 * row_bytes;
+        t.h1 = (d.row1 - d.row0) * (int64_t)row_bytes;
+        t.h1s = (d.row1 - d.row0) * (int64_t)p.hkv;
+        t.s = nullptr;
         // lane 16g+i holds the k (i < 8) or v (i >= 8) scale of token pv_token(g, i & 7)
-        if constexpr (SCALE == SC_TOKEN_HEAD) st = ((c & 8) ? p.v_scale : p.k_scale) + kvh + (size_t)d.row0 * p.hkv;
-        if (d.last >= kTile - 1) load_tile<D, KVT, SCALE, NT>(r, kt, vt, st, lofs, row_bytes);
-        else load_tile_part<D, KVT, SCALE, NT>(r, kt, vt, st, g, c, row_bytes, p.hkv, d.last);
+        if constexpr (SCALE == SC_TOKEN_HEAD) t.s = ((c & 8) ? p.v_scale : p.k_scale) + kvh + (size_t)d.row0 * p.hkv;
+        if (d.last >= kTile - 1) load_tile<D, KVT, SCALE, NT, B16>(r, t, c, lofs, row_bytes, p.hkv);
+        else load_tile_part<D, KVT, SCALE, NT, B16>(r, t, g, c, row_bytes, p.hkv, d.last);
     };
 
     auto compute = [&](const TileRaw<KLOADS, VDW> &r, const Desc &d) {
@@ -705,12 +738,15 @@ static hipError_t launch_p(const Params &p, hipStream_t stream) {
     dim3 grid(p.nparts), block(64 * p.wpg);
     // with one head block per kv head every KV byte is read by one wave only: stream it
     const bool nt = p.nhb == 1;
-    if (p.block_table) {
-        if (nt) hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, false>), grid, block, 0, stream, p);
+    if (p.block_table && p.block_size == 16) {  // 32-token tiles span two blocks
+        if (nt) hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, true, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, false, true>), grid, block, 0, stream, p);
+    } else if (p.block_table) {
+        if (nt) hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, true, false>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, true, false, false>), grid, block, 0, stream, p);
     } else {
-        if (nt) hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, false, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, false, false>), grid, block, 0, stream, p);
+        if (nt) hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, false, true, false>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((partition_kernel<D, KVT, QT, SCALE, false, false, false>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }

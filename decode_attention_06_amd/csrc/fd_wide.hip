@@ -138,7 +138,7 @@ __device__ __forceinline__ void wg_barrier() {
 
 }  // namespace
 
-template <int WPG, int NSLOT, int QT, int SCALE, bool PAGED>
+template <int WPG, int NSLOT, int QT, int SCALE, bool PAGED, bool B16>
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(3)))
 void wide_partition_kernel(Params p) {
     using LY = WideLayout<WPG, SCALE>;
@@ -248,29 +248,41 @@ void wide_partition_kernel(Params p) {
     auto issue = [&](const Cursor &k, int si) {
         const int t0 = k.tt * kTile;
         const int last = min(k.n - t0, kTile) - 1;  // rows past it repeat it (valid; masked later)
-        int64_t row0;
-        if constexpr (PAGED)
+        // first cache rows of the tile's two 16-token halves (blocks of 16 tokens: two blocks)
+        int64_t row0, row1;
+        if constexpr (PAGED) {
             row0 = (int64_t)ld_uniform(p.block_table, (size_t)k.b * p.max_blocks + t0 / p.block_size) *
                        p.block_size + (t0 % p.block_size);
-        else
+            if constexpr (B16)
+                row1 = last < 16 ? row0 + 16
+                                 : (int64_t)ld_uniform(p.block_table, (size_t)k.b * p.max_blocks + (t0 + 16) / 16) * 16;
+            else
+                row1 = row0 + 16;
+        } else {
             row0 = (int64_t)ld_uniform(p.kv_start, k.b) + t0;
+            row1 = row0 + 16;
+        }
+        auto cache_row = [&](int tok) -> int64_t {
+            if constexpr (!B16) return row0 + tok;
+            return tok < 16 ? row0 + tok : row1 + (tok - 16);
+        };
         const int kvh = (k.grp * WPG) / p.nhb;
         uint8_t *slot = ring + si * LY::SLOT;
-        const uint8_t *kb = (const uint8_t *)p.k + (size_t)kvh * D + (size_t)row0 * row_bytes;
-        const uint8_t *vb = (const uint8_t *)p.v + (size_t)kvh * D + (size_t)row0 * row_bytes;
+        const uint8_t *kb = (const uint8_t *)p.k + (size_t)kvh * D;
+        const uint8_t *vb = (const uint8_t *)p.v + (size_t)kvh * D;
 #pragma unroll
         for (int u = 0; u < LY::OPS_KV; u++) {
             const int o = wave * LY::OPS_KV + u;  // copies 0..3: K rows 8o..8o+7; 4..7: V rows
             const int row = 8 * (o & 3) + (lane >> 3);
-            const uint32_t rc = (uint32_t)min(row, last);
+            const size_t src = (size_t)cache_row(min(row, last)) * row_bytes;
             if (o < 4)
-                copy16_to_lds(kb + rc * row_bytes + 16 * ((lane & 7) ^ (row & 7)), slot + o * 1024);
+                copy16_to_lds(kb + src + 16 * ((lane & 7) ^ (row & 7)), slot + o * 1024);
             else
-                copy16_to_lds(vb + rc * row_bytes + 16 * (lane & 7), slot + LY::KV_BYTES + (o - 4) * 1024);
+                copy16_to_lds(vb + src + 16 * (lane & 7), slot + LY::KV_BYTES + (o - 4) * 1024);
         }
         if constexpr (SCALE == SC_TOKEN_HEAD) {
             const int t = min(lane & 31, last);
-            const float *sb = (lane < 32 ? p.k_scale : p.v_scale) + kvh + (size_t)(row0 + t) * p.hkv;
+            const float *sb = (lane < 32 ? p.k_scale : p.v_scale) + kvh + (size_t)cache_row(t) * p.hkv;
             copy4_to_lds(sb, slot + 2 * LY::KV_BYTES + wave * LY::SC_BYTES);
         }
     };
@@ -490,10 +502,12 @@ static hipError_t launch_w(const Params &p, hipStream_t stream) {
     // in one CU's 160 KB of LDS
     constexpr int NSLOT = WPG == 2 ? 3 : (SCALE == SC_TOKEN_HEAD ? 5 : 6);
     dim3 grid(p.nparts), block(64 * WPG);
-    if (p.block_table)
-        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, true>), grid, block, 0, stream, p);
+    if (p.block_table && p.block_size == 16)  // 32-token tiles span two blocks
+        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
+    else if (p.block_table)
+        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, true, false>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, false, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
     FD_OK = 0,
     FD_ERR_INVALID_ARG = 1, /* null pointer, bad count, inconsistent dtype / scale mode      */
-    FD_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, block_size not 32/64, dtype combination   */
+    FD_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, block_size not 16/32/64, dtype combination */
     FD_ERR_WORKSPACE = 3,   /* workspace missing, too small or not 256-byte aligned           */
     FD_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch                        */
 } fd_status;
@@ -86,7 +86,8 @@ typedef enum {
  *   max_seq_len  host-side upper bound of seq_len (<= 2^24); sizes the grid and the workspace
  *                only.
  *                Paged mode needs max_seq_len <= max_blocks_per_seq * block_size.
- *   block_size   32 or 64 in paged mode; ignored (pass 0) in contiguous mode.
+ *   block_size   16, 32 or 64 in paged mode (16: the 15.9 page size; a 32-token kernel tile then
+ *                spans two blocks); ignored (pass 0) in contiguous mode.
  *   scale_mode   FD_SCALE_NONE for f16/bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 KV.
  *   k_scale,     fp32 dequantisation scales (value = decode(byte) * scale), NULL when none.
  *   v_scale
@@ -169,7 +170,7 @@ int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream)
  * id and pos < max_blocks_per_seq * block_size (paged), the row exists (contiguous); inputs are
  * finite.  Host-checked errors as for fd_decode_attention: FD_ERR_INVALID_ARG (null pointers,
  * batch or heads <= 0, both or neither of block_table / kv_start, a dtype or scale_mode not
- * allowed), FD_ERR_UNSUPPORTED (head_dim not 64 / 128, block_size not 32 / 64), FD_ERR_LAUNCH.
+ * allowed), FD_ERR_UNSUPPORTED (head_dim not 64 / 128, block_size not 16 / 32 / 64), FD_ERR_LAUNCH.
  */
 int fd_kv_append(const void *k_new, const void *v_new, int new_dtype, void *k_cache, void *v_cache,
                  const int32_t *block_table, int max_blocks_per_seq, const int32_t *kv_start,

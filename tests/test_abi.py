@@ -108,7 +108,8 @@ BAD = [
     (dict(num_partitions=-2), fd.FD_ERR_INVALID_ARG),
     (dict(max_seq_len=(1 << 24) + 32, max_blocks_per_seq=(1 << 19) + 1), fd.FD_ERR_INVALID_ARG),
     (dict(head_dim=96), fd.FD_ERR_UNSUPPORTED),
-    (dict(block_size=16, max_blocks_per_seq=16), fd.FD_ERR_UNSUPPORTED),
+    (dict(block_size=8, max_blocks_per_seq=256), fd.FD_ERR_UNSUPPORTED),
+    (dict(block_size=128), fd.FD_ERR_UNSUPPORTED),
     (dict(max_blocks_per_seq=0), fd.FD_ERR_INVALID_ARG),
     (dict(workspace=None), fd.FD_ERR_WORKSPACE),
     (dict(workspace_bytes_=16), fd.FD_ERR_WORKSPACE),
@@ -121,6 +122,11 @@ def test_bad_arguments_rejected_before_launch(change, expect):
     # valid-but-fake pointers: if validation let this through, the launch would fail with
     # FD_ERR_LAUNCH (no GPU here) -- the test needs the specific host-side code instead.
     assert fd.decode_attention_raw(**good_args(**change)) == expect
+
+
+def test_block_size_16_accepted_up_to_the_launch():
+    # without a GPU the launch itself fails: the host checks passed
+    assert fd.decode_attention_raw(**good_args(block_size=16, max_blocks_per_seq=128)) == fd.FD_ERR_LAUNCH
 
 
 def test_read_probe_rejects_bad_arguments():
@@ -163,7 +169,8 @@ BAD_APPEND = [
     (dict(v_scale=None), fd.FD_ERR_INVALID_ARG),
     (dict(kv_dtype=fd.FD_F16), fd.FD_ERR_INVALID_ARG),         # f16 cache with a scale mode
     (dict(head_dim=96), fd.FD_ERR_UNSUPPORTED),
-    (dict(block_size=16), fd.FD_ERR_UNSUPPORTED),
+    (dict(block_size=8), fd.FD_ERR_UNSUPPORTED),
+    (dict(block_size=128), fd.FD_ERR_UNSUPPORTED),
     (dict(max_blocks_per_seq=0), fd.FD_ERR_INVALID_ARG),
 ]
 

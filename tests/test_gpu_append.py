@@ -92,6 +92,7 @@ APPEND_CASES = [
     ("f16_f32in", dict(batch=6, hkv=2, d=128, kv="f16", scale="none", new="f32", paged=True)),
     ("bf16_f32in_contig", dict(batch=4, hkv=2, d=128, kv="bf16", scale="none", new="f32", paged=False)),
     ("bf16_bf16in_d64", dict(batch=4, hkv=3, d=64, kv="bf16", scale="none", new="bf16", paged=True, bs=32)),
+    ("fp8_tok_bf16in_bs16", dict(batch=8, hkv=2, d=128, kv="fp8_e4m3", scale="token_head", new="bf16", paged=True, bs=16)),
 ]
 
 

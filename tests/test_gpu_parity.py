@@ -118,6 +118,15 @@ SMALL = [
                                    q="bf16", scale="tensor", block_size=32)),
     ("wide_g64_tensor_f16q", dict(batch=2, hq=64, hkv=1, d=128, seq_lens=[2500, 95], kv="fp8_e4m3",
                                   q="f16", scale="tensor", block_size=64)),
+    # 16-token pages: every 32-token tile spans two blocks
+    ("bs16_fp8_tok_g8", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[700, 17, 48], kv="fp8_e4m3",
+                             q="bf16", scale="token_head", block_size=16)),
+    ("bs16_bf16_g4_d64", dict(batch=2, hq=8, hkv=2, d=64, seq_lens=[333, 16], kv="bf16", q="bf16",
+                              scale="none", block_size=16)),
+    ("bs16_wide_g128_tok", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1000, 31], kv="fp8_e4m3",
+                                q="bf16", scale="token_head", block_size=16)),
+    ("bs16_wide_g64_tensor", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[65, 300, 1], kv="fp8_e4m3",
+                                  q="bf16", scale="tensor", block_size=16)),
 ]
 
 
@@ -146,6 +155,27 @@ def test_wide_length_edges(n):
                                  max_seq_len=max(lens + [1]))
     for parts in (0, 3):
         check_case(f"wide_len{n}/p{parts}", case, num_partitions=parts)
+
+
+@pytest.mark.parametrize("wide", [False, True])
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 31, 32, 33, 47, 48, 49])
+def test_block16_length_edges(n, wide):
+    lens = [n, 16, n + 16]
+    hq = 128 if wide else 16
+    case = workloads.custom_case(seed=200 + n, device="cuda", batch=3, hq=hq, hkv=1 if wide else 2, d=128,
+                                 seq_lens=lens, kv="fp8_e4m3", q="bf16", scale="token_head", block_size=16,
+                                 max_seq_len=max(lens))
+    for parts in (0, 5):
+        check_case(f"bs16_len{n}{'_wide' if wide else ''}/p{parts}", case, num_partitions=parts)
+
+
+def test_block16_ragged_mix():
+    lens = [0, 1, 5000, 33, 0, 64, 2047, 12000, 31, 0, 700, 96]
+    case = workloads.custom_case(seed=23, device="cuda", batch=len(lens), hq=32, hkv=8, d=128,
+                                 seq_lens=lens, kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=16)
+    for parts in (3, 256):
+        check_case(f"bs16_ragged/p{parts}", case, num_partitions=parts)
 
 
 def test_wide_ragged_mix():
