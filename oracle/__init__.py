@@ -23,8 +23,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-F16, BF16, E4M3 = 1, 2, 3
-_DTYPE = {"f16": F16, "bf16": BF16, "fp8_e4m3": E4M3}
+F16, BF16, E4M3, I8 = 1, 2, 3, 4
+_DTYPE = {"f16": F16, "bf16": BF16, "fp8_e4m3": E4M3, "int8": I8}
 _SCALE = {"none": 0, "tensor": 1, "token_head": 2}
 
 
@@ -91,6 +91,8 @@ def _load():
         lib.orc_bf16_encode.argtypes = [ctypes.c_float]
         lib.orc_quantize_row_e4m3.restype = ctypes.c_float
         lib.orc_quantize_row_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+        lib.orc_quantize_row_i8.restype = ctypes.c_float
+        lib.orc_quantize_row_i8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
         lib.orc_kv_append.restype = ctypes.c_int
         lib.orc_kv_append.argtypes = [ctypes.POINTER(_Append)]
         _lib = lib
@@ -222,6 +224,14 @@ def quantize_row_e4m3(x, scale: float = 0.0):
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.zeros(x.shape[0], dtype=np.uint8)
     sc = _load().orc_quantize_row_e4m3(x.ctypes.data, int(x.shape[0]), float(scale), out.ctypes.data)
+    return out, float(np.float32(sc))
+
+
+def quantize_row_i8(x, scale: float = 0.0):
+    """(codes int8[n], scale) for one fp32 row: scale = amax/127 unless a scale > 0 is given."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.shape[0], dtype=np.int8)
+    sc = _load().orc_quantize_row_i8(x.ctypes.data, int(x.shape[0]), float(scale), out.ctypes.data)
     return out, float(np.float32(sc))
 
 

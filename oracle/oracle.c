@@ -22,7 +22,8 @@
  * Readings where the pages are silent (all stated in the design doc):
  *   - q head h reads kv head h / (QH / KVH).
  *   - FP8 means OCP E4M3FN; a dequantised element is decode(byte) * scale, the scale being
- *     one fp32 per tensor or one fp32 per (token, kv head) stored like the cache rows.
+ *     one fp32 per tensor or one fp32 per (token, kv head) stored like the cache rows.  INT8 KV
+ *     ([CH15] 15.11) is the same with two's-complement int8 codes.
  *   - The empty sequence (seq_len 0) gives out = 0 and lse = -inf.
  *   - lse is the natural log of sum_t exp(s_t).
  */
@@ -34,7 +35,7 @@
 #include <string.h>
 
 /* dtype and scale codes of this file's own interface */
-enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3 };
+enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_I8 = 4 };
 enum { ORC_SCALE_NONE = 0, ORC_SCALE_TENSOR = 1, ORC_SCALE_TOKEN_HEAD = 2 };
 
 typedef struct {
@@ -90,6 +91,7 @@ static double load_elem(const void *base, size_t idx, int dtype) {
     case ORC_F16: return orc_f16_to_double(((const uint16_t *)base)[idx]);
     case ORC_BF16: return orc_bf16_to_double(((const uint16_t *)base)[idx]);
     case ORC_E4M3: return orc_e4m3_to_double(((const uint8_t *)base)[idx]);
+    case ORC_I8: return (double)((const int8_t *)base)[idx];  /* [CH15] 15.11: int8 codes x scale */
     default: return NAN;
     }
 }
@@ -336,6 +338,29 @@ float orc_quantize_row_e4m3(const float *x, int n, float scale_in, uint8_t *out)
     return scale;
 }
 
+/* One row, INT8 ([CH15] 15.18 row-wise absmax, int8 quant; [CH15] 15.11 per-token scales): with
+ * scale_in > 0 use it, else scale = amax / 127 in fp32 (1 for an all-zero row); code[i] = the
+ * integer nearest to x[i] / scale (fp32 quotient; ties to even), clamped to [-127, 127].
+ * Returns the scale used. */
+float orc_quantize_row_i8(const float *x, int n, float scale_in, int8_t *out) {
+    float scale = scale_in;
+    if (!(scale_in > 0.0f)) {
+        float amax = 0.0f;
+        for (int i = 0; i < n; i++) {
+            const float a = fabsf(x[i]);
+            if (a > amax) amax = a;
+        }
+        scale = amax > 0.0f ? amax / 127.0f : 1.0f;
+    }
+    for (int i = 0; i < n; i++) {
+        double q = rint((double)(x[i] / scale));  /* fp32 quotient, exact in double; half to even */
+        if (q > 127.0) q = 127.0;
+        if (q < -127.0) q = -127.0;
+        out[i] = (int8_t)q;
+    }
+    return scale;
+}
+
 typedef struct {
     const float *k_new;         /* [batch][hkv][d] fp32 (f16 / bf16 inputs converted exactly)    */
     const float *v_new;
@@ -376,6 +401,14 @@ int orc_kv_append(const orc_append *a) {
                         orc_quantize_row_e4m3(x, a->d, sc[0], (uint8_t *)cache + base);
                     } else if (a->scale_mode == ORC_SCALE_TOKEN_HEAD) {
                         sc[row * a->hkv + g] = orc_quantize_row_e4m3(x, a->d, 0.0f, (uint8_t *)cache + base);
+                    } else {
+                        return -1;
+                    }
+                } else if (a->kv_dtype == ORC_I8) {
+                    if (a->scale_mode == ORC_SCALE_TENSOR) {
+                        orc_quantize_row_i8(x, a->d, sc[0], (int8_t *)cache + base);
+                    } else if (a->scale_mode == ORC_SCALE_TOKEN_HEAD) {
+                        sc[row * a->hkv + g] = orc_quantize_row_i8(x, a->d, 0.0f, (int8_t *)cache + base);
                     } else {
                         return -1;
                     }

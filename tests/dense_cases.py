@@ -7,6 +7,7 @@ import numpy as np
 import torch
 
 FP8_MAX = 448.0
+I8_MAX = 127.0
 
 
 def quant_rows(x):
@@ -16,6 +17,18 @@ def quant_rows(x):
     return y, s
 
 
+def quant_rows_i8(x):
+    amax = x.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / I8_MAX, torch.ones_like(amax)).to(torch.float32)
+    y = torch.round(x / s.unsqueeze(-1)).clamp(-I8_MAX, I8_MAX).to(torch.int8)
+    return y, s
+
+
+def _fill(kv):
+    """(storage dtype, poison value) of a quantised cache"""
+    return (torch.uint8, 0x7F) if kv == "fp8_e4m3" else (torch.int8, -128)
+
+
 class Dense:
     """Logical per-sequence data: k[b], v[b] stored [n_b][hkv][d]; ks[b], vs[b] scales."""
 
@@ -23,13 +36,14 @@ class Dense:
                  qmul=1.0):
         g = torch.Generator().manual_seed(seed)
         self.lens, self.hq, self.hkv, self.d = list(lens), hq, hkv, d
-        self.kv, self.qd, self.scale = kv, q, (scale if kv == "fp8_e4m3" else "none")
+        self.kv, self.qd, self.scale = kv, q, (scale if kv in ("fp8_e4m3", "int8") else "none")
         qdt = {"f16": torch.float16, "bf16": torch.bfloat16}[q]
         self.q = (torch.randn(len(lens), hq, d, generator=g) * qmul).to(qdt)
         self.k, self.v, self.ks, self.vs = [], [], [], []
         tensor_scale = None
+        qmax = I8_MAX if kv == "int8" else FP8_MAX
         if self.scale == "tensor":
-            tensor_scale = (float(np.float32(2.7 / FP8_MAX)), float(np.float32(3.1 / FP8_MAX)))
+            tensor_scale = (float(np.float32(2.7 / qmax)), float(np.float32(3.1 / qmax)))
         for n in lens:
             for store, sstore, which in ((self.k, self.ks, 0), (self.v, self.vs, 1)):
                 x = torch.randn(n, hkv, d, generator=g)
@@ -41,6 +55,15 @@ class Dense:
                         sstore.append(s)
                     else:
                         b, s = quant_rows(x)
+                        store.append(b)
+                        sstore.append(s)
+                elif kv == "int8":
+                    if self.scale == "tensor":
+                        s = tensor_scale[which]
+                        store.append(torch.round(x / s).clamp(-I8_MAX, I8_MAX).to(torch.int8))
+                        sstore.append(s)
+                    else:
+                        b, s = quant_rows_i8(x)
                         store.append(b)
                         sstore.append(s)
                 else:
@@ -63,13 +86,13 @@ class Dense:
         place = rng.permutation(total)
         mb = max_blocks or max(1, max(nb) if nb else 1)
         table = np.full((len(self.lens), mb), -1, dtype=np.int32)
-        fp8 = self.kv == "fp8_e4m3"
-        sdt = torch.uint8 if fp8 else self.k[0].dtype
+        quant = self.kv in ("fp8_e4m3", "int8")
+        sdt = _fill(self.kv)[0] if quant else self.k[0].dtype
         K = torch.empty(total, bs, self.hkv, self.d, dtype=sdt)
         V = torch.empty_like(K)
-        if fp8:
-            K.fill_(0x7F)
-            V.fill_(0x7F)
+        if quant:
+            K.fill_(_fill(self.kv)[1])
+            V.fill_(_fill(self.kv)[1])
         else:
             K.fill_(float("nan"))
             V.fill_(float("nan"))
@@ -94,14 +117,14 @@ class Dense:
         return kw
 
     def contiguous(self, gap=2):
-        fp8 = self.kv == "fp8_e4m3"
+        quant = self.kv in ("fp8_e4m3", "int8")
         rows = sum(self.lens) + gap * (len(self.lens) + 1)
-        sdt = torch.uint8 if fp8 else self.k[0].dtype
+        sdt = _fill(self.kv)[0] if quant else self.k[0].dtype
         K = torch.empty(rows, self.hkv, self.d, dtype=sdt)
         V = torch.empty_like(K)
-        if fp8:
-            K.fill_(0x7F)
-            V.fill_(0x7F)
+        if quant:
+            K.fill_(_fill(self.kv)[1])
+            V.fill_(_fill(self.kv)[1])
         else:
             K.fill_(float("nan"))
             V.fill_(float("nan"))

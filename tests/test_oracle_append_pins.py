@@ -121,9 +121,35 @@ def test_quantize_zero_row_and_fixed_scale():
     assert [e4m3_value(int(c)) for c in b] == [0.0, 96.0, -96.0, 448.0, -448.0, 24.0]
 
 
+@pytest.mark.parametrize("mag", [1e-3, 1.0, 50.0])
+def test_quantize_row_i8_matches_numpy_round_half_even(mag):
+    g = np.random.default_rng(int(mag * 100) + 3)
+    for _ in range(100):
+        x = (g.standard_normal(128) * mag).astype(np.float32)
+        codes, s = oracle.quantize_row_i8(x)
+        want_s = np.float32(np.abs(x).max()) / np.float32(127.0)
+        assert s == want_s
+        want = np.clip(np.rint(x / want_s), -127, 127).astype(np.int8)   # fp32 quotient, half to even
+        assert np.array_equal(codes, want)
+        i = int(np.argmax(np.abs(x)))
+        assert int(codes[i]) == (127 if x[i] > 0 else -127)
+
+
+def test_quantize_row_i8_ties_zero_row_and_fixed_scale():
+    codes, _ = oracle.quantize_row_i8(np.array([0.5, 1.5, 2.5, -0.5, -2.5], np.float32), scale=1.0)
+    assert codes.tolist() == [0, 2, 2, 0, -2]                                   # ties to even
+    codes, s = oracle.quantize_row_i8(np.zeros(32, np.float32))
+    assert s == 1.0 and not codes.any()
+    codes, _ = oracle.quantize_row_i8(np.array([300.0, -1e9, 12.0], np.float32), scale=0.5)
+    assert codes.tolist() == [127, -127, 24]                                    # saturation
+
+
 # ---------------------------------------------------------------- append
 def _paged_cache(kv, nblocks, bs, hkv, d, g):
-    if kv == "fp8_e4m3":
+    if kv == "int8":
+        k = torch.from_numpy(g.integers(-127, 128, size=(nblocks, bs, hkv, d), dtype=np.int8))
+        v = torch.from_numpy(g.integers(-127, 128, size=(nblocks, bs, hkv, d), dtype=np.int8))
+    elif kv == "fp8_e4m3":
         k = torch.from_numpy(g.integers(0, 0x7E, size=(nblocks, bs, hkv, d), dtype=np.uint8))
         v = torch.from_numpy(g.integers(0, 0x7E, size=(nblocks, bs, hkv, d), dtype=np.uint8))
     else:
@@ -134,6 +160,7 @@ def _paged_cache(kv, nblocks, bs, hkv, d, g):
 
 
 @pytest.mark.parametrize("kv,scale", [("fp8_e4m3", "token_head"), ("fp8_e4m3", "tensor"),
+                                      ("int8", "token_head"), ("int8", "tensor"),
                                       ("f16", "none"), ("bf16", "none")])
 def test_append_writes_exactly_the_target_rows(kv, scale):
     g = np.random.default_rng(9)
@@ -165,8 +192,9 @@ def test_append_writes_exactly_the_target_rows(kv, scale):
         for h in range(hkv):
             for new, cache, sc, fixed in ((k_new, kc, ksc, 0.02), (v_new, vc, vsc, 0.03)):
                 x = new[b, h].numpy()
-                if kv == "fp8_e4m3":
-                    want, s = oracle.quantize_row_e4m3(x, fixed if scale == "tensor" else 0.0)
+                if kv in ("fp8_e4m3", "int8"):
+                    quant = oracle.quantize_row_e4m3 if kv == "fp8_e4m3" else oracle.quantize_row_i8
+                    want, s = quant(x, fixed if scale == "tensor" else 0.0)
                     assert np.array_equal(cache[row, h], want)
                     if scale == "token_head":
                         assert sc.reshape(-1, hkv)[row, h] == s

@@ -93,6 +93,8 @@ BRUTE_SHAPES = [
     (2, [12, 7], 4, 1, 8, "bf16", "bf16", "none", 4),
     (3, [3, 20, 1], 2, 2, 8, "f16", "f16", "none", 8),
     (4, [40], 8, 1, 64, "fp8_e4m3", "f16", "token_head", 32),
+    (5, [7, 30], 4, 2, 16, "int8", "bf16", "token_head", 8),
+    (6, [13, 2], 2, 1, 8, "int8", "f16", "tensor", 4),
 ]
 
 
@@ -108,7 +110,7 @@ def test_oracle_vs_bruteforce_paged(shape):
     np.testing.assert_allclose(lse, np.array(bl), rtol=1e-12, atol=1e-13)
 
 
-@pytest.mark.parametrize("shape", BRUTE_SHAPES[:3], ids=lambda s: f"seed{s[0]}")
+@pytest.mark.parametrize("shape", BRUTE_SHAPES[:3] + BRUTE_SHAPES[5:], ids=lambda s: f"seed{s[0]}")
 def test_oracle_vs_bruteforce_contiguous(shape):
     seed, lens, hq, hkv, d, kv, qd, scale, _ = shape
     dn = Dense(seed, lens, hq, hkv, d, kv=kv, q=qd, scale=scale)

@@ -17,6 +17,7 @@ Workloads (sizes as specified for the decode workloads this library targets):
                         E4M3 KV with one per-tensor scale, block_size 64.
 * ``ragged_fp8``        batch 256, 90 % seq_len ~ U[256, 2048] and 10 % ~ U[32K, 128K],
                         32 q / 8 kv heads, head_dim 128, E4M3 KV, block_size 32, shuffled blocks.
+* ``int8_32k``          ``fp8_32k`` with INT8 KV (per-(token, kv-head) scales).
 
 Recipe (the readings are listed in the design doc):
 
@@ -28,7 +29,8 @@ Recipe (the readings are listed in the design doc):
 * FP8 rows are quantised row-absmax style, the way activations are quantised in the
   "小算子融合 residual + RMSNorm + quant" passage of the ch.15 profiling page:
   ``scale = amax / 448`` (1 if amax is 0), ``byte = RNE(x / scale)`` via torch's own
-  ``float8_e4m3fn`` cast.  Per-tensor scale takes amax over the whole tensor.
+  ``float8_e4m3fn`` cast.  Per-tensor scale takes amax over the whole tensor.  INT8 rows the
+  same way with ``scale = amax / 127`` and ``code = round-half-even(x / scale)`` in [-127, 127].
 * Paged caches hold ``sum(ceil(n_b / bs))`` live blocks plus 8 spare blocks, placed by a random
   permutation (the "fragmented" page placement of the ch.15 paged-KV scan passage).
   Everything the kernels must never read is poisoned: slots past ``seq_len`` in the last block,
@@ -49,7 +51,9 @@ SPARE_BLOCKS = 8
 CONTIG_GAP_ROWS = 3
 
 # dtype names shared by the binding, the oracle wrapper and the tests
-KV_DTYPES = ("f16", "bf16", "fp8_e4m3")
+KV_DTYPES = ("f16", "bf16", "fp8_e4m3", "int8")
+QUANTISED = ("fp8_e4m3", "int8")
+INT8_MAX = 127.0
 Q_DTYPES = ("f16", "bf16")
 SCALE_MODES = ("none", "tensor", "token_head")
 
@@ -67,6 +71,8 @@ WORKLOADS = {
     "ragged_fp8": dict(batch=256, hq=32, hkv=8, d=128,
                        lens=("mix", 0.1, (256, 2048), (32768, 131072)), kv="fp8_e4m3",
                        q="bf16", block_size=32, scale="token_head", paged=True),
+    "int8_32k": dict(batch=32, hq=64, hkv=8, d=128, lens=("loguniform", 1024, 32768), kv="int8",
+                     q="bf16", block_size=64, scale="token_head", paged=True),
 }
 
 
@@ -101,7 +107,7 @@ class Case:
         return self.hq // self.hkv
 
     def kv_elem_bytes(self) -> int:
-        return 1 if self.kv_dtype == "fp8_e4m3" else 2
+        return 1 if self.kv_dtype in QUANTISED else 2
 
     def kv_read_bytes(self) -> int:
         """K+V payload plus scale bytes the method must read for this step."""
@@ -145,7 +151,8 @@ def draw_seq_lens(spec, batch: int, rng: np.random.Generator) -> list:
 
 
 def _nan_bits(dtype: str) -> int:
-    return {"f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}[dtype]
+    # int8 has no NaN: -128 lies outside the quantised range [-127, 127] (and its scales are NaN)
+    return {"f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F, "int8": 0x80}[dtype]
 
 
 def _quant_rows(x: torch.Tensor):
@@ -163,10 +170,24 @@ def _quant_tensor(x: torch.Tensor, amax: float):
     return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
 
 
+def _quant_rows_i8(x: torch.Tensor):
+    """Row-absmax INT8 quantisation of the last dim: returns (int8 codes, fp32 scales)."""
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / INT8_MAX, torch.ones_like(amax))
+    y = torch.round(x / scale.unsqueeze(-1)).clamp_(-INT8_MAX, INT8_MAX)
+    return y.to(torch.int8), scale.to(torch.float32)
+
+
+def _quant_tensor_i8(x: torch.Tensor, amax: float):
+    scale = float(np.float32(amax / INT8_MAX if amax > 0 else 1.0))
+    y = torch.round(x / scale).clamp_(-INT8_MAX, INT8_MAX)
+    return y.to(torch.int8), scale
+
+
 def _fill_store(n_rows: int, hkv: int, d: int, kv: str, scale: str, device, gen,
                 chunk_rows: int = 1 << 19):
     """Generate K and V row stores ([n_rows][hkv][d]) plus scales, chunk by chunk."""
-    storage_dtype = torch.uint8 if kv == "fp8_e4m3" else _TORCH[kv]
+    storage_dtype = {"fp8_e4m3": torch.uint8, "int8": torch.int8}.get(kv) or _TORCH[kv]
     k = torch.empty((n_rows, hkv, d), dtype=storage_dtype, device=device)
     v = torch.empty_like(k)
     ks = vs = None
@@ -177,8 +198,9 @@ def _fill_store(n_rows: int, hkv: int, d: int, kv: str, scale: str, device, gen,
         # per-tensor amax needs the whole tensor: generate at once (sizes here allow it)
         ksrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32)
         vsrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32)
-        kb, kscale = _quant_tensor(ksrc, float(ksrc.abs().max()))
-        vb, vscale = _quant_tensor(vsrc, float(vsrc.abs().max()))
+        quant = _quant_tensor_i8 if kv == "int8" else _quant_tensor
+        kb, kscale = quant(ksrc, float(ksrc.abs().max()))
+        vb, vscale = quant(vsrc, float(vsrc.abs().max()))
         k.copy_(kb)
         v.copy_(vb)
         del ksrc, vsrc
@@ -189,8 +211,8 @@ def _fill_store(n_rows: int, hkv: int, d: int, kv: str, scale: str, device, gen,
         r1 = min(n_rows, r0 + chunk_rows)
         for dst, sdst in ((k, ks), (v, vs)):
             src = torch.randn((r1 - r0, hkv, d), generator=gen, device=device, dtype=torch.float32)
-            if kv == "fp8_e4m3":
-                b, s = _quant_rows(src)
+            if kv in QUANTISED:
+                b, s = (_quant_rows_i8 if kv == "int8" else _quant_rows)(src)
                 dst[r0:r1] = b
                 sdst[r0:r1] = s
             else:
@@ -203,6 +225,8 @@ def _poison_rows(t: torch.Tensor, rows: torch.Tensor, nan_bits: int):
         return
     if t.dtype == torch.uint8:
         t[rows] = nan_bits
+    elif t.dtype == torch.int8:
+        t[rows] = int(np.uint8(nan_bits).view(np.int8))
     elif t.dtype == torch.float32:
         t[rows] = float("nan")
     else:
@@ -227,7 +251,7 @@ def _build(name, cfg, seed, device, seq_lens) -> Case:
     hq, hkv, d = cfg["hq"], cfg["hkv"], cfg["d"]
     kv, qd, scale, paged = cfg["kv"], cfg["q"], cfg["scale"], cfg["paged"]
     bs = cfg["block_size"] if paged else 0
-    if kv != "fp8_e4m3":
+    if kv not in QUANTISED:
         scale = "none"
     max_seq_len = int(cfg.get("max_seq_len", max(seq_lens) if seq_lens else 0))
     gen = torch.Generator(device=device).manual_seed(seed)
