@@ -1,6 +1,10 @@
 """Benchmark: one flash-decoding step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fp8_32k] [--num-partitions 0]
+                    [--block-size B] [--seq-len T] [--layout contiguous|ordered|fragmented] [--batch N]
+
+The last four override the named workload (page-size / length / layout sweeps); the default run
+uses none of them.
 
 Prints ONE JSON line.  A step is one fd_decode_attention call (split-KV partition kernel +
 combine kernel) over one batch of synthetic, seeded inputs already resident in HBM.  Each step
@@ -50,9 +54,20 @@ def partition_kernel_name(case) -> str:
     return "wide_partition_kernel" if wide else "partition_kernel"
 
 
-def measured_traffic(workload: str):
+def compute_note(case) -> str:
+    """The arithmetic the partition kernel runs for this case's dtypes."""
+    qk = {"fp8_e4m3": f"E4M3 K -> {case.q_dtype} MFMA q.k, f16 MFMA p.v",
+          "int8": "INT8 K/V -> f16 (exact) MFMA q.k (q as f16) and p.v",
+          "f16": "f16 MFMA q.k and p.v",
+          "bf16": "bf16 MFMA q.k, bf16 MFMA p.v (p split into two bf16 terms)"}[case.kv_dtype]
+    return qk + ", f32 softmax and accumulate"
+
+
+def measured_traffic(workload: str, overridden: bool = False):
     """HBM traffic per partition launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and the workload as defined; else None."""
+    if overridden:
+        return None
     path = os.path.join(ROOT, "profiles", f"traffic_partition_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -88,7 +103,7 @@ def kv_append_timing(fd, torch, case, target, stream, reps=50):
     b.record(stream)
     torch.cuda.synchronize()
     rows = int((target.seq_len > 0).sum()) * case.hkv * 2
-    eb = {"fp8_e4m3": 1, "f16": 2, "bf16": 2}[case.kv_dtype]
+    eb = {"fp8_e4m3": 1, "int8": 1, "f16": 2, "bf16": 2}[case.kv_dtype]
     moved = rows * case.d * (2 + eb) + (rows * 4 if case.scale_mode == "token_head" else 0)
     us = a.elapsed_time(b) * 1e3 / reps
     return {"us_per_call": round(us, 2), "rows": rows, "bytes_moved": moved,
@@ -128,6 +143,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--no-read-probe", action="store_true")
+    ap.add_argument("--block-size", type=int, default=None, help="page size override (16, 32, 64)")
+    ap.add_argument("--seq-len", type=int, default=None, help="every sequence this many tokens")
+    ap.add_argument("--layout", choices=("contiguous", "ordered", "fragmented"), default=None,
+                    help="contiguous rows, or pages in table order / shuffled")
+    ap.add_argument("--batch", type=int, default=None)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -144,7 +164,19 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    case = workloads.make_case(args.workload, seed=args.seed, device=dev)
+    overrides, seq_lens = {}, None
+    if args.batch is not None:
+        overrides["batch"] = args.batch
+    if args.block_size is not None:
+        overrides["block_size"] = args.block_size
+    if args.layout is not None:
+        overrides["paged"] = args.layout != "contiguous"
+        overrides["shuffle"] = args.layout == "fragmented"
+    if args.seq_len is not None:
+        nb = args.batch if args.batch is not None else workloads.WORKLOADS[args.workload]["batch"]
+        seq_lens = [args.seq_len] * nb
+        overrides["max_seq_len"] = args.seq_len
+    case = workloads.make_case(args.workload, seed=args.seed, device=dev, seq_lens=seq_lens, **overrides)
     kv_bytes = case.kv_read_bytes()
     ncopy = args.copies or max(2, math.ceil(2 * MALL_BYTES / max(kv_bytes, 1)) + 1)
     copies = [case]
@@ -215,7 +247,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"int8": "f16", "f16": "f16"}.get(case.kv_dtype, case.q_dtype),
         "data": "synthetic",
         "config": {
             "workload": args.workload, "batch": case.batch, "num_q_heads": case.hq,
@@ -224,7 +256,9 @@ def main():
             "tokens": int(sum(case.seq_lens)), "max_seq_len": case.max_seq_len,
             "kv_read_bytes": kv_bytes, "partitions": nparts,
             "kv_copies_rotated": ncopy, "seed": args.seed,
-            "compute": "E4M3/bf16 K -> bf16 MFMA q.k, f16 MFMA p.v, f32 softmax and accumulate",
+            "overrides": {"block_size": args.block_size, "seq_len": args.seq_len, "layout": args.layout,
+                          "batch": args.batch} if (overrides or seq_lens) else None,
+            "compute": compute_note(case),
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -234,7 +268,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k_achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload, bool(overrides or seq_lens)),
             "kernel_us_mean": round(kmean_ms * 1e3, 2),
             "kernel_us_p10_p90": [round(float(np.percentile(kdur_ms, 10)) * 1e3, 2),
                                   round(float(np.percentile(kdur_ms, 90)) * 1e3, 2)],

@@ -14,10 +14,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_LAUNCH = 0, 1, 2, 3, 4
-FD_F32, FD_F16, FD_BF16, FD_FP8_E4M3 = 0, 1, 2, 3
+FD_F32, FD_F16, FD_BF16, FD_FP8_E4M3, FD_INT8 = 0, 1, 2, 3, 4
 FD_SCALE_NONE, FD_SCALE_PER_TENSOR, FD_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 
-DTYPE_CODES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8_e4m3": FD_FP8_E4M3}
+DTYPE_CODES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8_e4m3": FD_FP8_E4M3, "int8": FD_INT8}
 SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head": FD_SCALE_PER_TOKEN_HEAD}
 EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
            "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe",
@@ -202,7 +202,7 @@ def kv_append(k_new, v_new, k_cache, v_cache, pos, *, kv_dtype: str, block_table
               block_size: int = 0, scale_mode: str = "none", k_scale=None, v_scale=None, stream=None):
     """Write the current token's K/V rows ``k_new``/``v_new`` ([batch][num_kv_heads][head_dim],
     f32/f16/bf16 GPU tensors) into the cache at token ``pos[b]`` of each sequence (in place;
-    per-token E4M3 scales are written too).  Layouts and codes as ``include/fd.h``."""
+    per-token E4M3 / INT8 scales are written too).  Layouts and codes as ``include/fd.h``."""
     import torch
 
     _require_cuda(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, pos=pos,

@@ -133,11 +133,12 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len)) return FD_ERR_INVALID_ARG;
     if (num_partitions < 0) return FD_ERR_INVALID_ARG;
     if ((block_table == nullptr) == (kv_start == nullptr)) return FD_ERR_INVALID_ARG;
-    if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
+    if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3 && kv_dtype != FD_INT8)
+        return FD_ERR_INVALID_ARG;
     if (q_dtype != FD_F16 && q_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
     if (out_dtype != FD_F32 && out_dtype != FD_F16 && out_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
     if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return FD_ERR_INVALID_ARG;
-    if (kv_dtype == FD_FP8_E4M3) {
+    if (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) {
         if (scale_mode != FD_SCALE_PER_TENSOR && scale_mode != FD_SCALE_PER_TOKEN_HEAD) return FD_ERR_INVALID_ARG;
         if (!k_scale || !v_scale) return FD_ERR_INVALID_ARG;
     } else {
@@ -216,8 +217,9 @@ int fd_kv_append(const void *k_new, const void *v_new, int new_dtype, void *k_ca
     if (batch <= 0 || batch > 65535 || num_kv_heads <= 0 || num_kv_heads > 4096) return FD_ERR_INVALID_ARG;
     if ((block_table == nullptr) == (kv_start == nullptr)) return FD_ERR_INVALID_ARG;
     if (new_dtype != FD_F32 && new_dtype != FD_F16 && new_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
-    if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
-    if (kv_dtype == FD_FP8_E4M3) {
+    if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3 && kv_dtype != FD_INT8)
+        return FD_ERR_INVALID_ARG;
+    if (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) {
         if (scale_mode != FD_SCALE_PER_TENSOR && scale_mode != FD_SCALE_PER_TOKEN_HEAD) return FD_ERR_INVALID_ARG;
         if (!k_scale || !v_scale) return FD_ERR_INVALID_ARG;
     } else if (scale_mode != FD_SCALE_NONE) {

@@ -9,7 +9,9 @@
 // (E = D / 64), so loads and stores are coalesced.  E4M3 rows: the wave's max |x| (a butterfly)
 // gives scale = amax / 448 (1 for an all-zero row), q = x / scale in IEEE fp32 (correctly
 // rounded division), clamped to +-448, then the hardware convert rounds to the nearest E4M3
-// value (ties to even).  f16 / bf16 caches take the value rounded to nearest even.
+// value (ties to even).  INT8 rows: scale = amax / 127, the code is x / scale rounded to the
+// nearest integer (ties to even), clamped to +-127.  f16 / bf16 caches take the value rounded
+// to nearest even.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,6 +29,8 @@ __device__ __forceinline__ uint32_t e4m3_rne_x2(float q0, float q1) {
 
 // Clamp to the E4M3 range by comparisons (a NaN passes through unchanged).
 __device__ __forceinline__ float clamp448(float q) { return q > 448.0f ? 448.0f : (q < -448.0f ? -448.0f : q); }
+// Clamp to the symmetric INT8 range [-127, 127].
+__device__ __forceinline__ float clamp127(float q) { return q > 127.0f ? 127.0f : (q < -127.0f ? -127.0f : q); }
 
 template <int NT>
 __device__ __forceinline__ float load_new(const void *src, size_t i) {
@@ -55,7 +59,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
         float x[E];
 #pragma unroll
         for (int i = 0; i < E; i++) x[i] = load_new<NT>(src, src0 + i);
-        if constexpr (KVT == KV_FP8) {
+        if constexpr (KVT == KV_FP8 || KVT == KV_I8) {
+            constexpr float qmax = (KVT == KV_FP8) ? 448.0f : 127.0f;
             float *sc = which ? a.v_scale : a.k_scale;
             float scale;
             if constexpr (SCALE == SC_TOKEN_HEAD) {
@@ -64,17 +69,21 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
                 for (int i = 1; i < E; i++) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
                 for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, off));
-                scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+                scale = amax > 0.0f ? amax / qmax : 1.0f;
                 if (lane == 0) sc[row * a.hkv + g] = scale;
             } else {
                 scale = sc[0];
             }
             uint8_t *dst = (uint8_t *)cache + dst0;
-            if constexpr (E == 2) {
-                *(uint16_t *)dst = (uint16_t)e4m3_rne_x2(clamp448(x[0] / scale), clamp448(x[1] / scale));
+            uint32_t code;
+            if constexpr (KVT == KV_FP8) {
+                code = e4m3_rne_x2(clamp448(x[0] / scale), E == 2 ? clamp448(x[1] / scale) : 0.0f);
             } else {
-                dst[0] = (uint8_t)e4m3_rne_x2(clamp448(x[0] / scale), 0.0f);
+                code = (uint32_t)(uint8_t)(int8_t)(int)clamp127(__builtin_rintf(x[0] / scale));
+                if constexpr (E == 2) code |= (uint32_t)(uint8_t)(int8_t)(int)clamp127(__builtin_rintf(x[1] / scale)) << 8;
             }
+            if constexpr (E == 2) *(uint16_t *)dst = (uint16_t)code;
+            else dst[0] = (uint8_t)code;
         } else {
             uint16_t h[E];
 #pragma unroll
@@ -110,6 +119,10 @@ template <int D, int NT>
 static hipError_t launch_a3(const AppendParams &a, int kv, int sc, hipStream_t stream) {
     if (kv == KV_F16) return launch_a4<D, NT, KV_F16, SC_NONE>(a, stream);
     if (kv == KV_BF16) return launch_a4<D, NT, KV_BF16, SC_NONE>(a, stream);
+    if (kv == KV_I8) {
+        if (sc == SC_TENSOR) return launch_a4<D, NT, KV_I8, SC_TENSOR>(a, stream);
+        return launch_a4<D, NT, KV_I8, SC_TOKEN_HEAD>(a, stream);
+    }
     if (sc == SC_TENSOR) return launch_a4<D, NT, KV_FP8, SC_TENSOR>(a, stream);
     return launch_a4<D, NT, KV_FP8, SC_TOKEN_HEAD>(a, stream);
 }

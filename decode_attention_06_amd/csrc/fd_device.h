@@ -17,7 +17,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
-enum { KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3 };
+enum { KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3, KV_I8 = 4 };
 enum { SC_NONE = 0, SC_TENSOR = 1, SC_TOKEN_HEAD = 2 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -58,6 +58,21 @@ __device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t w) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
     else
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// Two int8 codes -> two f16 values (exact), for codes placed in bytes 0 and 2 of x with bytes 1
+// and 3 zero: each 16-bit half 0x00bb becomes 0x64 | (bb ^ 0x80), i.e. the f16 value 1024 +
+// (code + 128), and subtracting 1152 leaves the code.
+__device__ __forceinline__ uint32_t i8x2_to_f16x2(uint32_t x) {
+    const f16x2_t biased = __builtin_bit_cast(f16x2_t, x ^ 0x64806480u);
+    return __builtin_bit_cast(uint32_t, biased - f16x2_t{(_Float16)1152.0f, (_Float16)1152.0f});
+}
+
+// bf16 pair -> f16 pair (exact for |x| in the f16 normal range; used for q against INT8 KV).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    const float lo = __builtin_bit_cast(float, w << 16), hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {

@@ -66,7 +66,7 @@ __device__ __forceinline__ int pv_token(int g, int j) { return (j < 4) ? 4 * g +
 
 template <int D, int KVT>
 struct Geometry {
-    static constexpr int EB = (KVT == KV_FP8) ? 1 : 2;  // bytes per KV element
+    static constexpr int EB = (KVT == KV_FP8 || KVT == KV_I8) ? 1 : 2;  // bytes per KV element
     static constexpr int E = 16 / EB;                   // elements per 16-byte load
     static constexpr int KSTEPS = D / 32;               // MFMA k-steps of q.k^T
     static constexpr int KLOADS = (D / 4) / E;          // 16-byte K loads per lane per 16-token half
@@ -183,6 +183,10 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves
 void partition_kernel(Params p) {
     using G = Geometry<D, KVT>;
     constexpr int EB = G::EB, E = G::E, KSTEPS = G::KSTEPS, KLOADS = G::KLOADS, DT = G::DT, VDW = G::VDW;
+    // q.k^T operand type: q's own, except against INT8 KV (codes become f16 exactly; a bf16 q is
+    // converted to f16 once per segment)
+    constexpr int QM = (KVT == KV_I8) ? KV_F16 : QT;
+    constexpr bool QCVT = (KVT == KV_I8 && QT == KV_BF16);
     __shared__ float sh_scale_all[kMaxWavesPerGroup][64];
     __shared__ int sh_prefix[kLdsBatch + 1];  // tiles of the sequences before b (b <= batch)
 
@@ -337,9 +341,18 @@ void partition_kernel(Params p) {
         m_run = -INFINITY;
         l_run = 0.0f;
     };
-    auto next_segment = [&]() {
+    auto convert_q = [&](u32x4_t (&dst)[KSTEPS], const u32x4_t (&src)[KSTEPS]) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; kk++) qop[kk] = qnext[kk];
+        for (int kk = 0; kk < KSTEPS; kk++) {
+            if constexpr (QCVT)
+                dst[kk] = u32x4_t{bf16x2_to_f16x2(src[kk][0]), bf16x2_to_f16x2(src[kk][1]),
+                                  bf16x2_to_f16x2(src[kk][2]), bf16x2_to_f16x2(src[kk][3])};
+            else
+                dst[kk] = src[kk];
+        }
+    };
+    auto next_segment = [&]() {
+        convert_q(qop, qnext);
         reset_state();
     };
 
@@ -388,10 +401,18 @@ void partition_kernel(Params p) {
                     const uint32_t w0 = wv[2 * (kk % 2)], w1 = wv[2 * (kk % 2) + 1];
                     a = u32x4_t{cvt_fp8x2<QT, false>(w0), cvt_fp8x2<QT, true>(w0),
                                 cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
+                } else if constexpr (KVT == KV_I8) {
+                    // bytes 0,1 / 2,3 of each dword -> 0x00bb 16-bit halves (zero bytes: selector 0x0C)
+                    const u32x4_t wv = r.k[half][kk / 2];
+                    const uint32_t w0 = wv[2 * (kk % 2)], w1 = wv[2 * (kk % 2) + 1];
+                    a = u32x4_t{i8x2_to_f16x2(__builtin_amdgcn_perm(0u, w0, 0x0C010C00u)),
+                                i8x2_to_f16x2(__builtin_amdgcn_perm(0u, w0, 0x0C030C02u)),
+                                i8x2_to_f16x2(__builtin_amdgcn_perm(0u, w1, 0x0C010C00u)),
+                                i8x2_to_f16x2(__builtin_amdgcn_perm(0u, w1, 0x0C030C02u))};
                 } else {
                     a = r.k[half][kk];
                 }
-                sacc[half] = mfma_qk<QT>(a, qop[kk], sacc[half]);
+                sacc[half] = mfma_qk<QM>(a, qop[kk], sacc[half]);
             }
         }
 
@@ -462,7 +483,21 @@ void partition_kernel(Params p) {
                 pp[u] = pack_f16(p0, p1);
             }
             const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
-            if constexpr (KVT == KV_FP8) {
+            if constexpr (KVT == KV_I8) {
+#pragma unroll
+                for (int wd = 0; wd < VDW; wd++) {
+                    uint32_t a[4][4];
+#pragma unroll
+                    for (int u = 0; u < 4; u++)
+#pragma unroll
+                        for (int k = 0; k < 4; k++)  // byte k of rows 2u, 2u+1 -> f16 pair (token 2u, 2u+1)
+                            a[k][u] = i8x2_to_f16x2(__builtin_amdgcn_perm(r.v[2 * u + 1][wd], r.v[2 * u][wd],
+                                                                          0x0C000C00u | ((4u + k) << 16) | (uint32_t)k));
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        acc[4 * wd + k] = mfma_f16(u32x4_t{a[k][0], a[k][1], a[k][2], a[k][3]}, pop, acc[4 * wd + k]);
+                }
+            } else if constexpr (KVT == KV_FP8) {
 #pragma unroll
                 for (int wd = 0; wd < VDW; wd++) {
                     uint32_t a[4][4];
@@ -544,7 +579,8 @@ void partition_kernel(Params p) {
     Desc da, db;
     describe(da);
     issue(ra, da);
-    load_q(qop, da);
+    load_q(qnext, da);
+    convert_q(qop, qnext);
     reset_state();
     for (;;) {
         bool more = advance(db);
@@ -755,6 +791,14 @@ template <int D>
 static hipError_t launch_d(const Params &p, int kv, int qt, int sc, hipStream_t stream) {
     if (kv == KV_F16) return launch_p<D, KV_F16, KV_F16, SC_NONE>(p, stream);
     if (kv == KV_BF16) return launch_p<D, KV_BF16, KV_BF16, SC_NONE>(p, stream);
+    if (kv == KV_I8) {
+        if (qt == KV_BF16) {
+            if (sc == SC_TENSOR) return launch_p<D, KV_I8, KV_BF16, SC_TENSOR>(p, stream);
+            return launch_p<D, KV_I8, KV_BF16, SC_TOKEN_HEAD>(p, stream);
+        }
+        if (sc == SC_TENSOR) return launch_p<D, KV_I8, KV_F16, SC_TENSOR>(p, stream);
+        return launch_p<D, KV_I8, KV_F16, SC_TOKEN_HEAD>(p, stream);
+    }
     if (qt == KV_BF16) {
         if (sc == SC_TENSOR) return launch_p<D, KV_FP8, KV_BF16, SC_TENSOR>(p, stream);
         return launch_p<D, KV_FP8, KV_BF16, SC_TOKEN_HEAD>(p, stream);

@@ -53,7 +53,8 @@ typedef enum {
     FD_F32 = 0,      /* output only                                                       */
     FD_F16 = 1,      /* IEEE binary16                                                     */
     FD_BF16 = 2,     /* bfloat16                                                          */
-    FD_FP8_E4M3 = 3  /* OCP E4M3FN bytes (KV only): bias 7, no infinities, 0x7F/0xFF = NaN */
+    FD_FP8_E4M3 = 3, /* OCP E4M3FN bytes (KV only): bias 7, no infinities, 0x7F/0xFF = NaN */
+    FD_INT8 = 4      /* two's-complement int8 codes (KV only), value = code * scale        */
 } fd_dtype;
 
 typedef enum {
@@ -88,7 +89,8 @@ typedef enum {
  *                Paged mode needs max_seq_len <= max_blocks_per_seq * block_size.
  *   block_size   16, 32 or 64 in paged mode (16: the 15.9 page size; a 32-token kernel tile then
  *                spans two blocks); ignored (pass 0) in contiguous mode.
- *   scale_mode   FD_SCALE_NONE for f16/bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 KV.
+ *   scale_mode   FD_SCALE_NONE for f16/bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 / INT8
+ *                KV (15.11: quantised KV, per-token k/v scales).
  *   k_scale,     fp32 dequantisation scales (value = decode(byte) * scale), NULL when none.
  *   v_scale
  *   softmax_scale  multiplies q . k (natural-exp softmax); usually 1/sqrt(head_dim).
@@ -160,12 +162,12 @@ int fd_fp8_e4m3_decode(const uint8_t *in, float *out, int n, hipStream_t stream)
  *                before this step); a negative value leaves that sequence untouched.  The row is
  *                block_table[b][pos / block_size] * block_size + pos % block_size (paged) or
  *                kv_start[b] + pos (contiguous).
- *   k_scale, v_scale  E4M3 only.  FD_SCALE_PER_TOKEN_HEAD: written, per (row, kv head), as
- *                amax |row| / 448 in fp32 (1 for an all-zero row), and each value is stored as
- *                the E4M3 code nearest to x / scale (ties to even).  FD_SCALE_PER_TENSOR: the
- *                given k_scale[0] / v_scale[0] are used (not written); x / scale saturates at
- *                +-448.  f16 / bf16 caches (scale_mode FD_SCALE_NONE) store x rounded to
- *                nearest even.
+ *   k_scale, v_scale  E4M3 / INT8 only.  FD_SCALE_PER_TOKEN_HEAD: written, per (row, kv head),
+ *                as amax |row| / QMAX in fp32 (1 for an all-zero row; QMAX = 448 for E4M3, 127
+ *                for INT8), and each value is stored as the code nearest to x / scale (fp32
+ *                quotient, ties to even).  FD_SCALE_PER_TENSOR: the given k_scale[0] /
+ *                v_scale[0] are used (not written); x / scale saturates at +-QMAX.  f16 / bf16
+ *                caches (scale_mode FD_SCALE_NONE) store x rounded to nearest even.
  * Device-side contract (not checked): the table entry of block pos / block_size is a valid block
  * id and pos < max_blocks_per_seq * block_size (paged), the row exists (contiguous); inputs are
  * finite.  Host-checked errors as for fd_decode_attention: FD_ERR_INVALID_ARG (null pointers,

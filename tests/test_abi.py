@@ -99,7 +99,11 @@ BAD = [
     (dict(block_table=None), fd.FD_ERR_INVALID_ARG),         # neither
     (dict(kv_dtype=7), fd.FD_ERR_INVALID_ARG),
     (dict(q_dtype=fd.FD_FP8_E4M3), fd.FD_ERR_INVALID_ARG),
+    (dict(q_dtype=fd.FD_INT8), fd.FD_ERR_INVALID_ARG),
     (dict(out_dtype=5), fd.FD_ERR_INVALID_ARG),
+    (dict(out_dtype=fd.FD_INT8), fd.FD_ERR_INVALID_ARG),
+    (dict(kv_dtype=fd.FD_INT8, scale_mode=fd.FD_SCALE_NONE), fd.FD_ERR_INVALID_ARG),  # INT8 needs scales
+    (dict(kv_dtype=fd.FD_INT8, v_scale=None), fd.FD_ERR_INVALID_ARG),
     (dict(scale_mode=fd.FD_SCALE_NONE), fd.FD_ERR_INVALID_ARG),  # FP8 needs scales
     (dict(k_scale=None), fd.FD_ERR_INVALID_ARG),
     (dict(kv_dtype=fd.FD_BF16), fd.FD_ERR_INVALID_ARG),          # bf16 KV with a scale mode
@@ -127,6 +131,14 @@ def test_bad_arguments_rejected_before_launch(change, expect):
 def test_block_size_16_accepted_up_to_the_launch():
     # without a GPU the launch itself fails: the host checks passed
     assert fd.decode_attention_raw(**good_args(block_size=16, max_blocks_per_seq=128)) == fd.FD_ERR_LAUNCH
+
+
+@pytest.mark.parametrize("scale", [1, 2])
+@pytest.mark.parametrize("q_dtype", [1, 2])
+def test_int8_kv_accepted_up_to_the_launch(scale, q_dtype):
+    args = good_args(kv_dtype=fd.FD_INT8, scale_mode=scale, q_dtype=q_dtype)
+    assert fd.decode_attention_raw(**args) == fd.FD_ERR_LAUNCH
+    assert fd.kv_append_raw(**good_append(kv_dtype=fd.FD_INT8, scale_mode=scale)) == fd.FD_ERR_LAUNCH
 
 
 def test_read_probe_rejects_bad_arguments():
@@ -168,6 +180,8 @@ BAD_APPEND = [
     (dict(scale_mode=fd.FD_SCALE_NONE), fd.FD_ERR_INVALID_ARG),  # E4M3 needs a scale mode
     (dict(v_scale=None), fd.FD_ERR_INVALID_ARG),
     (dict(kv_dtype=fd.FD_F16), fd.FD_ERR_INVALID_ARG),         # f16 cache with a scale mode
+    (dict(kv_dtype=fd.FD_INT8, scale_mode=fd.FD_SCALE_NONE), fd.FD_ERR_INVALID_ARG),
+    (dict(new_dtype=fd.FD_INT8), fd.FD_ERR_INVALID_ARG),
     (dict(head_dim=96), fd.FD_ERR_UNSUPPORTED),
     (dict(block_size=8), fd.FD_ERR_UNSUPPORTED),
     (dict(block_size=128), fd.FD_ERR_UNSUPPORTED),

@@ -1,6 +1,6 @@
 """GPU parity of the KV-cache append (fd_kv_append) against the oracle, through the C ABI.
 
-The bar is bit-exact: the stored E4M3 codes, f16/bf16 values and per-token scales are integer /
+The bar is bit-exact: the stored E4M3 / INT8 codes, f16/bf16 values and per-token scales are integer /
 byte results decided in fp32, the same precision on both sides.  Every byte of the caches and
 every scale is compared (rows not appended must be left untouched).  An end-to-end case appends
 a token to every sequence of a decode batch and runs the attention over the grown sequences.
@@ -52,6 +52,8 @@ def _append_case(seed, *, batch, hkv, d, kv, scale, new, paged, bs=64, nblocks=N
     rows_per_seq = 3 * max(bs, 32)
     if kv == "fp8_e4m3":
         mk = lambda shape: torch.randint(0, 0x7E, shape, generator=g, dtype=torch.uint8)  # noqa: E731
+    elif kv == "int8":
+        mk = lambda shape: torch.randint(-127, 128, shape, generator=g, dtype=torch.int8)  # noqa: E731
     else:
         dt = {"f16": torch.float16, "bf16": torch.bfloat16}[kv]
         mk = lambda shape: torch.randn(shape, generator=g).to(dt)  # noqa: E731
@@ -93,6 +95,10 @@ APPEND_CASES = [
     ("bf16_f32in_contig", dict(batch=4, hkv=2, d=128, kv="bf16", scale="none", new="f32", paged=False)),
     ("bf16_bf16in_d64", dict(batch=4, hkv=3, d=64, kv="bf16", scale="none", new="bf16", paged=True, bs=32)),
     ("fp8_tok_bf16in_bs16", dict(batch=8, hkv=2, d=128, kv="fp8_e4m3", scale="token_head", new="bf16", paged=True, bs=16)),
+    ("i8_tok_bf16in_bs64", dict(batch=8, hkv=2, d=128, kv="int8", scale="token_head", new="bf16", paged=True)),
+    ("i8_tok_f32in_d64_bs16", dict(batch=8, hkv=3, d=64, kv="int8", scale="token_head", new="f32", paged=True, bs=16)),
+    ("i8_tensor_f16in_contig", dict(batch=5, hkv=2, d=128, kv="int8", scale="tensor", new="f16", paged=False)),
+    ("i8_tensor_f32in_d64_bs32", dict(batch=4, hkv=1, d=64, kv="int8", scale="tensor", new="f32", paged=True, bs=32)),
 ]
 
 
@@ -118,17 +124,21 @@ def test_kv_append_bitwise_equals_oracle(name, kw):
     print(f"[{name}] PASS bitwise", flush=True)
 
 
-@pytest.mark.parametrize("wname", ["fp8_32k_small", "wide_mqa"])
+@pytest.mark.parametrize("wname", ["fp8_32k_small", "wide_mqa", "int8_small"])
 def test_append_then_attend(wname):
     # append one token to each sequence, then attend over the grown sequences (both paths)
     if wname == "fp8_32k_small":
         case = workloads.custom_case(seed=31, device="cpu", batch=4, hq=64, hkv=8, d=128,
                                      seq_lens=[127, 64, 1000, 5], kv="fp8_e4m3", q="bf16",
                                      scale="token_head", block_size=64, max_seq_len=1100)
-    else:
+    elif wname == "wide_mqa":
         case = workloads.custom_case(seed=32, device="cpu", batch=3, hq=128, hkv=1, d=128,
                                      seq_lens=[63, 700, 32], kv="fp8_e4m3", q="bf16",
                                      scale="tensor", block_size=64, max_seq_len=800)
+    else:
+        case = workloads.custom_case(seed=33, device="cpu", batch=4, hq=32, hkv=4, d=128,
+                                     seq_lens=[15, 16, 900, 3], kv="int8", q="bf16",
+                                     scale="token_head", block_size=16, max_seq_len=1000)
     # every sequence gets a block for its next token (the spare blocks of the generator)
     bt = case.block_table.clone()
     nb = case.k_cache.shape[0]

@@ -2,7 +2,7 @@
 
 Bar (per KV type): max |gpu - oracle| over all output elements and relative L2 error
 ||gpu - oracle|| / ||oracle|| must stay within 2e-3 / 1e-3 for f16/bf16 KV and 5e-3 / 3e-3 for
-E4M3 KV (the oracle dequantises the same bytes with the same scales).  Results are printed as
+E4M3 and INT8 KV (the oracle dequantises the same bytes with the same scales).  Results are printed as
 ``[case] PASS max_abs=... rel_l2=...`` lines.
 """
 import math
@@ -17,7 +17,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3), "fp8_e4m3": (5e-3, 3e-3)}
+TOL = {"f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3), "fp8_e4m3": (5e-3, 3e-3), "int8": (5e-3, 3e-3)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -127,6 +127,20 @@ SMALL = [
                                 q="bf16", scale="token_head", block_size=16)),
     ("bs16_wide_g64_tensor", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[65, 300, 1], kv="fp8_e4m3",
                                   q="bf16", scale="tensor", block_size=16)),
+    # INT8 KV: both scale modes and q types, both head dims, every page size and contiguous, a
+    # group of 128 (eight 16-head blocks per kv head)
+    ("gqa8_i8_tok", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[65, 1500, 31], kv="int8",
+                         q="bf16", scale="token_head", block_size=64)),
+    ("g8_i8_tok_f16q_bs32", dict(batch=2, hq=8, hkv=1, d=128, seq_lens=[300, 64], kv="int8",
+                                 q="f16", scale="token_head", block_size=32)),
+    ("mqa128_i8_tensor", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[2049, 333], kv="int8",
+                              q="bf16", scale="tensor", block_size=64)),
+    ("g4_i8_tok_d64_contig", dict(batch=3, hq=8, hkv=2, d=64, seq_lens=[40, 1, 129], kv="int8",
+                                  q="bf16", scale="token_head", paged=False, block_size=0)),
+    ("g32_i8_tensor_f16q_d64", dict(batch=2, hq=32, hkv=1, d=64, seq_lens=[513, 7], kv="int8",
+                                    q="f16", scale="tensor", block_size=32)),
+    ("bs16_i8_tok_g8", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[700, 17, 48], kv="int8",
+                            q="bf16", scale="token_head", block_size=16)),
 ]
 
 
@@ -145,6 +159,17 @@ def test_length_edges(n):
                                  max_seq_len=max(lens + [1]))
     for parts in (0, 3):
         check_case(f"len{n}/p{parts}", case, num_partitions=parts)
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 63, 64, 65, 4095])
+def test_int8_length_edges(n, bs):
+    lens = [n, 5, n]
+    case = workloads.custom_case(seed=300 + n, device="cuda", batch=3, hq=16, hkv=2, d=128, seq_lens=lens,
+                                 kv="int8", q="bf16", scale="token_head", block_size=bs,
+                                 max_seq_len=max(lens + [1]))
+    for parts in (0, 3):
+        check_case(f"i8_len{n}_bs{bs}/p{parts}", case, num_partitions=parts)
 
 
 @pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 191, 192, 193, 4095])
@@ -268,6 +293,10 @@ def test_workload_gqa_bf16_full():
 
 def test_workload_fp8_32k_full():
     check_case("fp8_32k", workloads.make_case("fp8_32k", device="cuda"))
+
+
+def test_workload_int8_32k_full():
+    check_case("int8_32k", workloads.make_case("int8_32k", device="cuda"))
 
 
 def test_workload_mqa_fp8_128k_sampled():
