@@ -36,7 +36,7 @@ class _Problem(ctypes.Structure):
         ("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
         ("d", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
-        ("softmax_scale", ctypes.c_double),
+        ("softmax_scale", ctypes.c_double), ("nq", ctypes.c_int32),
     ]
 
 
@@ -123,7 +123,7 @@ class Problem:
 
     def __init__(self, *, q, k_cache, v_cache, seq_len, batch, hq, hkv, d, q_dtype, kv_dtype,
                  scale_mode="none", k_scale=None, v_scale=None, block_table=None, kv_start=None,
-                 block_size=0, softmax_scale):
+                 block_size=0, softmax_scale, nq=1):
         self._keep = dict(q=_host(q), k=_host(k_cache), v=_host(v_cache),
                           bt=_host(block_table, np.int32), ks=_host(kv_start, np.int32),
                           sl=_host(seq_len, np.int32), ksc=_host(k_scale, np.float32),
@@ -133,12 +133,13 @@ class Problem:
         self.d = d
         self.batch = batch
         self.hq = hq
+        self.nq = int(nq)
         self.seq_lens = [int(x) for x in k["sl"]]
         self.s = _Problem(ptr(k["q"]), ptr(k["k"]), ptr(k["v"]), ptr(k["bt"]), ptr(k["ks"]),
                           ptr(k["sl"]), ptr(k["ksc"]), ptr(k["vsc"]), batch, hq, hkv, d,
                           block_size, 0 if k["bt"] is None else k["bt"].shape[1],
                           _DTYPE[q_dtype], _DTYPE[kv_dtype], _SCALE[scale_mode],
-                          float(softmax_scale))
+                          float(softmax_scale), int(nq))
 
     @classmethod
     def from_case(cls, case):
@@ -147,15 +148,18 @@ class Problem:
                    batch=case.batch, hq=case.hq, hkv=case.hkv, d=case.d, q_dtype=case.q_dtype,
                    kv_dtype=case.kv_dtype, scale_mode=case.scale_mode, k_scale=case.k_scale,
                    v_scale=case.v_scale, block_table=case.block_table, kv_start=case.kv_start,
-                   block_size=case.block_size, softmax_scale=case.softmax_scale)
+                   block_size=case.block_size, softmax_scale=case.softmax_scale,
+                   nq=getattr(case, "nq", 1))
 
 
 def decode_attention(prob: Problem, seqs=None, nthreads: int | None = None):
-    """(out [B][Hq][D], lse [B][Hq]) in float64.  ``seqs``: optional iterable of sequence ids to
-    compute (others are NaN)."""
+    """(out [B][Hq][D], lse [B][Hq]) in float64 -- or [B][nq][Hq][D], [B][nq][Hq] for a window of
+    nq > 1 query tokens per sequence.  ``seqs``: optional iterable of sequence ids to compute
+    (others are NaN)."""
     lib = _load()
-    out = np.full((prob.batch, prob.hq, prob.d), np.nan, dtype=np.float64)
-    lse = np.full((prob.batch, prob.hq), np.nan, dtype=np.float64)
+    rows = (prob.batch, prob.nq, prob.hq) if prob.nq > 1 else (prob.batch, prob.hq)
+    out = np.full(rows + (prob.d,), np.nan, dtype=np.float64)
+    lse = np.full(rows, np.nan, dtype=np.float64)
     mask = None
     if seqs is not None:
         mask = np.zeros(prob.batch, dtype=np.uint8)

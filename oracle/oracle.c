@@ -26,6 +26,11 @@
  *     ([CH15] 15.11) is the same with two's-complement int8 codes.
  *   - The empty sequence (seq_len 0) gives out = 0 and lse = -inf.
  *   - lse is the natural log of sum_t exp(s_t).
+ *   - A window of nq query tokens per sequence ([FD] 2.2 tiles several query rows per block;
+ *     [CH15] 15.21 verifies a window of draft tokens in one pass): the window's tokens are the
+ *     last nq tokens already in the cache, so query row m (0-based) sits at position
+ *     seq_len - nq + m and attends to tokens [0, seq_len - nq + m]; a row whose range is empty
+ *     (seq_len < nq - m) gives out = 0 and lse = -inf.  nq = 1 is the ordinary decode step.
  */
 #include <math.h>
 #include <pthread.h>
@@ -51,7 +56,10 @@ typedef struct {
     int32_t block_size, max_blocks;
     int32_t q_dtype, kv_dtype, scale_mode;
     double softmax_scale;
+    int32_t nq;                /* query tokens per sequence (0 or 1: one); q is [batch][nq][hq][d] */
 } orc_problem;
+
+static int nq_of(const orc_problem *p) { return p->nq > 1 ? p->nq : 1; }
 
 /* --- element decoders (exact conversions to double, written from the format definitions) --- */
 
@@ -119,17 +127,19 @@ static double row_scale(const float *s, int mode, int64_t row, int hkv, int g) {
  * with s_t = softmax_scale * sum_d q[d] * K[t][d]  ([FA] 2.2).  Subtracting m is exact in real
  * arithmetic (it cancels in acc / l); it only keeps exp() finite.  An empty range gives
  * m = -inf, l = 0, acc = 0.  Returns 0, or -1 on a bad argument. */
-int orc_attend_range(const orc_problem *p, int b, int h, int t0, int t1,
-                     double *m_out, double *l_out, double *acc) {
-    const int d = p->d, hkv = p->hkv, group = p->hq / p->hkv;
+int orc_attend_range_q(const orc_problem *p, int b, int mq, int h, int t0, int t1,
+                       double *m_out, double *l_out, double *acc) {
+    const int d = p->d, hkv = p->hkv, group = p->hq / p->hkv, nq = nq_of(p);
     const int g = h / group;                               /* [CH15] 15.12 */
     double *s, *qv, m = -INFINITY, l = 0.0;
-    if (b < 0 || b >= p->batch || h < 0 || h >= p->hq || t0 < 0 || t1 < t0) return -1;
+    if (b < 0 || b >= p->batch || mq < 0 || mq >= nq || h < 0 || h >= p->hq || t0 < 0 || t1 < t0)
+        return -1;
     for (int i = 0; i < d; i++) acc[i] = 0.0;
     if (t1 == t0) { *m_out = -INFINITY; *l_out = 0.0; return 0; }
     s = (double *)malloc(sizeof(double) * (size_t)(t1 - t0));
     qv = (double *)malloc(sizeof(double) * (size_t)d);
-    for (int i = 0; i < d; i++) qv[i] = load_elem(p->q, ((size_t)b * p->hq + h) * d + i, p->q_dtype);
+    for (int i = 0; i < d; i++)
+        qv[i] = load_elem(p->q, (((size_t)b * nq + mq) * p->hq + h) * d + i, p->q_dtype);
     /* scores */
     for (int t = t0; t < t1; t++) {
         int64_t row = token_row(p, b, t);
@@ -153,6 +163,12 @@ int orc_attend_range(const orc_problem *p, int b, int h, int t0, int t1,
     *m_out = m;
     *l_out = l;
     return 0;
+}
+
+/* The same for query row 0 (the only row of an ordinary decode step). */
+int orc_attend_range(const orc_problem *p, int b, int h, int t0, int t1,
+                     double *m_out, double *l_out, double *acc) {
+    return orc_attend_range_q(p, b, 0, h, t0, t1, m_out, l_out, acc);
 }
 
 /* Merge of partial states over disjoint token ranges of one (sequence, head) into the final
@@ -187,16 +203,19 @@ typedef struct {
     int tid, nthreads, status;
 } orc_job;
 
-/* One (b, h): out = acc / l over tokens [0, seq_len[b]), lse = m + ln l  ([FA] 2.2; [FD] 3.1). */
-static int attend_one(const orc_problem *p, int b, int h, double *out, double *lse) {
+/* One (b, query row mq, h): out = acc / l over tokens [0, seq_len[b] - nq + mq + 1),
+ * lse = m + ln l  ([FA] 2.2; [FD] 3.1; the window reading in the header). */
+static int attend_one(const orc_problem *p, int b, int mq, int h, double *out, double *lse) {
     double m, l;
-    int n = p->seq_len[b];
+    const int len = p->seq_len[b];
+    const int n = len - nq_of(p) + mq + 1;
+    if (len < 0) return -1;
     if (n <= 0) {
         for (int i = 0; i < p->d; i++) out[i] = 0.0;
         *lse = -INFINITY;
-        return n < 0 ? -1 : 0;
+        return 0;
     }
-    if (orc_attend_range(p, b, h, 0, n, &m, &l, out)) return -1;
+    if (orc_attend_range_q(p, b, mq, h, 0, n, &m, &l, out)) return -1;
     for (int i = 0; i < p->d; i++) out[i] /= l;
     *lse = m + log(l);
     return 0;
@@ -205,16 +224,17 @@ static int attend_one(const orc_problem *p, int b, int h, double *out, double *l
 static void *worker(void *arg) {
     orc_job *job = (orc_job *)arg;
     const orc_problem *p = job->p;
-    long items = (long)p->batch * p->hq;
+    const long rows = (long)nq_of(p) * p->hq;  /* (query row, head) pairs per sequence */
+    long items = (long)p->batch * rows;
     for (long it = job->tid; it < items; it += job->nthreads) {
-        int b = (int)(it / p->hq), h = (int)(it % p->hq);
+        int b = (int)(it / rows), mq = (int)(it % rows / p->hq), h = (int)(it % p->hq);
         if (job->seq_mask && !job->seq_mask[b]) continue;
-        if (attend_one(p, b, h, job->out + (size_t)it * p->d, job->lse + it)) job->status = -1;
+        if (attend_one(p, b, mq, h, job->out + (size_t)it * p->d, job->lse + it)) job->status = -1;
     }
     return NULL;
 }
 
-/* out[batch][hq][d], lse[batch][hq] (both double).  seq_mask (optional) selects the sequences to
+/* out[batch][nq][hq][d], lse[batch][nq][hq] (both double).  seq_mask (optional) selects the sequences to
  * compute; the others are left untouched.  Work is spread over nthreads POSIX threads by
  * (sequence, head) pairs.  Returns 0, or -1 on a bad argument. */
 int orc_decode_attention(const orc_problem *p, const uint8_t *seq_mask, double *out, double *lse,

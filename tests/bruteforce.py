@@ -51,3 +51,22 @@ def attention(q, ks, vs, scale):
         outs.append(ob)
         lses.append(lb)
     return outs, lses
+
+
+def attention_window(q, ks, vs, scale):
+    """A window of M query tokens per sequence: q [B][M][Hq][D] float64; row m of sequence b sits
+    at position n_b - M + m and sees tokens [0, n_b - M + m] (none: out 0, lse -inf).  Returns
+    (out [B][M][Hq][D], lse [B][M][Hq]) as nested lists, from `attention` on each row's prefix."""
+    B, M = q.shape[0], q.shape[1]
+    outs, lses = [], []
+    for b in range(B):
+        n = ks[b].shape[0]
+        ob, lb = [], []
+        for m in range(M):
+            L = max(0, n - M + m + 1)
+            o, ls = attention(q[b:b + 1, m], [ks[b][:L]], [vs[b][:L]], scale)
+            ob.append(o[0])
+            lb.append(ls[0])
+        outs.append(ob)
+        lses.append(lb)
+    return outs, lses
