@@ -49,8 +49,8 @@ def kernel_hash() -> str:
 
 def partition_kernel_name(case) -> str:
     """Which partition kernel the library's plan runs for this case (E4M3 KV, head_dim 128 and
-    a multiple of 64 query heads per kv head take the wide-group kernel)."""
-    wide = case.kv_dtype == "fp8_e4m3" and case.d == 128 and case.group % 64 == 0
+    a multiple of 64 query heads per kv head take the wide-group kernel, with one query token)."""
+    wide = case.kv_dtype == "fp8_e4m3" and case.d == 128 and case.group % 64 == 0 and case.nq == 1
     return "wide_partition_kernel" if wide else "partition_kernel"
 
 
@@ -188,13 +188,15 @@ def main():
             c.k_scale = case.k_scale.clone()
             c.v_scale = case.v_scale.clone()
         copies.append(c)
-    out = torch.empty((case.batch, case.hq, case.d), dtype=torch.float32, device=dev)
-    lse = torch.empty((case.batch, case.hq), dtype=torch.float32, device=dev)
+    # [batch][hq][d] -- or [batch][nq][hq][d] for a window of nq query tokens: the kernels write
+    # one row per query row, so the buffers take q's shape
+    out = torch.empty(tuple(case.q.shape), dtype=torch.float32, device=dev)
+    lse = torch.empty(tuple(case.q.shape[:-1]), dtype=torch.float32, device=dev)
     wsb = fd.workspace_bytes(case.batch, case.hq, case.hkv, case.d, case.max_seq_len, case.block_size,
-                             case.kv_dtype, args.num_partitions)
+                             case.kv_dtype, args.num_partitions, num_query=case.nq)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     nparts = fd.plan_partitions(case.batch, case.hq, case.hkv, case.d, case.max_seq_len,
-                                case.block_size, case.kv_dtype, args.num_partitions)
+                                case.block_size, case.kv_dtype, args.num_partitions, num_query=case.nq)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):

@@ -21,7 +21,8 @@ DTYPE_CODES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8_e4m3": FD_FP8
 SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head": FD_SCALE_PER_TOKEN_HEAD}
 EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
            "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe",
-           "fd_kv_append", "fd_fp8_e4m3_encode")
+           "fd_kv_append", "fd_fp8_e4m3_encode", "fd_decode_attention_mq", "fd_workspace_bytes_mq",
+           "fd_plan_partitions_mq")
 
 _lock = threading.Lock()
 _lib = None
@@ -52,6 +53,12 @@ def lib() -> ctypes.CDLL:
         L.fd_decode_attention.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                           i32, i32, i32, vp, vp, ctypes.c_float, vp, i32, vp, vp, sz,
                                           i32, vp]
+        L.fd_decode_attention_mq.restype = i32
+        L.fd_decode_attention_mq.argtypes = [vp, i32] + L.fd_decode_attention.argtypes[1:]
+        L.fd_workspace_bytes_mq.restype = sz
+        L.fd_workspace_bytes_mq.argtypes = [i32] * 9
+        L.fd_plan_partitions_mq.restype = i32
+        L.fd_plan_partitions_mq.argtypes = [i32] * 9
         L.fd_workspace_bytes.restype = sz
         L.fd_workspace_bytes.argtypes = [i32] * 8
         L.fd_plan_partitions.restype = i32
@@ -84,19 +91,19 @@ def version() -> int:
 
 
 def workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0,
-                    kv_dtype="fp8_e4m3", num_partitions=0) -> int:
-    n = lib().fd_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                 block_size, DTYPE_CODES.get(kv_dtype, kv_dtype), num_partitions)
+                    kv_dtype="fp8_e4m3", num_partitions=0, num_query=1) -> int:
+    n = lib().fd_workspace_bytes_mq(batch, num_query, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                    block_size, DTYPE_CODES.get(kv_dtype, kv_dtype), num_partitions)
     if n == ctypes.c_size_t(-1).value:
         raise FdError(FD_ERR_INVALID_ARG, "fd_workspace_bytes")
     return n
 
 
 def plan_partitions(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0,
-                    kv_dtype="fp8_e4m3", num_partitions=0) -> int:
+                    kv_dtype="fp8_e4m3", num_partitions=0, num_query=1) -> int:
     """Number of partitions (partition-kernel waves) the library will use."""
-    n = lib().fd_plan_partitions(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
-                                 DTYPE_CODES.get(kv_dtype, kv_dtype), num_partitions)
+    n = lib().fd_plan_partitions_mq(batch, num_query, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                    block_size, DTYPE_CODES.get(kv_dtype, kv_dtype), num_partitions)
     if n < 0:
         raise FdError(FD_ERR_INVALID_ARG, "fd_plan_partitions")
     return n
@@ -112,6 +119,14 @@ def decode_attention_raw(q, k_cache, v_cache, block_table, max_blocks_per_seq, k
                                      block_size, kv_dtype, q_dtype, scale_mode, k_scale, v_scale,
                                      ctypes.c_float(softmax_scale), out, out_dtype, lse, workspace,
                                      workspace_bytes_, num_partitions, stream)
+
+
+def decode_attention_mq_raw(q, num_query, *args) -> int:
+    """Direct call of fd_decode_attention_mq: the arguments of ``decode_attention_raw`` with the
+    window size after q; returns the status."""
+    a = list(args)
+    a[17] = ctypes.c_float(a[17])  # softmax_scale
+    return lib().fd_decode_attention_mq(q, num_query, *a)
 
 
 def _ptr(t):
@@ -130,35 +145,50 @@ def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_ta
                      block_size: int = 0, out=None, out_dtype: str = "f32", lse=None,
                      workspace=None, num_partitions: int = 0, stream=None):
     """One decode step on the GPU.  Shapes follow ``include/fd.h``; sizes are read from the
-    tensors.  ``out``/``workspace`` are allocated with torch when not given (pass them in to
-    keep the call allocation-free).  Returns ``out``."""
+    tensors.  A 4-d q [batch][num_query][heads][head_dim] is a window of query tokens per
+    sequence (fd_decode_attention_mq; out and lse get the same leading dims).  ``out``/``workspace``
+    are allocated with torch when not given (pass them in to keep the call allocation-free).
+    Returns ``out``."""
     import torch
 
     _require_cuda(q=q, k_cache=k_cache, v_cache=v_cache, seq_len=seq_len, block_table=block_table,
                   kv_start=kv_start, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse,
                   workspace=workspace)
-    batch, hq, d = q.shape
+    window = q.dim() == 4
+    if window:
+        batch, nq, hq, d = q.shape
+    else:
+        (batch, hq, d), nq = q.shape, 1
     hkv = num_kv_heads if num_kv_heads is not None else k_cache.shape[-2]
     q_code = {torch.float16: FD_F16, torch.bfloat16: FD_BF16}[q.dtype]
     kv_code = DTYPE_CODES[kv_dtype]
     out_code = DTYPE_CODES[out_dtype]
     if out is None:
-        out = torch.empty((batch, hq, d), dtype={"f32": torch.float32, "f16": torch.float16,
+        out = torch.empty(tuple(q.shape), dtype={"f32": torch.float32, "f16": torch.float16,
                                                  "bf16": torch.bfloat16}[out_dtype], device=q.device)
+    # the kernels write one out row (and one lse value) per query row of q: refuse buffers of
+    # another size before anything is launched
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous tensor of q's shape {tuple(q.shape)} (got {tuple(out.shape)})")
+    if lse is not None and (lse.numel() != q.numel() // d or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous fp32 tensor of {q.numel() // d} elements")
     max_blocks = 0 if block_table is None else block_table.shape[1]
-    need = workspace_bytes(batch, hq, hkv, d, max_seq_len, block_size, kv_dtype, num_partitions)
+    need = workspace_bytes(batch, hq, hkv, d, max_seq_len, block_size, kv_dtype, num_partitions, nq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = decode_attention_raw(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), max_blocks,
-                              _ptr(kv_start), _ptr(seq_len), batch, max_seq_len, hq, hkv, d,
-                              block_size, kv_code, q_code, SCALE_CODES[scale_mode], _ptr(k_scale),
-                              _ptr(v_scale), float(softmax_scale), _ptr(out), out_code, _ptr(lse),
-                              _ptr(workspace), ws_bytes, num_partitions, stream)
+    args = (_ptr(k_cache), _ptr(v_cache), _ptr(block_table), max_blocks, _ptr(kv_start), _ptr(seq_len),
+            batch, max_seq_len, hq, hkv, d, block_size, kv_code, q_code, SCALE_CODES[scale_mode],
+            _ptr(k_scale), _ptr(v_scale), float(softmax_scale), _ptr(out), out_code, _ptr(lse),
+            _ptr(workspace), ws_bytes, num_partitions, stream)
+    if window:
+        st = decode_attention_mq_raw(_ptr(q), nq, *args)
+    else:
+        st = decode_attention_raw(_ptr(q), *args)
     if st != FD_OK:
-        raise FdError(st)
+        raise FdError(st, "fd_decode_attention_mq" if window else "fd_decode_attention")
     return out
 
 

@@ -17,6 +17,7 @@ namespace {
 constexpr long kDefaultWaves = 2048;
 constexpr long kDefaultWavesWide = 3072;
 constexpr int kMaxSeqLen = 1 << 24;
+constexpr int kMaxQueryWindow = 64;  // query tokens per sequence in one call
 
 thread_local hipEvent_t t_prof_begin = nullptr, t_prof_end = nullptr;
 
@@ -34,8 +35,9 @@ struct Plan {
 
 // Groups of 64+ query heads per kv head with E4M3 KV and head_dim 128 take the wide-group
 // kernel: 32 heads per wave, and 2 or 4 waves of one kv head share every K/V tile through LDS.
-bool use_wide(int group, int head_dim, int kv_dtype) {
-    return kv_dtype == FD_FP8_E4M3 && head_dim == 128 && group % 64 == 0;
+// (A window of several query tokens per sequence takes the 16-column kernel.)
+bool use_wide(int group, int head_dim, int kv_dtype, int nq) {
+    return nq == 1 && kv_dtype == FD_FP8_E4M3 && head_dim == 128 && group % 64 == 0;
 }
 
 bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
@@ -50,10 +52,12 @@ bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
 // divisor of their count up to 8 (wide kernel: 4 or 2 head blocks of one kv head); workgroup w
 // of the partition kernel takes tiles [w*q + min(w, r), ...) of the concatenation of all unit
 // groups (TT tiles of 32 tokens).  The workgroup count is capped by the largest TT the sizes allow.
-Plan make_plan(int batch, int hq, int hkv, int head_dim, int kv_dtype, int max_seq_len, int num_partitions) {
+// A window of nq query tokens multiplies the MFMA columns of a kv head: cols = group * nq.
+Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, int max_seq_len,
+               int num_partitions) {
     Plan pl;
-    const int group = hq / hkv;
-    pl.wide = use_wide(group, head_dim, kv_dtype);
+    const int group = hq / hkv, cols = group * nq;
+    pl.wide = use_wide(group, head_dim, kv_dtype, nq);
     if (pl.wide) {
         pl.hb = fd::kWideHeadBlock;
         pl.nhb = group / pl.hb;
@@ -61,7 +65,7 @@ Plan make_plan(int batch, int hq, int hkv, int head_dim, int kv_dtype, int max_s
         pl.groups = hkv * pl.nhb / pl.wpg;
     } else {
         pl.hb = fd::kHeadBlock;
-        pl.nhb = (int)cdiv(group, pl.hb);
+        pl.nhb = (int)cdiv(cols, pl.hb);
         const long ups = (long)hkv * pl.nhb;
         pl.wpg = 1;
         for (int d = fd::kMaxWavesPerGroup; d >= 1; d--)
@@ -101,36 +105,53 @@ const char *fd_status_string(int status) {
     }
 }
 
-int fd_plan_partitions(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
-                       int block_size, int kv_dtype, int num_partitions) {
+int fd_plan_partitions_mq(int batch, int num_query, int num_q_heads, int num_kv_heads, int head_dim,
+                          int max_seq_len, int block_size, int kv_dtype, int num_partitions) {
     (void)block_size;
     if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_partitions < 0) return -1;
-    return make_plan(batch, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len, num_partitions).nparts;
+    if (num_query < 1 || num_query > kMaxQueryWindow) return -1;
+    return make_plan(batch, num_query, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len, num_partitions)
+        .nparts;
+}
+
+int fd_plan_partitions(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                       int block_size, int kv_dtype, int num_partitions) {
+    return fd_plan_partitions_mq(batch, 1, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
+                                 kv_dtype, num_partitions);
+}
+
+size_t fd_workspace_bytes_mq(int batch, int num_query, int num_q_heads, int num_kv_heads, int head_dim,
+                             int max_seq_len, int block_size, int kv_dtype, int num_partitions) {
+    (void)block_size;
+    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_partitions < 0)
+        return (size_t)-1;
+    if (num_query < 1 || num_query > kMaxQueryWindow) return (size_t)-1;
+    Plan pl = make_plan(batch, num_query, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len,
+                        num_partitions);
+    return ws_bytes(pl, head_dim);
 }
 
 size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
                           int block_size, int kv_dtype, int num_partitions) {
-    (void)block_size;
-    if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len) || num_partitions < 0)
-        return (size_t)-1;
-    Plan pl = make_plan(batch, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len, num_partitions);
-    return ws_bytes(pl, head_dim);
+    return fd_workspace_bytes_mq(batch, 1, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
+                                 kv_dtype, num_partitions);
 }
 
-int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
-                        const int32_t *block_table, int max_blocks_per_seq,
-                        const int32_t *kv_start, const int32_t *seq_len,
-                        int batch, int max_seq_len,
-                        int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                        int kv_dtype, int q_dtype, int scale_mode,
-                        const float *k_scale, const float *v_scale,
-                        float softmax_scale,
-                        void *out, int out_dtype, float *lse,
-                        void *workspace, size_t workspace_bytes,
-                        int num_partitions, hipStream_t stream) {
+int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *kv_start, const int32_t *seq_len,
+                           int batch, int max_seq_len,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int kv_dtype, int q_dtype, int scale_mode,
+                           const float *k_scale, const float *v_scale,
+                           float softmax_scale,
+                           void *out, int out_dtype, float *lse,
+                           void *workspace, size_t workspace_bytes,
+                           int num_partitions, hipStream_t stream) {
     // ---- argument validation (host only, nothing launched on failure)
     if (!q || !k_cache || !v_cache || !seq_len || !out) return FD_ERR_INVALID_ARG;
     if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len)) return FD_ERR_INVALID_ARG;
+    if (num_query < 1 || num_query > kMaxQueryWindow) return FD_ERR_INVALID_ARG;
     if (num_partitions < 0) return FD_ERR_INVALID_ARG;
     if ((block_table == nullptr) == (kv_start == nullptr)) return FD_ERR_INVALID_ARG;
     if (kv_dtype != FD_F16 && kv_dtype != FD_BF16 && kv_dtype != FD_FP8_E4M3 && kv_dtype != FD_INT8)
@@ -151,7 +172,8 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
         if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
         if ((long)max_seq_len > (long)max_blocks_per_seq * block_size) return FD_ERR_INVALID_ARG;
     }
-    const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len, num_partitions);
+    const Plan pl = make_plan(batch, num_query, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len,
+                              num_partitions);
     const size_t need = ws_bytes(pl, head_dim);
     if (!workspace || workspace_bytes < need) return FD_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255) return FD_ERR_WORKSPACE;
@@ -176,6 +198,8 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     p.max_blocks = block_table ? max_blocks_per_seq : 0;
     p.max_seq_len = max_seq_len;
     p.group = num_q_heads / num_kv_heads;
+    p.nq = num_query;
+    p.cols = p.group * num_query;
     p.hb = pl.hb;
     p.nhb = pl.nhb;
     p.wpg = pl.wpg;
@@ -196,6 +220,23 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
     if (t_prof_end) (void)hipEventRecord(t_prof_end, stream);
     if (fd::launch_combine(p, stream) != hipSuccess) return FD_ERR_LAUNCH;
     return FD_OK;
+}
+
+int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_table, int max_blocks_per_seq,
+                        const int32_t *kv_start, const int32_t *seq_len,
+                        int batch, int max_seq_len,
+                        int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int kv_dtype, int q_dtype, int scale_mode,
+                        const float *k_scale, const float *v_scale,
+                        float softmax_scale,
+                        void *out, int out_dtype, float *lse,
+                        void *workspace, size_t workspace_bytes,
+                        int num_partitions, hipStream_t stream) {
+    return fd_decode_attention_mq(q, 1, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start, seq_len,
+                                  batch, max_seq_len, num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype,
+                                  q_dtype, scale_mode, k_scale, v_scale, softmax_scale, out, out_dtype, lse,
+                                  workspace, workspace_bytes, num_partitions, stream);
 }
 
 int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end) {

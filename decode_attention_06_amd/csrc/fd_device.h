@@ -27,6 +27,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // fp32 and f16, and acc / l is unchanged (both carry the same reference m), while the rescale
 // of the accumulator is skipped on most tiles.
 constexpr float kRescaleSlack = 8.0f;
+// Largest finite float: m = max(m_run, -kMaxFloat) keeps exp2 of (score - m) at 0, not NaN, while a
+// column has seen no token (m_run = -inf).
+constexpr float kMaxFloat = 3.40282347e38f;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 // ---------------------------------------------------------------- small helpers

@@ -18,7 +18,7 @@ constexpr int kMaxWavesPerGroup = 8;
 constexpr int kLdsBatch = 4096;
 
 struct Params {
-    const void *q;
+    const void *q;               // [batch][nq][hq][d]
     const void *k;
     const void *v;
     const int32_t *block_table;  // paged mode
@@ -34,8 +34,10 @@ struct Params {
     int block_size, max_blocks;
     int max_seq_len;  // host bound; seq_len values above it are clamped (never read past it)
     int group;        // hq / hkv
-    int hb;           // heads per head block (kHeadBlock or kWideHeadBlock)
-    int nhb;          // head blocks per kv head: ceil(group / hb)
+    int nq;           // query tokens per sequence (a window of nq rows; 1 for a plain decode step)
+    int cols;         // MFMA columns per kv head: group * nq (column m * group + h: row m, head h)
+    int hb;           // columns per head block (kHeadBlock or kWideHeadBlock)
+    int nhb;          // head blocks per kv head: ceil(cols / hb)
     int wpg;          // waves per partition workgroup = units per unit group (divides hkv*nhb)
     int groups;       // unit groups per sequence: hkv * nhb / wpg
     int nparts;       // partition workgroups (equal shares of the step's tiles)

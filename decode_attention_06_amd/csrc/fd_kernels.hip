@@ -278,6 +278,7 @@ void partition_kernel(Params p) {
     struct Desc {
         int64_t row0, row1;       // first cache rows of the tile's two 16-token halves
         int b, u_in, t0, last;    // sequence, unit in sequence, first token, last valid token in tile
+        int nrel;                 // tokens of the sequence from t0 on (> last)
         int seg;                  // segment index within the workgroup's range
         bool first, lastseg, whole;
     };
@@ -285,7 +286,8 @@ void partition_kernel(Params p) {
         d.b = b;
         d.u_in = grp * p.wpg + wave;
         d.t0 = tt * kTile;
-        d.last = min(n - d.t0, kTile) - 1;
+        d.nrel = n - d.t0;
+        d.last = min(d.nrel, kTile) - 1;
         if constexpr (PAGED) {
             d.row0 = (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + d.t0 / p.block_size) *
                          p.block_size + (d.t0 % p.block_size);
@@ -327,14 +329,34 @@ void partition_kernel(Params p) {
     u32x4_t qop[KSTEPS], qnext[KSTEPS];  // q operand of the current segment / of the next one
     f32x4_t acc[DT];
     float m_run = -INFINITY, l_run = 0.0f;
-    // q operand (B of q.k^T) of segment d's unit: column c = head hloc, k-slots of lane group g
+    // Lane column c of unit u_in: column col = hb * 16 + c of its kv head, i.e. query row
+    // m = col / group of the sequence's window and head hl = col % group of the kv head's group
+    struct Col {
+        bool valid;
+        int m, hl;
+    };
+    auto col_of = [&](int u_in) -> Col {
+        const int col = (u_in % p.nhb) * kHeadBlock + c;
+        Col r;
+        r.valid = col < p.cols;
+        if (p.nq == 1) {  // wave-uniform
+            r.m = 0;
+            r.hl = col;
+        } else {
+            r.m = col / p.group;
+            r.hl = col - r.m * p.group;
+        }
+        return r;
+    };
+    // q operand (B of q.k^T) of segment d's unit: lane column c, k-slots of lane group g
     auto load_q = [&](u32x4_t (&dst)[KSTEPS], const Desc &d) {
-        const int kvh = d.u_in / p.nhb, hb = d.u_in % p.nhb;
-        const int hloc = hb * kHeadBlock + c;
-        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)d.b * p.hq + kvh * p.group + hloc) * D;
+        const int kvh = d.u_in / p.nhb;
+        const Col cl = col_of(d.u_in);
+        const uint16_t *qrow =
+            (const uint16_t *)p.q + (((size_t)d.b * p.nq + cl.m) * p.hq + kvh * p.group + cl.hl) * D;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; kk++)
-            dst[kk] = hloc < p.group ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
+            dst[kk] = cl.valid ? *(const u32x4_t *)(qrow + qk_elem<E>(g, kk)) : u32x4_t{0, 0, 0, 0};
     };
     auto reset_state = [&]() {
 #pragma unroll
@@ -428,9 +450,13 @@ void partition_kernel(Params p) {
             else x *= qk_scale;
             s[j] = x;
         }
-        if (last < kTile - 1) {
+        // last token of this tile column c may see: query row m of a window of nq rows stops
+        // nq - 1 - m tokens before the sequence's end (a plain step: the tile's last valid token)
+        int lastc = last;
+        if (p.nq > 1) lastc = min(d.nrel - (p.nq - 1 - col_of(d.u_in).m), kTile) - 1;
+        if (__any(lastc < kTile - 1)) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) s[j] = (pv_token(g, j) <= last) ? s[j] : -INFINITY;
+            for (int j = 0; j < 8; j++) s[j] = (pv_token(g, j) <= lastc) ? s[j] : -INFINITY;
         }
         float mt = s[0];
 #pragma unroll
@@ -438,18 +464,21 @@ void partition_kernel(Params p) {
         mt = fmaxf(mt, shfl_xor_f(mt, 16));
         mt = fmaxf(mt, shfl_xor_f(mt, 32));
         // move the reference max only when some head exceeds it by more than kRescaleSlack
+        // (a column with no visible token yet keeps m_run = -inf: the max with -kMaxFloat below keeps
+        // its weights 0 and its alpha 1 instead of NaN)
         if (__any(mt > m_run + kRescaleSlack)) {  // wave-uniform; always taken on a segment's first tile
-            const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(fmaxf(m_run, -kMaxFloat) - fmaxf(m_new, -kMaxFloat));
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < DT; i++) acc[i] *= alpha;
             m_run = m_new;
         }
         float pj[8], psum = 0.0f;
+        const float m_ref = fmaxf(m_run, -kMaxFloat);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            pj[j] = __builtin_amdgcn_exp2f(s[j] - m_run);
+            pj[j] = __builtin_amdgcn_exp2f(s[j] - m_ref);
             psum += pj[j];
         }
         l_run += psum;
@@ -533,10 +562,10 @@ void partition_kernel(Params p) {
 
     // ---- segment result: total running sum over the four lane groups of head c
     auto finalize = [&](const Desc &d) {
-        const int kvh = d.u_in / p.nhb, hb = d.u_in % p.nhb;
-        const int hloc = hb * kHeadBlock + c;
-        const bool hvalid = hloc < p.group;
-        const int h = kvh * p.group + hloc;
+        const int kvh = d.u_in / p.nhb;
+        const Col cl = col_of(d.u_in);
+        const bool hvalid = cl.valid;
+        const size_t orow_idx = ((size_t)d.b * p.nq + cl.m) * p.hq + kvh * p.group + cl.hl;  // out / lse row
         float l_tot = l_run + shfl_xor_f(l_run, 16);
         l_tot += shfl_xor_f(l_tot, 32);
         f32x4_t o[DT];
@@ -545,8 +574,8 @@ void partition_kernel(Params p) {
         // lane (g, c) holds d = DT*(4g + r) + dt in o[dt][r]
         if (d.whole) {
             if (hvalid) {
-                const size_t orow = ((size_t)d.b * p.hq + h) * D;
-                const float inv = 1.0f / l_tot;
+                const size_t orow = orow_idx * D;
+                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // 0: a window row with no token
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     float v[DT];
@@ -554,7 +583,7 @@ void partition_kernel(Params p) {
                     for (int dt = 0; dt < DT; dt++) v[dt] = o[dt][r] * inv;
                     store_row_chunk<DT>(p.out, p.out_dtype, orow + DT * (4 * g + r), v);
                 }
-                if (p.lse && g == 0) p.lse[(size_t)d.b * p.hq + h] = (m_run + log2f(l_tot)) * kLn2;
+                if (p.lse && g == 0) p.lse[orow_idx] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
             }
         } else if (hvalid) {
             // slot 0: the range's first segment; slot 1: its last (a middle one is always whole)
@@ -626,11 +655,12 @@ void partition_kernel(Params p) {
 
 // ---------------------------------------------------------------- combine kernel
 //
-// Grid: x = q head, y = sequence.  Block: one wave.  For a unit cut by workgroup boundaries,
+// Grid: x = window row * hq + q head, y = sequence.  Block: one wave.  For a unit cut by workgroup boundaries,
 // merges its pieces -- slot 1 (or 0) of the first workgroup, slot 0 of the later ones -- with the
 // log-sum-exp rule for two partial states (m_a, l_a, acc_a), (m_b, l_b, acc_b):
 //   M = max(m_a, m_b),  w = 2^(m - M),  l = w_a l_a + w_b l_b,  acc = w_a acc_a + w_b acc_b
-// (an empty state has m = -inf and weight 0), then out = acc / l, lse = (M + log2 l) ln 2.
+// (an empty state has m = -inf and weight 0), then out = acc / l, lse = (M + log2 l) ln 2 (a
+// window row that sees no token: out = 0, lse = -inf).
 // Lane (j = lane / 8, k = lane % 8) folds pieces j, j+8, ... in order over output elements
 // [k*D/8, (k+1)*D/8), four pieces' loads in flight at a time; the eight lane-group states are
 // then merged by a fixed butterfly (both partners compute the same sums).  Also writes out = 0,
@@ -638,12 +668,13 @@ void partition_kernel(Params p) {
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     constexpr int PER = D / 8;  // output elements per lane
-    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int mq = blockIdx.x / p.hq, h = blockIdx.x % p.hq, b = blockIdx.y, lane = threadIdx.x;
     const int j = lane >> 3, k = lane & 7;
-    const int kvh = h / p.group, hloc = h % p.group;
-    const int u_in = kvh * p.nhb + hloc / p.hb;
-    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = hloc % p.hb;
-    const size_t obase = ((size_t)b * p.hq + h) * D + PER * k;
+    const int kvh = h / p.group, col = mq * p.group + h % p.group;  // column of the kv head
+    const int u_in = kvh * p.nhb + col / p.hb;
+    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = col % p.hb;
+    const size_t orow_idx = ((size_t)b * p.nq + mq) * p.hq + h;  // out / lse row
+    const size_t obase = orow_idx * D + PER * k;
 
     auto store = [&](const float *v) {
         if (p.out_dtype == 0) {
@@ -688,7 +719,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
             for (int i = 0; i < PER; i++) z[i] = 0.0f;
             store(z);
         }
-        if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = -INFINITY;
+        if (p.lse && lane == 0) p.lse[orow_idx] = -INFINITY;
         return;
     }
     const int64_t U0 = Pb * p.groups + (int64_t)grp * Tb;
@@ -721,8 +752,11 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             if (i0 + 8 * u < np) {
-                const float mn = fmaxf(m, ml[u].x);  // finite: every piece holds a token
-                const float wa = __builtin_amdgcn_exp2f(m - mn), wb = __builtin_amdgcn_exp2f(ml[u].x - mn);
+                // a piece of a window row can hold no visible token (m = -inf, l = 0): the max with
+                // -kMaxFloat gives it weight 0 (and an all-empty state weight 1 on zeros), not NaN
+                const float mn = fmaxf(m, ml[u].x);
+                const float ma = fmaxf(m, -kMaxFloat), mb = fmaxf(ml[u].x, -kMaxFloat), mc = fmaxf(mn, -kMaxFloat);
+                const float wa = __builtin_amdgcn_exp2f(ma - mc), wb = __builtin_amdgcn_exp2f(mb - mc);
                 l = l * wa + ml[u].y * wb;
 #pragma unroll
                 for (int e = 0; e < PER / 4; e++) {
@@ -748,11 +782,11 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
         m = mn;
     }
     if (j == 0) {
-        const float inv = 1.0f / l;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
         for (int e = 0; e < PER; e++) o[e] *= inv;
         store(o);
-        if (p.lse && lane == 0) p.lse[(size_t)b * p.hq + h] = (m + log2f(l)) * kLn2;
+        if (p.lse && lane == 0) p.lse[orow_idx] = l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -833,7 +867,7 @@ hipError_t launch_partition(const Params &p, int kv_dtype, int q_dtype, int scal
 }
 
 hipError_t launch_combine(const Params &p, hipStream_t stream) {
-    dim3 grid(p.hq, p.batch), block(64);
+    dim3 grid(p.hq * p.nq, p.batch), block(64);
     if (p.d == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, stream, p);
     else hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, stream, p);
     return hipGetLastError();

@@ -142,6 +142,42 @@ int fd_plan_partitions(int batch, int num_q_heads, int num_kv_heads, int head_di
                        int max_seq_len, int block_size, int kv_dtype, int num_partitions);
 
 /*
+ * fd_decode_attention_mq -- the same step for a window of num_query query tokens per sequence,
+ * e.g. the draft tokens a speculative-decoding verify pass checks at once ("第 15 章 · GPU
+ * Profiling 与 LLM 推理优化实战", section 15.21; "从 SGLang Kernel源码到 GPU Trace：DeepSeek V4.1
+ * Flash-Decode", section 2.2, tiles several query rows per block).  The window's tokens are the
+ * last num_query tokens already in the cache (seq_len[b] counts them), so query row m sits at
+ * position seq_len[b] - num_query + m and attends to tokens [0, seq_len[b] - num_query + m] (a
+ * causal window; a row with an empty range gets out = 0, lse = -inf).  All K/V bytes of a
+ * sequence are read once for the whole window: row m of every head of a kv head's group is one
+ * more MFMA column of that kv head.
+ *   q      [batch][num_query][num_q_heads][head_dim], q_dtype, contiguous.
+ *   out    [batch][num_query][num_q_heads][head_dim] in out_dtype.
+ *   lse    optional [batch][num_query][num_q_heads] fp32.
+ *   num_query  1..64; 1 is exactly fd_decode_attention.  Every other argument, the workspace
+ *          rule (size from fd_workspace_bytes_mq with the same num_query) and the status codes
+ *          are as for fd_decode_attention.  Windows always take the 16-column kernel.
+ */
+int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *kv_start, const int32_t *seq_len,
+                           int batch, int max_seq_len,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int kv_dtype, int q_dtype, int scale_mode,
+                           const float *k_scale, const float *v_scale,
+                           float softmax_scale,
+                           void *out, int out_dtype, float *lse,
+                           void *workspace, size_t workspace_bytes,
+                           int num_partitions, hipStream_t stream);
+
+/* fd_workspace_bytes_mq / fd_plan_partitions_mq -- fd_workspace_bytes / fd_plan_partitions for a
+ * window of num_query query tokens ((size_t)-1 / -1 also when num_query is outside 1..64). */
+size_t fd_workspace_bytes_mq(int batch, int num_query, int num_q_heads, int num_kv_heads, int head_dim,
+                             int max_seq_len, int block_size, int kv_dtype, int num_partitions);
+int fd_plan_partitions_mq(int batch, int num_query, int num_q_heads, int num_kv_heads, int head_dim,
+                          int max_seq_len, int block_size, int kv_dtype, int num_partitions);
+
+/*
  * fd_fp8_e4m3_decode -- diagnostic: decodes n E4M3 bytes with the exact hardware conversions the
  * attention kernels use and writes out[2*i] = value via the f16 path, out[2*i+1] = value via the
  * bf16 path (both fp32, [2*n]).  Format: OCP 8-bit floating point, E4M3 (as for fd_dtype).

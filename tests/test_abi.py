@@ -192,3 +192,43 @@ BAD_APPEND = [
 @pytest.mark.parametrize("change,expect", BAD_APPEND, ids=[str(sorted(c)) for c, _ in BAD_APPEND])
 def test_kv_append_bad_arguments_rejected_before_launch(change, expect):
     assert fd.kv_append_raw(**good_append(**change)) == expect
+
+
+# ---------------------------------------------------------------- window of query tokens
+def _mq_call(nq, **kw):
+    a = good_args(**kw)
+    q = a.pop("q")
+    return fd.decode_attention_mq_raw(q, nq, *a.values())
+
+
+@pytest.mark.parametrize("nq", [0, -1, 65])
+def test_window_size_out_of_range_rejected(nq):
+    assert _mq_call(nq) == fd.FD_ERR_INVALID_ARG
+    assert fd.lib().fd_workspace_bytes_mq(2, nq, 8, 2, 128, 2000, 64, fd.FD_FP8_E4M3, 0) == ctypes.c_size_t(-1).value
+    assert fd.lib().fd_plan_partitions_mq(2, nq, 8, 2, 128, 2000, 64, fd.FD_FP8_E4M3, 0) == -1
+
+
+@pytest.mark.parametrize("nq", [1, 2, 16, 64])
+def test_window_accepted_up_to_the_launch(nq):
+    assert _mq_call(nq) == fd.FD_ERR_LAUNCH
+
+
+def test_window_other_arguments_checked_as_for_one_token():
+    for change, expect in BAD:
+        assert _mq_call(3, **change) == expect, change
+
+
+def test_window_of_one_matches_the_plain_plan():
+    for args in [(32, 64, 8, 128, 32768, 64, fd.FD_FP8_E4M3), (4, 128, 1, 128, 131072, 64, fd.FD_FP8_E4M3),
+                 (16, 32, 8, 128, 4096, 64, fd.FD_BF16)]:
+        b, hq, hkv, d, n, bs, kv = args
+        assert fd.lib().fd_plan_partitions_mq(b, 1, hq, hkv, d, n, bs, kv, 0) == fd.lib().fd_plan_partitions(b, hq, hkv, d, n, bs, kv, 0)
+        assert fd.lib().fd_workspace_bytes_mq(b, 1, hq, hkv, d, n, bs, kv, 0) == fd.lib().fd_workspace_bytes(b, hq, hkv, d, n, bs, kv, 0)
+
+
+def test_window_workspace_grows_with_the_columns():
+    # G = 8, nq = 4: 32 columns per kv head = 2 sixteen-column blocks; MQA windows leave the wide kernel
+    one = fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3")
+    four = fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3", num_query=4)
+    assert four >= one
+    assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3", num_query=2) == 2048 // 8

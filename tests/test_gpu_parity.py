@@ -45,7 +45,7 @@ def compare(name, got, ref, kv_dtype, seqs=None):
 
 
 def run_gpu(case, **kw):
-    lse = torch.empty((case.batch, case.hq), dtype=torch.float32, device="cuda")
+    lse = torch.empty(tuple(case.q.shape[:-1]), dtype=torch.float32, device="cuda")
     out = fd.decode_case(case, lse=lse, **kw)
     torch.cuda.synchronize()
     return out, lse

@@ -1,0 +1,124 @@
+"""GPU parity of the window of query tokens per sequence (fd_decode_attention_mq) against the
+oracle, through the C ABI.
+
+Query row m of a window of nq tokens sits at position seq_len - nq + m and attends to tokens
+[0, seq_len - nq + m]; every row of every head of a kv head's group is one more MFMA column of
+that kv head.  Bars as for the single-token step (per KV type).  Cases cover windows narrower and
+wider than one 16-column block, rows whose prefix ends inside, at and before a tile, sequences
+shorter than the window (empty rows: out 0, lse -inf), split units at several partition counts,
+both scale modes, INT8 and bf16 KV, 16-token pages and contiguous rows, and the full-size
+verify workload (batch 32, 64/8 heads, 4-token window, E4M3, T log-uniform 1K-32K).
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_06_amd as fd
+import oracle
+import workloads
+from test_gpu_parity import TOL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    fd.lib()
+    yield
+
+
+def check_window(name, case, num_partitions=0, seqs=None):
+    print(f"[{name}] lens={case.seq_lens[:8]} nq={case.nq} G={case.group} D={case.d} kv={case.kv_dtype} "
+          f"scale={case.scale_mode} bs={case.block_size} partitions={num_partitions}", flush=True)
+    lse = torch.empty(case.q.shape[:-1], dtype=torch.float32, device="cuda")
+    out = fd.decode_case(case, lse=lse, num_partitions=num_partitions)
+    torch.cuda.synchronize()
+    assert out.shape == case.q.shape
+    ref, ref_lse = oracle.decode_attention(oracle.Problem.from_case(case), seqs=seqs)
+    got = out.double().cpu().numpy()
+    gl = lse.cpu().numpy().astype(np.float64)
+    if seqs is not None:
+        got, ref, gl, ref_lse = got[seqs], ref[seqs], gl[seqs], ref_lse[seqs]
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    err = got - ref
+    max_abs = float(np.abs(err).max())
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
+    tol_abs, tol_rel = TOL[case.kv_dtype]
+    ok = max_abs <= tol_abs and rel <= tol_rel
+    print(f"[{name}] {'PASS' if ok else 'FAIL'} max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ok, f"{name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(gl)), f"{name}: lse finiteness differs"
+    assert np.all(np.isneginf(gl[~fin])), f"{name}: empty rows must give -inf"
+    if fin.any():
+        assert np.max(np.abs(gl[fin] - ref_lse[fin])) < 1e-3, f"{name}: lse mismatch"
+    return out
+
+
+WINDOW = [
+    # name, kwargs for workloads.custom_case
+    ("g8_nq2_fp8_tok", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[65, 1500, 31], nq=2, kv="fp8_e4m3",
+                            q="bf16", scale="token_head", block_size=64)),
+    ("g8_nq4_fp8_tok", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[700, 33, 4], nq=4, kv="fp8_e4m3",
+                            q="bf16", scale="token_head", block_size=64)),
+    ("g4_nq3_bf16_d64", dict(batch=2, hq=8, hkv=2, d=64, seq_lens=[333, 17], nq=3, kv="bf16", q="bf16",
+                             scale="none", block_size=32)),
+    ("g1_nq16_f16_contig", dict(batch=2, hq=4, hkv=4, d=128, seq_lens=[16, 300], nq=16, kv="f16", q="f16",
+                                scale="none", paged=False, block_size=0)),
+    ("mqa128_nq2_fp8_tensor", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[2049, 40], nq=2, kv="fp8_e4m3",
+                                   q="bf16", scale="tensor", block_size=64)),
+    ("g8_nq5_i8_bs16", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[3, 100, 48], nq=5, kv="int8", q="f16",
+                            scale="token_head", block_size=16)),
+    ("g6_nq3_fp8_f16q_bs32", dict(batch=2, hq=12, hkv=2, d=128, seq_lens=[95, 64], nq=3, kv="fp8_e4m3",
+                                  q="f16", scale="tensor", block_size=32)),
+]
+
+
+@pytest.mark.parametrize("name,kw", WINDOW, ids=[w[0] for w in WINDOW])
+@pytest.mark.parametrize("parts", [0, 1, 3, 100000])
+def test_window_small_shapes(name, kw, parts):
+    case = workloads.custom_case(seed=40, device="cuda", **kw)
+    check_window(f"{name}/p{parts}", case, num_partitions=parts)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 31, 32, 33, 34, 35, 36, 63, 64, 65, 4095])
+def test_window_length_edges(n):
+    # window of 4: the rows' prefixes end 3, 2, 1, 0 tokens before the sequence's end
+    lens = [n, 4, n + 1]
+    case = workloads.custom_case(seed=500 + n, device="cuda", batch=3, hq=16, hkv=2, d=128, seq_lens=lens,
+                                 nq=4, kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64,
+                                 max_seq_len=max(lens))
+    for parts in (0, 5):
+        check_window(f"window_len{n}/p{parts}", case, num_partitions=parts)
+
+
+def test_window_of_one_equals_the_single_token_step_bitwise():
+    case = workloads.custom_case(seed=41, device="cuda", batch=3, hq=16, hkv=2, d=128, seq_lens=[900, 5, 64],
+                                 kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64)
+    a = fd.decode_case(case)
+    case.q = case.q.unsqueeze(1).contiguous()
+    case.nq = 1
+    b = fd.decode_case(case)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b[:, 0])
+
+
+def test_window_rows_match_single_token_steps_on_prefixes():
+    # row m of the window = the plain step over the first seq_len - nq + m + 1 tokens (GPU vs GPU)
+    case = workloads.custom_case(seed=42, device="cuda", batch=2, hq=16, hkv=2, d=128, seq_lens=[1000, 77],
+                                 nq=3, kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64)
+    win = fd.decode_case(case)
+    for m in range(3):
+        c = workloads.Case(**{k: getattr(case, k) for k in case.__dataclass_fields__})
+        c.q, c.nq = case.q[:, m].contiguous(), 1
+        c.seq_len = case.seq_len - (3 - 1 - m)
+        one = fd.decode_case(c)
+        torch.cuda.synchronize()
+        err = (win[:, m] - one).abs().max().item()
+        assert err < 2e-4, (m, err)
+
+
+def test_workload_verify_fp8_32k_full():
+    check_window("verify_fp8_32k", workloads.make_case("verify_fp8_32k", device="cuda"))

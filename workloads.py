@@ -18,6 +18,8 @@ Workloads (sizes as specified for the decode workloads this library targets):
 * ``ragged_fp8``        batch 256, 90 % seq_len ~ U[256, 2048] and 10 % ~ U[32K, 128K],
                         32 q / 8 kv heads, head_dim 128, E4M3 KV, block_size 32, shuffled blocks.
 * ``int8_32k``          ``fp8_32k`` with INT8 KV (per-(token, kv-head) scales).
+* ``verify_fp8_32k``    ``fp8_32k`` with a window of 4 query tokens per sequence (a speculative-
+                        decoding verify pass over 4 draft tokens already in the cache).
 
 Recipe (the readings are listed in the design doc):
 
@@ -73,6 +75,9 @@ WORKLOADS = {
                        q="bf16", block_size=32, scale="token_head", paged=True),
     "int8_32k": dict(batch=32, hq=64, hkv=8, d=128, lens=("loguniform", 1024, 32768), kv="int8",
                      q="bf16", block_size=64, scale="token_head", paged=True),
+    "verify_fp8_32k": dict(batch=32, hq=64, hkv=8, d=128, lens=("loguniform", 1024, 32768),
+                           kv="fp8_e4m3", q="bf16", block_size=64, scale="token_head", paged=True,
+                           nq=4),
 }
 
 
@@ -101,6 +106,7 @@ class Case:
     seq_len: torch.Tensor                # int32 [B]
     max_blocks: int
     softmax_scale: float
+    nq: int = 1                          # query tokens per sequence (q is [B][nq][Hq][D] when > 1)
 
     @property
     def group(self) -> int:
@@ -255,7 +261,9 @@ def _build(name, cfg, seed, device, seq_lens) -> Case:
         scale = "none"
     max_seq_len = int(cfg.get("max_seq_len", max(seq_lens) if seq_lens else 0))
     gen = torch.Generator(device=device).manual_seed(seed)
-    q = torch.randn((batch, hq, d), generator=gen, device=device, dtype=torch.float32).to(_TORCH[qd])
+    nq = int(cfg.get("nq", 1))
+    qshape = (batch, nq, hq, d) if nq > 1 else (batch, hq, d)
+    q = torch.randn(qshape, generator=gen, device=device, dtype=torch.float32).to(_TORCH[qd])
     nan = _nan_bits(kv)
     if paged:
         nb_per = [(n + bs - 1) // bs for n in seq_lens]
@@ -313,14 +321,14 @@ def _build(name, cfg, seed, device, seq_lens) -> Case:
                 scale_mode=scale, block_size=bs, paged=paged, seq_lens=seq_lens,
                 max_seq_len=max_seq_len, q=q, k_cache=k, v_cache=v, k_scale=ks, v_scale=vs,
                 block_table=block_table, kv_start=kv_start, seq_len=seq_len,
-                max_blocks=max_blocks, softmax_scale=1.0 / math.sqrt(d))
+                max_blocks=max_blocks, softmax_scale=1.0 / math.sqrt(d), nq=nq)
 
 
 def custom_case(seed=0, device="cpu", *, batch, hq, hkv, d, seq_lens, kv="fp8_e4m3", q="bf16",
-                block_size=64, scale="token_head", paged=True, shuffle=True, max_seq_len=None):
+                block_size=64, scale="token_head", paged=True, shuffle=True, max_seq_len=None, nq=1):
     """A case with explicit shapes (edge cases and small parity sizes)."""
     cfg = dict(batch=batch, hq=hq, hkv=hkv, d=d, lens=("fixed_list", list(seq_lens)), kv=kv,
-               q=q, block_size=block_size, scale=scale, paged=paged, shuffle=shuffle)
+               q=q, block_size=block_size, scale=scale, paged=paged, shuffle=shuffle, nq=nq)
     if max_seq_len is not None:
         cfg["max_seq_len"] = max_seq_len
     return _build("custom", cfg, seed, device, list(seq_lens))
