@@ -16,6 +16,8 @@ roofline        = the partition kernel: the same algorithmic bytes / its mean du
                   HIP events recorded around it on its stream, against 8 TB/s HBM peak; traffic =
                   HBM bytes per launch from committed rocprofv3 counter runs of the same sources.
 read_probe      = a plain 128-bit streaming read of 4 GiB (the practical read ceiling).
+graph           = the same step captured once per KV copy in a HIP graph and replayed (launch
+                  overhead removed; `value` stays the eager call).
 cpu_baseline    = the fp64 oracle on up to 16 host cores, the whole step, same inputs.
 """
 from __future__ import annotations
@@ -110,6 +112,29 @@ def kv_append_timing(fd, torch, case, target, stream, reps=50):
             "what": "fd_kv_append: one bf16 K and V row per (sequence, kv head) into the cache"}
 
 
+def graph_step_timing(torch, step, ncopy, steps, stream):
+    """The same step captured once per KV copy in a HIP graph (the library is capture-safe: no
+    allocation, memset or host sync) and replayed `steps` times, rotating the copies as the eager
+    loop does.  Returns microseconds per step."""
+    graphs = []
+    for i in range(ncopy):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i, torch.cuda.current_stream().cuda_stream)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(3 * ncopy):
+        graphs[i % ncopy].replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(steps):
+        graphs[i % ncopy].replay()
+    b.record()
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) * 1e3 / steps, 2)
+
+
 def read_probe(fd, torch, dev, stream, nbytes=4 << 30, reps=5):
     """The practical HBM read ceiling: a plain coalesced 128-bit streaming read of a 4 GiB buffer
     (fd_hbm_read_probe), best over a few grid sizes, mean of `reps` back-to-back reads each."""
@@ -143,6 +168,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--no-read-probe", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--block-size", type=int, default=None, help="page size override (16, 32, 64)")
     ap.add_argument("--seq-len", type=int, default=None, help="every sequence this many tokens")
     ap.add_argument("--layout", choices=("contiguous", "ordered", "fragmented"), default=None,
@@ -280,6 +306,13 @@ def main():
     }
 
     result["kv_append"] = kv_append_timing(fd, torch, case, copies[0], stream)
+
+    if not args.no_graph:
+        def graph_step(i, s):
+            fd.decode_case(copies[i % ncopy], out=out, lse=lse, workspace=ws,
+                           num_partitions=args.num_partitions, stream=s)
+        result["graph"] = {"us_per_step": graph_step_timing(torch, graph_step, ncopy, args.steps, stream),
+                           "what": "the same step captured once per KV copy in a HIP graph, replayed"}
 
     if not args.no_read_probe:
         result["read_probe"] = read_probe(fd, torch, dev, stream)
