@@ -127,6 +127,11 @@ SMALL = [
                                 q="bf16", scale="token_head", block_size=16)),
     ("bs16_wide_g64_tensor", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[65, 300, 1], kv="fp8_e4m3",
                                   q="bf16", scale="tensor", block_size=16)),
+    # one long sequence over few units: the combine spreads each row over several waves (D slices)
+    ("mqa8_d64_long_f16", dict(batch=1, hq=8, hkv=1, d=64, seq_lens=[4000], kv="f16", q="f16",
+                               scale="none", block_size=32)),
+    ("mqa16_d128_long_fp8", dict(batch=2, hq=16, hkv=1, d=128, seq_lens=[5000, 3], kv="fp8_e4m3",
+                                 q="bf16", scale="token_head", block_size=64)),
     # INT8 KV: both scale modes and q types, both head dims, every page size and contiguous, a
     # group of 128 (eight 16-head blocks per kv head)
     ("gqa8_i8_tok", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[65, 1500, 31], kv="int8",
