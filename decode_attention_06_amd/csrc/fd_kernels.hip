@@ -655,24 +655,30 @@ void partition_kernel(Params p) {
 
 // ---------------------------------------------------------------- combine kernel
 //
-// Grid: x = window row * hq + q head, y = sequence.  Block: one wave.  For a unit cut by workgroup boundaries,
-// merges its pieces -- slot 1 (or 0) of the first workgroup, slot 0 of the later ones -- with the
-// log-sum-exp rule for two partial states (m_a, l_a, acc_a), (m_b, l_b, acc_b):
+// Grid: x = window row * hq + q head, y = sequence.  Block: NW waves.  For a unit cut by
+// workgroup boundaries, merges its pieces -- slot 1 (or 0) of the first workgroup, slot 0 of the
+// later ones -- with the log-sum-exp rule for two partial states (m_a, l_a, acc_a), (m_b, l_b, acc_b):
 //   M = max(m_a, m_b),  w = 2^(m - M),  l = w_a l_a + w_b l_b,  acc = w_a acc_a + w_b acc_b
 // (an empty state has m = -inf and weight 0), then out = acc / l, lse = (M + log2 l) ln 2 (a
 // window row that sees no token: out = 0, lse = -inf).
-// Lane (j = lane / 8, k = lane % 8) folds pieces j, j+8, ... in order over output elements
-// [k*D/8, (k+1)*D/8), four pieces' loads in flight at a time; the eight lane-group states are
-// then merged by a fixed butterfly (both partners compute the same sums).  Also writes out = 0,
-// lse = -inf for empty sequences.  Fixed order throughout: deterministic.
-template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(Params p) {
+// Lane group j = lane / 8 of wave w (global group g = 8 w + j) folds pieces g, g + 8 NW, ... in
+// order over output elements [k*D/8, (k+1)*D/8), k = lane % 8, four pieces' loads in flight at a
+// time; the eight lane-group states of a wave are merged by a fixed butterfly (both partners
+// compute the same sums), and the NW wave states, in wave order, through LDS.  A row of at most
+// 32 pieces is merged by wave 0 alone (one round of loads).  Many pieces per row (a few very long
+// sequences over many workgroups) make the single-wave merge a chain of dependent load rounds;
+// NW > 1 splits that chain.  Also writes out = 0, lse = -inf for empty sequences.  Fixed order
+// throughout: deterministic for a given NW.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
     constexpr int PER = D / 8;  // output elements per lane
-    const int mq = blockIdx.x / p.hq, h = blockIdx.x % p.hq, b = blockIdx.y, lane = threadIdx.x;
+    __shared__ float sh_state[NW > 1 ? NW : 1][D + 2];
+    const int mq = blockIdx.x / p.hq, h = blockIdx.x % p.hq, b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = NW > 1 ? uni((int)(threadIdx.x >> 6)) : 0;
     const int j = lane >> 3, k = lane & 7;
     const int kvh = h / p.group, col = mq * p.group + h % p.group;  // column of the kv head
     const int u_in = kvh * p.nhb + col / p.hb;
-    const int grp = u_in / p.wpg, wave = u_in % p.wpg, c = col % p.hb;
+    const int grp = u_in / p.wpg, uw = u_in % p.wpg, c = col % p.hb;
     const size_t orow_idx = ((size_t)b * p.nq + mq) * p.hq + h;  // out / lse row
     const size_t obase = orow_idx * D + PER * k;
 
@@ -713,6 +719,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     const int64_t TT = tot * p.groups, Pb = bef;
     const int Tb = mine;
     if (Tb == 0) {
+        if (wave != 0) return;
         if (j == 0) {
             float z[PER];
 #pragma unroll
@@ -729,21 +736,26 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
     // pieces: the ranges wlo..whi in order (never empty: with fewer tiles than workgroups every
     // non-empty range holds one tile and split_owner(t) = t)
     const int np = (int)(whi - wlo + 1);
+    // the same for every wave of the workgroup: the split-up merge (and its barrier) runs in all
+    // of them or in none
+    const int nw = np <= 32 ? 1 : NW;
+    if (wave >= nw) return;
     const int first_slot = split_lo(sp, wlo) == U0 ? 0 : 1;  // unit began inside wlo's range
     auto slot_of = [&](int i) -> size_t {
-        return (((size_t)(wlo + i) * 2 + (i == 0 ? first_slot : 0)) * p.wpg + wave) * p.hb + c;
+        return (((size_t)(wlo + i) * 2 + (i == 0 ? first_slot : 0)) * p.wpg + uw) * p.hb + c;
     };
 
-    // ---- this lane group's pieces j, j+8, ..., four at a time
+    // ---- this lane group's pieces g, g + 8 nw, ..., four at a time
+    const int g = 8 * wave + j, gstride = 8 * nw;
     float m = -INFINITY, l = 0.0f, o[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) o[i] = 0.0f;
-    for (int i0 = j; i0 < np; i0 += 32) {
+    for (int i0 = g; i0 < np; i0 += 4 * gstride) {
         float2 ml[4];
         float4 x[4][PER / 4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            const size_t slot = slot_of(min(i0 + 8 * u, np - 1));
+            const size_t slot = slot_of(min(i0 + gstride * u, np - 1));
             ml[u] = p.ws_ml[slot];
             const float *src = p.ws_acc + slot * D + PER * k;
 #pragma unroll
@@ -751,7 +763,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
         }
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            if (i0 + 8 * u < np) {
+            if (i0 + gstride * u < np) {
                 // a piece of a window row can hold no visible token (m = -inf, l = 0): the max with
                 // -kMaxFloat gives it weight 0 (and an all-empty state weight 1 on zeros), not NaN
                 const float mn = fmaxf(m, ml[u].x);
@@ -769,7 +781,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
             }
         }
     }
-    // ---- merge the eight lane-group states
+    // ---- merge the eight lane-group states of the wave
 #pragma unroll
     for (int off = 8; off < 64; off <<= 1) {
         const float mo = shfl_xor_f(m, off), lo = shfl_xor_f(l, off);
@@ -780,6 +792,34 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < PER; e++) o[e] = o[e] * wa + shfl_xor_f(o[e], off) * wb;
         m = mn;
+    }
+    if constexpr (NW > 1) {
+        // ---- then the wave states, in wave order (lanes 0..7 of a wave hold its state)
+        if (nw > 1) {
+            if (j == 0) {
+#pragma unroll
+                for (int e = 0; e < PER; e += 4)
+                    *(float4 *)&sh_state[wave][PER * k + e] = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+                if (k == 0) {
+                    sh_state[wave][D] = m;
+                    sh_state[wave][D + 1] = l;
+                }
+            }
+            __syncthreads();
+            if (wave != 0) return;
+            if (j == 0) {
+                for (int w2 = 1; w2 < nw; w2++) {
+                    const float mo = sh_state[w2][D], lo = sh_state[w2][D + 1];
+                    const float mn = fmaxf(m, mo);
+                    const float wa = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+                    const float wb = mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+                    l = l * wa + lo * wb;
+#pragma unroll
+                    for (int e = 0; e < PER; e++) o[e] = o[e] * wa + sh_state[w2][PER * k + e] * wb;
+                    m = mn;
+                }
+            }
+        }
     }
     if (j == 0) {
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -866,10 +906,26 @@ hipError_t launch_partition(const Params &p, int kv_dtype, int q_dtype, int scal
     return launch_d<64>(p, kv_dtype, q_dtype, scale_mode, stream);
 }
 
+// Waves per combine workgroup: the partition workgroups per sequence bound the pieces of a row
+// from above on average; past 16 of them rows of the longer sequences exceed the 32 pieces one
+// wave merges in a single round of loads.
+static int combine_waves(const Params &p) {
+    const long per_seq = (long)p.nparts / p.batch;
+    return per_seq > 64 ? 8 : per_seq > 16 ? 4 : 1;
+}
+
+template <int D>
+static void launch_combine_d(const Params &p, int nw, hipStream_t stream) {
+    dim3 grid(p.hq * p.nq, p.batch);
+    if (nw == 8) hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(512), 0, stream, p);
+    else if (nw == 4) hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((combine_kernel<D, 1>), grid, dim3(64), 0, stream, p);
+}
+
 hipError_t launch_combine(const Params &p, hipStream_t stream) {
-    dim3 grid(p.hq * p.nq, p.batch), block(64);
-    if (p.d == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, stream, p);
-    else hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, stream, p);
+    const int nw = combine_waves(p);
+    if (p.d == 128) launch_combine_d<128>(p, nw, stream);
+    else launch_combine_d<64>(p, nw, stream);
     return hipGetLastError();
 }
 

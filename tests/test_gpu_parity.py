@@ -127,7 +127,7 @@ SMALL = [
                                 q="bf16", scale="token_head", block_size=16)),
     ("bs16_wide_g64_tensor", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[65, 300, 1], kv="fp8_e4m3",
                                   q="bf16", scale="tensor", block_size=16)),
-    # one long sequence over few units: the combine spreads each row over several waves (D slices)
+    # one long sequence over few units: many pieces per row, merged by several combine waves
     ("mqa8_d64_long_f16", dict(batch=1, hq=8, hkv=1, d=64, seq_lens=[4000], kv="f16", q="f16",
                                scale="none", block_size=32)),
     ("mqa16_d128_long_fp8", dict(batch=2, hq=16, hkv=1, d=128, seq_lens=[5000, 3], kv="fp8_e4m3",
@@ -261,6 +261,18 @@ def test_run_to_run_bitwise_deterministic():
     a, la = run_gpu(case)
     b, lb = run_gpu(case)
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_run_to_run_bitwise_deterministic_many_pieces():
+    # one MQA sequence over hundreds of workgroups: each row's pieces are split over the eight
+    # waves of its combine workgroup and merged through LDS in a fixed order
+    case = workloads.custom_case(seed=5, device="cuda", batch=1, hq=128, hkv=1, d=128,
+                                 seq_lens=[40000], kv="fp8_e4m3", q="bf16", scale="tensor",
+                                 block_size=64)
+    a, la = run_gpu(case)
+    b, lb = run_gpu(case)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    check_case("mqa_one_long_seq", case)
 
 
 def test_block_placement_bitwise_invariant():
