@@ -18,7 +18,9 @@ roofline        = the partition kernel: the same algorithmic bytes / its mean du
 read_probe      = a plain 128-bit streaming read of 4 GiB (the practical read ceiling).
 graph           = the same step captured once per KV copy in a HIP graph and replayed (launch
                   overhead removed; `value` stays the eager call).
-cpu_baseline    = the fp64 oracle on up to 16 host cores, the whole step, same inputs.
+cpu_baseline    = the fp64 oracle on up to 16 host cores, the whole step, same inputs; one_core =
+                  the oracle on one thread over a bounded sample of whole sequences.
+gpu_state       = GPU clock levels and power (amdgpu sysfs) right after the timed steps.
 """
 from __future__ import annotations
 
@@ -110,6 +112,57 @@ def kv_append_timing(fd, torch, case, target, stream, reps=50):
     us = a.elapsed_time(b) * 1e3 / reps
     return {"us_per_call": round(us, 2), "rows": rows, "bytes_moved": moved,
             "what": "fd_kv_append: one bf16 K and V row per (sequence, kv head) into the cache"}
+
+
+def one_core_oracle(oracle, prob, case, np, min_tokens=20000):
+    """The oracle on one host thread over a bounded sample: whole sequences in index order until
+    they hold at least `min_tokens` tokens; the rate is that sample's KV bytes over its time."""
+    seqs, tok = [], 0
+    for b, n in enumerate(case.seq_lens):
+        if n > 0:
+            seqs.append(b)
+            tok += n
+        if tok >= min_tokens:
+            break
+    if not seqs:
+        return None
+    per_token = case.kv_read_bytes() / max(sum(case.seq_lens), 1)
+    t0 = time.perf_counter()
+    oracle.decode_attention(prob, seqs=seqs, nthreads=1)
+    dt = time.perf_counter() - t0
+    return {"value": round(per_token * tok / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "sample": f"sequences {seqs[0]}..{seqs[-1]} ({len(seqs)} sequences, {tok} tokens, all heads), "
+                      f"one run: {dt:.2f} s wall"}
+
+
+def gpu_state():
+    """Clock levels and power of the GPU right after the timed steps (boost clocks change kernel
+    times from run to run), read from the amdgpu driver's sysfs files -- no program is started.
+    None where the files are not visible."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        try:
+            if open(os.path.join(dev, "vendor")).read().strip() != "0x1002":
+                continue
+        except OSError:
+            continue
+        state = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                levels = open(os.path.join(dev, name)).read().splitlines()
+            except OSError:
+                continue
+            cur = [ln.split(":", 1)[-1].strip(" *") for ln in levels if ln.rstrip().endswith("*")]
+            state[name[7:] + "_current"] = cur[0] if cur else None
+        for hw in glob.glob(os.path.join(dev, "hwmon", "hwmon*")):
+            for f in ("power1_average", "power1_input"):
+                try:
+                    state[f + "_W"] = int(open(os.path.join(hw, f)).read()) / 1e6
+                except (OSError, ValueError):
+                    pass
+        if state:
+            return {"source": dev, **state}
+    return None
 
 
 def graph_step_timing(torch, step, ncopy, steps, stream):
@@ -339,7 +392,9 @@ def main():
             "sample": f"the whole step ({case.batch} sequences, {sum(case.seq_lens)} tokens, all heads), "
                       f"median of {runs} run(s): {dt:.2f} s wall",
             "us_per_step": round(dt * 1e6, 1),
+            "one_core": one_core_oracle(oracle, prob, case, np),
         }
+    result["gpu_state"] = gpu_state()
     print(json.dumps(result), flush=True)
 
 
