@@ -297,6 +297,7 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
+    state = gpu_state()
 
     # ---- partition-kernel durations from HIP events recorded around it, on its stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -394,7 +395,7 @@ def main():
             "us_per_step": round(dt * 1e6, 1),
             "one_core": one_core_oracle(oracle, prob, case, np),
         }
-    result["gpu_state"] = gpu_state()
+    result["gpu_state"] = state
     print(json.dumps(result), flush=True)
 
 
