@@ -43,11 +43,37 @@ KERNEL_SRCS = [os.path.join(ROOT, "decode_attention_06_amd", "csrc", f)
                for f in ("fd_kernels.hip", "fd_wide.hip", "fd_device.h", "fd_internal.h")]
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without comments and with runs of whitespace collapsed (string literals
+    kept; a '//' inside one does not start a comment)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == '"':
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash() -> str:
-    """Hash of the device sources: committed counter runs count only while it is unchanged."""
+    """Hash of the device code (comments and layout ignored): committed counter runs count only
+    while it is unchanged."""
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+        h.update(strip_comments(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -16,9 +16,13 @@
 // The split-KV combine (log-sum-exp merge of per-split (m, l, acc)) is the same recurrence
 // applied to whole partial states.
 //
-// gfx950 design (differs from the pages' Hopper kernel):
-//   * One wave64 workgroup per (sequence, kv head, head block, split).  No LDS: every MFMA
-//     operand is loaded straight from HBM into the register layout the instruction wants.
+// gfx950 design (differs from the pages' Hopper kernel, which stages KV through shared memory
+// with async copies and runs mma.sync on 32-wide warps):
+//   * Persistent workgroups of up to 8 wave64s, one wave per unit (sequence, kv head, 16-head
+//     block) of a unit group; each workgroup streams an equal share of the step's 32-token tiles
+//     (balanced over the sum of all sequences' lengths, computed on the device).  KV is never
+//     staged in LDS: every MFMA operand is loaded straight from HBM into the register layout the
+//     instruction wants, one tile ahead of the compute.
 //   * q.k^T runs on v_mfma_f32_16x16x32_{bf16,f16}: A = 16 tokens x 32 d of K (converted to
 //     q's type -- exact for E4M3), B = 32 d x 16 heads of q.  Lane (g = lane/16, c = lane%16)
 //     of the C tile holds the scores of tokens 4g..4g+3 of the 16-token half for head c.

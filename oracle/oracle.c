@@ -19,7 +19,7 @@
  *         per-token k/v scales, dequantised inside the scan) and section 15.12 (one KV head
  *         serves group = QH / KVH query heads).
  *
- * Readings where the pages are silent (all stated in the design doc):
+ * Readings where the pages are silent:
  *   - q head h reads kv head h / (QH / KVH).
  *   - FP8 means OCP E4M3FN; a dequantised element is decode(byte) * scale, the scale being
  *     one fp32 per tensor or one fp32 per (token, kv head) stored like the cache rows.  INT8 KV
@@ -264,12 +264,12 @@ int orc_decode_attention(const orc_problem *p, const uint8_t *seq_mask, double *
  * KV-cache append of the current token: the step that precedes the scan.
  *
  * Sources: [CH15] 15.9 (paged cache writes; its exercise 4 adds a single-token decode append),
- * 15.11 (quantised KV with per-token k/v scales) and 15.18 (row-wise absmax -> scale ->
- * quantise).  Readings: a row is one token's D values of one kv head; its scale is
- * amax|x| / 448 (448 = largest E4M3 value; 1 when the row is all zeros); the quantised value is
- * x / scale, clamped to [-448, 448], rounded to the nearest E4M3 value with ties to an even
- * mantissa.  The decision is taken in fp32 -- scale and quotient are fp32 operations -- the
- * precision the kernels quantise in; only the final rounding to E4M3 is done here by exact
+ * 15.11 (quantised KV with per-token k/v scales) and 15.18 (row-wise absmax -> scale -> quantise).
+ * Readings where the pages are silent: a row is one token's D values of one kv head; its scale is
+ * amax|x| / 448 (448 = largest E4M3 value; 1 when the row is all zeros); the quantised value is x /
+ * scale, clamped to [-448, 448], rounded to the nearest E4M3 value with ties to an even mantissa.
+ * The decision is taken in fp32 -- scale and quotient are fp32 operations -- the precision the
+ * kernels quantise in; only the final rounding to E4M3 is done here by exact
  * search.  f16 / bf16 caches store the fp32 value rounded to nearest-even.
  * ====================================================================================== */
 

@@ -21,7 +21,7 @@ Workloads (sizes as specified for the decode workloads this library targets):
 * ``verify_fp8_32k``    ``fp8_32k`` with a window of 4 query tokens per sequence (a speculative-
                         decoding verify pass over 4 draft tokens already in the cache).
 
-Recipe (the readings are listed in the design doc):
+Recipe (readings where the pages leave the inputs open):
 
 * Sequence lengths come from ``numpy.random.Generator(PCG64(seed))``; integer bounds are
   inclusive; log-uniform is ``round(exp(U(ln a, ln b)))``; the ragged mix has exactly
