@@ -22,7 +22,7 @@ SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head
 EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
            "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe",
            "fd_kv_append", "fd_fp8_e4m3_encode", "fd_decode_attention_mq", "fd_workspace_bytes_mq",
-           "fd_plan_partitions_mq")
+           "fd_plan_partitions_mq", "fd_check_inputs")
 
 _lock = threading.Lock()
 _lib = None
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp]
         L.fd_fp8_e4m3_encode.restype = i32
         L.fd_fp8_e4m3_encode.argtypes = [vp, vp, i32, vp]
+        L.fd_check_inputs.restype = i32
+        L.fd_check_inputs.argtypes = [vp, vp, i32, vp, i32, i32, i32, ctypes.c_int64, vp, vp]
         _lib = L
         return L
 
@@ -275,6 +277,44 @@ def set_profile_events(begin=None, end=None):
     st = lib().fd_set_profile_events(bp, ep)
     if st != FD_OK:
         raise FdError(st, "fd_set_profile_events")
+
+
+CHECK_KINDS = {0: "none", 1: "seq_len", 2: "block_table", 3: "kv_start"}
+
+
+def check_inputs_raw(seq_len, block_table, max_blocks_per_seq, kv_start, batch, max_seq_len, block_size,
+                     extent, result, stream) -> int:
+    """Direct call of fd_check_inputs with integer pointers; returns the status."""
+    return lib().fd_check_inputs(seq_len, block_table, max_blocks_per_seq, kv_start, batch, max_seq_len,
+                                 block_size, extent, result, stream)
+
+
+def check_inputs(seq_len, *, max_seq_len: int, extent: int, block_table=None, kv_start=None,
+                 block_size: int = 0, result=None, stream=None) -> dict:
+    """Debug validation of the device-side contract (see ``fd_check_inputs`` in include/fd.h):
+    seq_len range, the used block-table entries against ``extent`` physical blocks (paged) or
+    kv_start + seq_len against ``extent`` rows (contiguous).  ``result``: optional int32 GPU
+    tensor of 4 elements to write into.  Synchronises the device and returns
+    {"violations", "first_sequence", "kind", "value"}."""
+    import torch
+
+    _require_cuda(seq_len=seq_len, block_table=block_table, kv_start=kv_start)
+    batch = seq_len.numel()
+    max_blocks = 0 if block_table is None else block_table.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(seq_len.device).cuda_stream
+    if result is None:
+        result = torch.empty(4, dtype=torch.int32, device=seq_len.device)
+    elif result.dtype != torch.int32 or result.numel() < 4 or result.device != seq_len.device:
+        raise ValueError("result must be an int32 GPU tensor of at least 4 elements")
+    st = check_inputs_raw(seq_len.data_ptr(), None if block_table is None else block_table.data_ptr(),
+                          max_blocks, None if kv_start is None else kv_start.data_ptr(), batch, max_seq_len,
+                          block_size, extent, result.data_ptr(), stream)
+    if st != FD_OK:
+        raise FdError(st, "fd_check_inputs")
+    torch.cuda.synchronize(seq_len.device)
+    n, first, kind, value = result[:4].cpu().tolist()
+    return {"violations": n, "first_sequence": first, "kind": CHECK_KINDS.get(kind, kind), "value": value}
 
 
 def hbm_read_probe(buf, out, blocks: int, stream=None):

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "fd.h"
+#include "fd_check.h"
 #include "fd_internal.h"
 
 namespace {
@@ -93,6 +94,25 @@ size_t ws_bytes(const Plan &pl, int head_dim) {
 extern "C" {
 
 int fd_version(void) { return FD_VERSION; }
+
+int fd_check_inputs(const int32_t *seq_len, const int32_t *block_table, int max_blocks_per_seq,
+                    const int32_t *kv_start, int batch, int max_seq_len, int block_size,
+                    int64_t extent, int32_t *result, hipStream_t stream) {
+    if (!seq_len || !result) return FD_ERR_INVALID_ARG;
+    if (batch <= 0 || max_seq_len < 0 || extent < 0) return FD_ERR_INVALID_ARG;
+    if ((block_table == nullptr) == (kv_start == nullptr)) return FD_ERR_INVALID_ARG;
+    if (block_table) {
+        if (block_size != 16 && block_size != 32 && block_size != 64) return FD_ERR_UNSUPPORTED;
+        if (max_blocks_per_seq <= 0) return FD_ERR_INVALID_ARG;
+        // every used entry (logical block < ceil(seq_len / block_size), seq_len <= max_seq_len)
+        // then lies inside the table row
+        if ((long)max_seq_len > (long)max_blocks_per_seq * block_size) return FD_ERR_INVALID_ARG;
+    }
+    if (fd::launch_check(seq_len, block_table, max_blocks_per_seq, kv_start, batch, max_seq_len, block_size,
+                         extent, result, stream) != hipSuccess)
+        return FD_ERR_LAUNCH;
+    return FD_OK;
+}
 
 const char *fd_status_string(int status) {
     switch (status) {

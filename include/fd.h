@@ -106,9 +106,10 @@ typedef enum {
  *                that many (testing and tuning).  Capped by the number of tiles the sizes allow.
  *   stream       HIP stream to enqueue on (0 = null stream).
  *
- * Device-side contract (not checked; violating it is undefined): seq_len[b] <= max_seq_len,
- * block_table entries for logical blocks < ceil(seq_len[b] / block_size) are valid block ids,
- * kv_start[b] + seq_len[b] rows exist.  The kernels read only those entries and rows, so
+ * Device-side contract (not checked by the step; violating it is undefined; fd_check_inputs
+ * validates it for debugging): seq_len[b] <= max_seq_len, block_table entries for logical
+ * blocks < ceil(seq_len[b] / block_size) are valid block ids, kv_start[b] + seq_len[b] rows
+ * exist.  The kernels read only those entries and rows, so
  * unused table entries and unused slots of a last block may hold anything.
  *
  * Returns FD_OK or an fd_status.
@@ -240,6 +241,34 @@ int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end);
  * FD_ERR_LAUNCH.
  */
 int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, hipStream_t stream);
+
+/*
+ * fd_check_inputs -- debug validation of the device-side contract of fd_decode_attention(_mq)
+ * and fd_kv_append: the values a step reads from device memory to locate KV rows, checked
+ * against the sizes the caller states.  The step itself never checks them: it would need a host
+ * synchronisation per step (15.17); call this while debugging, or in tests.  Paged addressing
+ * as in 15.26 (token t of sequence b: block_table[b * max_blocks_per_seq + t / block_size]).
+ *
+ *   seq_len, block_table, max_blocks_per_seq, kv_start, batch, max_seq_len, block_size
+ *                exactly as for fd_decode_attention (one of block_table / kv_start is NULL).
+ *   extent       number of physical blocks of the cache (paged) or rows (contiguous).
+ *   result       device int32[4], written (not read first):
+ *                [0] number of sequences that violate the contract,
+ *                [1] the lowest such sequence, or -1 when there is none,
+ *                [2] what is wrong with it: 0 nothing, 1 seq_len outside [0, max_seq_len],
+ *                    2 a used block-table entry (logical block < ceil(seq_len / block_size))
+ *                    outside [0, extent) -- [3] then holds the lowest such entry's value,
+ *                    3 kv_start[b] < 0 or kv_start[b] + seq_len[b] > extent,
+ *                [3] the offending value (seq_len, table entry or kv_start).
+ * Unused table entries are not read.  Asynchronous on `stream` (three small launches, no memset,
+ * no allocation); the caller synchronises before reading `result`.  Host-checked errors as for
+ * fd_decode_attention (null seq_len / result, batch <= 0, max_seq_len < 0, extent < 0, both or
+ * neither of block_table / kv_start, paged max_seq_len above the table, block_size not
+ * 16/32/64); FD_ERR_LAUNCH if a launch fails.
+ */
+int fd_check_inputs(const int32_t *seq_len, const int32_t *block_table, int max_blocks_per_seq,
+                    const int32_t *kv_start, int batch, int max_seq_len, int block_size,
+                    int64_t extent, int32_t *result, hipStream_t stream);
 
 /* fd_status_string -- static, NUL-terminated name of a status code (never NULL). */
 const char *fd_status_string(int status);

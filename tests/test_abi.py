@@ -232,3 +232,37 @@ def test_window_workspace_grows_with_the_columns():
     four = fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3", num_query=4)
     assert four >= one
     assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3", num_query=2) == 2048 // 8
+
+
+# ------------------------------------------------------------------ fd_check_inputs (debug validation)
+def good_check_args(**kw):
+    a = dict(seq_len=0x5000, block_table=0x4000, max_blocks_per_seq=32, kv_start=None, batch=2,
+             max_seq_len=2000, block_size=64, extent=100, result=0x9000, stream=None)
+    a.update(kw)
+    return a
+
+
+BAD_CHECK = [
+    (dict(seq_len=None), fd.FD_ERR_INVALID_ARG),
+    (dict(result=None), fd.FD_ERR_INVALID_ARG),
+    (dict(batch=0), fd.FD_ERR_INVALID_ARG),
+    (dict(max_seq_len=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(extent=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(kv_start=0x7000), fd.FD_ERR_INVALID_ARG),         # both table and kv_start
+    (dict(block_table=None), fd.FD_ERR_INVALID_ARG),        # neither
+    (dict(max_blocks_per_seq=0), fd.FD_ERR_INVALID_ARG),
+    (dict(max_seq_len=2049), fd.FD_ERR_INVALID_ARG),        # beyond the table row
+    (dict(block_size=8, max_blocks_per_seq=256), fd.FD_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("change,expect", BAD_CHECK, ids=[str(sorted(c)) for c, _ in BAD_CHECK])
+def test_check_inputs_bad_arguments_rejected_before_launch(change, expect):
+    assert fd.check_inputs_raw(**good_check_args(**change)) == expect
+
+
+@pytest.mark.parametrize("change", [dict(), dict(block_table=None, kv_start=0x7000, block_size=0),
+                                    dict(block_size=16, max_blocks_per_seq=125)])
+def test_check_inputs_accepted_up_to_the_launch(change):
+    # without a GPU the launch itself fails: the host checks passed
+    assert fd.check_inputs_raw(**good_check_args(**change)) == fd.FD_ERR_LAUNCH
