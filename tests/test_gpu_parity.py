@@ -246,6 +246,27 @@ def test_combine_many_pieces_per_row(parts):
     check_case(f"many_pieces/p{parts}", case, num_partitions=parts)
 
 
+def test_wide_kernel_batch_beyond_lds_prefix_table():
+    # more sequences (300) than the wide kernel keeps tile prefix sums for in LDS (256): tiles are
+    # located by wave scans of seq_len instead, in the partition kernel and the combine
+    lens = [int(x) for x in np.random.default_rng(7).integers(0, 200, size=300)]
+    lens[5], lens[0], lens[299] = 0, 1, 1000
+    case = workloads.custom_case(seed=7, device="cuda", batch=300, hq=64, hkv=1, d=128, seq_lens=lens,
+                                 kv="fp8_e4m3", q="bf16", scale="tensor", block_size=64)
+    for parts in (0, 97):
+        check_case(f"wide_batch300/p{parts}", case, num_partitions=parts)
+
+
+def test_partition_kernel_batch_beyond_lds_prefix_table():
+    # 4100 sequences: past the 4096 the 16-head kernel keeps in LDS
+    lens = [int(x) for x in np.random.default_rng(8).integers(0, 40, size=4100)]
+    lens[4099] = 300
+    case = workloads.custom_case(seed=8, device="cuda", batch=4100, hq=4, hkv=1, d=64, seq_lens=lens,
+                                 kv="f16", q="f16", scale="none", block_size=32)
+    for parts in (0, 333):
+        check_case(f"batch4100/p{parts}", case, num_partitions=parts)
+
+
 def test_peaky_scores():
     case = workloads.custom_case(seed=10, device="cuda", batch=2, hq=16, hkv=2, d=128,
                                  seq_lens=[3000, 700], kv="fp8_e4m3", q="bf16", scale="token_head",
