@@ -6,10 +6,11 @@
 The last four override the named workload (page-size / length / layout sweeps); the default run
 uses none of them.
 
-Prints ONE JSON line.  A step is one fd_decode_attention call (split-KV partition kernel +
-combine kernel) over one batch of synthetic, seeded inputs already resident in HBM.  Each step
-reads a different copy of the KV cache (the copies are rotated) so no step is served from the
-256 MB Infinity Cache left warm by the previous one.
+Prints ONE JSON line. After W warmup steps, untimed steps continue for --settle-ms (200 ms) so
+that the GPU clocks have ramped (reported as `settle`). A step is one fd_decode_attention call
+(split-KV partition kernel + combine kernel) over one batch of synthetic, seeded inputs already
+resident in HBM. Each step reads a different copy of the KV cache (the copies are rotated) so no
+step is served from the 256 MB Infinity Cache left warm by the previous one.
 
 value           = KV-read bytes (K + V payload + scales) per step / mean step time, in GB/s.
 roofline        = the partition kernel: the same algorithmic bytes / its mean duration from
@@ -241,6 +242,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps after the warmup until the GPU has been busy this long")
     ap.add_argument("--workload", default="fp8_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--num-partitions", type=int, default=0)
@@ -311,7 +314,17 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+    # clock settle: after idle the GPU's clocks take ~10 ms of load to ramp (steps run up to 10 %
+    # slower meanwhile), so untimed steps continue until the GPU has been busy for settle_ms;
+    # the timed steps then see steady-state decode, as a serving loop does
     torch.cuda.synchronize()
+    settle_steps, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step(args.warmup + settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t0) * 1e3
 
     # ---- timed region: exactly K steps, back to back
     t_start = torch.cuda.Event(enable_timing=True)
@@ -360,6 +373,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
+                   "what": "untimed steps after the warmup until the clocks reach steady state"},
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
