@@ -95,16 +95,17 @@ def compute_note(case) -> str:
     return qk + ", f32 softmax and accumulate"
 
 
-def measured_traffic(workload: str, overridden: bool = False):
+def measured_traffic(workload: str, partitions: int, overridden: bool = False):
     """HBM traffic per partition launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source and the workload as defined; else None."""
+    taken on the current device code, with the same partition count, on the workload as
+    defined; else None."""
     if overridden:
         return None
     path = os.path.join(ROOT, "profiles", f"traffic_partition_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_src_sha256_16") != kernel_hash():
+    if rec.get("kernel_src_sha256_16") != kernel_hash() or rec.get("partitions") != partitions:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -402,7 +403,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k_achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload, bool(overrides or seq_lens)),
+            "traffic": measured_traffic(args.workload, nparts, bool(overrides or seq_lens)),
             "kernel_us_mean": round(kmean_ms * 1e3, 2),
             "kernel_us_p10_p90": [round(float(np.percentile(kdur_ms, 10)) * 1e3, 2),
                                   round(float(np.percentile(kdur_ms, 90)) * 1e3, 2)],

@@ -100,10 +100,11 @@ typedef enum {
  *   workspace    device scratch of at least fd_workspace_bytes(...) bytes, 256-byte aligned.
  *                Contents need no initialisation and are clobbered; one workspace must not be
  *                shared by calls that may overlap.
- *   num_partitions  0 = automatic (one partition workgroup per `wpg` resident waves: 2048 waves,
- *                8 per CU on 256 CUs, or 3072 for the wide-group kernel that E4M3 KV with
- *                head_dim 128 and a multiple of 64 query heads per kv head uses); > 0 forces
- *                that many (testing and tuning).  Capped by the number of tiles the sizes allow.
+ *   num_partitions  0 = automatic (one partition workgroup per `wpg` of 2048 resident waves,
+ *                8 per CU on 256 CUs, for the 16-head kernel and for the wide-group kernel that
+ *                E4M3 KV with head_dim 128 and a multiple of 64 query heads per kv head uses);
+ *                > 0 forces that many (testing and tuning).  Capped by the number of tiles the
+ *                sizes allow.
  *   stream       HIP stream to enqueue on (0 = null stream).
  *
  * Device-side contract (not checked by the step; violating it is undefined; fd_check_inputs
