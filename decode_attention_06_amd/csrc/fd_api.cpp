@@ -84,12 +84,13 @@ Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, i
     return pl;
 }
 
-// Workspace: [ml slots][acc slots]; one slot pair per partition per unit of a group per head.
+// Workspace: [ml slots][row-scale slots][acc slots]; one slot pair per partition per unit of a
+// group per head.  Acc rows are fp32 (f16 and bf16 KV) or f16 (quantised KV: half the bytes).
 size_t ws_slots(const Plan &pl) { return (size_t)pl.nparts * 2 * pl.wpg * pl.hb; }
 
 size_t ws_bytes(const Plan &pl, int head_dim) {
     const size_t slots = ws_slots(pl);
-    return align256(slots * sizeof(float) * 2) + slots * head_dim * sizeof(float);
+    return align256(slots * sizeof(float) * 2) + align256(slots * sizeof(float)) + slots * head_dim * sizeof(float);
 }
 
 }  // namespace
@@ -229,11 +230,15 @@ int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, co
     p.groups = pl.groups;
     p.nparts = pl.nparts;
     p.out_dtype = out_dtype;
+    // quantised KV (parity bar 5e-3 / 3e-3) keeps its partial outputs in 16 bits: f16 of the value
+    // over its row's largest magnitude, relative rounding 2^-12 of that magnitude per piece
+    p.part16 = (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) ? 1 : 0;
     p.qk_scale = (float)((double)softmax_scale * 1.4426950408889634074);  // log2(e)
     {
         const size_t slots = ws_slots(pl);
         p.ws_ml = (float2 *)workspace;
-        p.ws_acc = (float *)((char *)workspace + align256(slots * sizeof(float) * 2));
+        p.ws_sc = (float *)((char *)workspace + align256(slots * sizeof(float) * 2));
+        p.ws_acc = (float *)((char *)p.ws_sc + align256(slots * sizeof(float)));
     }
 
     if (t_prof_begin) (void)hipEventRecord(t_prof_begin, stream);

@@ -28,8 +28,10 @@ struct Params {
     const float *v_scale;
     void *out;
     float *lse;
-    float *ws_acc;   // [nparts][2][wpg][hb][d]  unnormalised partial outputs
+    float *ws_acc;   // [nparts][2][wpg][hb][d]  unnormalised partial outputs (fp32, or f16 when part16)
     float2 *ws_ml;   // [nparts][2][wpg][hb]     (running max in log2 units, running sum)
+    float *ws_sc;    // [nparts][2][wpg][hb]     part16: the row's largest |value|, which divides it
+    int part16;      // partial outputs stored as f16 of value / row max (quantised KV), else fp32
     int batch, hq, hkv, d;
     int block_size, max_blocks;
     int max_seq_len;  // host bound; seq_len values above it are clamped (never read past it)

@@ -192,6 +192,8 @@ void partition_kernel(Params p) {
     // converted to f16 once per segment)
     constexpr int QM = (KVT == KV_I8) ? KV_F16 : QT;
     constexpr bool QCVT = (KVT == KV_I8 && QT == KV_BF16);
+    // quantised KV: partial outputs in 16 bits (the host sets Params::part16 by the same rule)
+    constexpr bool PART16 = (KVT == KV_FP8 || KVT == KV_I8);
     __shared__ float sh_scale_all[kMaxWavesPerGroup][64];
     __shared__ int sh_prefix[kLdsBatch + 1];  // tiles of the sequences before b (b <= batch)
 
@@ -589,18 +591,46 @@ void partition_kernel(Params p) {
                 }
                 if (p.lse && g == 0) p.lse[orow_idx] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
             }
-        } else if (hvalid) {
+        } else {
             // slot 0: the range's first segment; slot 1: its last (a middle one is always whole)
             const size_t slot = (((size_t)wg * 2 + (d.seg == 0 ? 0 : 1)) * p.wpg + wave) * kHeadBlock + c;
-            float *dst = p.ws_acc + slot * D;
+            if constexpr (PART16) {
+                // f16 of value / (largest |value| of the head's row): the row spans the four lane
+                // groups of column c (every lane joins the shuffles)
+                float mx = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
+                for (int r = 0; r < 4; r++)
 #pragma unroll
-                for (int dt = 0; dt < DT; dt += 4)
-                    *(float4 *)(dst + DT * (4 * g + r) + dt) =
-                        make_float4(o[dt][r], o[dt + 1][r], o[dt + 2][r], o[dt + 3][r]);
+                    for (int dt = 0; dt < DT; dt++) mx = fmaxf(mx, fabsf(o[dt][r]));
+                mx = fmaxf(mx, shfl_xor_f(mx, 16));
+                mx = fmaxf(mx, shfl_xor_f(mx, 32));
+                if (hvalid) {
+                    const float sc = mx > 0.0f ? mx : 1.0f, inv = 1.0f / sc;
+                    uint16_t *dst = (uint16_t *)p.ws_acc + slot * D;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+#pragma unroll
+                        for (int dt = 0; dt < DT; dt += 4)
+                            *(u32x2_t *)(dst + DT * (4 * g + r) + dt) =
+                                u32x2_t{pack_f16(o[dt][r] * inv, o[dt + 1][r] * inv),
+                                        pack_f16(o[dt + 2][r] * inv, o[dt + 3][r] * inv)};
+                    }
+                    if (g == 0) {
+                        p.ws_ml[slot] = make_float2(m_run, l_tot);
+                        p.ws_sc[slot] = sc;
+                    }
+                }
+            } else if (hvalid) {
+                float *dst = p.ws_acc + slot * D;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt += 4)
+                        *(float4 *)(dst + DT * (4 * g + r) + dt) =
+                            make_float4(o[dt][r], o[dt + 1][r], o[dt + 2][r], o[dt + 3][r]);
+                }
+                if (g == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
             }
-            if (g == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
         }
     };
 
@@ -761,9 +791,27 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
         for (int u = 0; u < 4; u++) {
             const size_t slot = slot_of(min(i0 + gstride * u, np - 1));
             ml[u] = p.ws_ml[slot];
-            const float *src = p.ws_acc + slot * D + PER * k;
+            if (p.part16) {  // f16 of value / row scale
+                const float sc = p.ws_sc[slot];
+                const uint16_t *src = (const uint16_t *)p.ws_acc + slot * D + PER * k;
 #pragma unroll
-            for (int e = 0; e < PER / 4; e++) x[u][e] = *(const float4 *)(src + 4 * e);
+                for (int e = 0; e < PER / 8; e++) {
+                    const u32x4_t w = *(const u32x4_t *)(src + 8 * e);
+                    float f[8];
+#pragma unroll
+                    for (int h = 0; h < 4; h++) {
+                        const uint32_t wh = w[h];
+                        f[2 * h] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wh & 0xFFFFu)) * sc;
+                        f[2 * h + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wh >> 16)) * sc;
+                    }
+                    x[u][2 * e] = make_float4(f[0], f[1], f[2], f[3]);
+                    x[u][2 * e + 1] = make_float4(f[4], f[5], f[6], f[7]);
+                }
+            } else {
+                const float *src = p.ws_acc + slot * D + PER * k;
+#pragma unroll
+                for (int e = 0; e < PER / 4; e++) x[u][e] = *(const float4 *)(src + 4 * e);
+            }
         }
 #pragma unroll
         for (int u = 0; u < 4; u++) {

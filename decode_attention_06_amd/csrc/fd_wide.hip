@@ -435,15 +435,27 @@ void wide_partition_kernel(Params p) {
             }
             if (p.lse && lh == 0) p.lse[(size_t)k.b * p.hq + head] = (m_run + log2f(l_tot)) * kLn2;
         } else {
-            // slot 0: the range's first segment; slot 1: its last (a middle one is always whole)
+            // slot 0: the range's first segment; slot 1: its last (a middle one is always whole).
+            // E4M3 KV: f16 of value / (largest |value| of the head's row, spread over the two lane
+            // halves), the scale beside it
             const size_t slot = (((size_t)wg * 2 + (seg == 0 ? 0 : 1)) * WPG + wave) * kWideHeadBlock + li;
-            float *dst = p.ws_acc + slot * D;
             const float sv = (SCALE == SC_TENSOR) ? tensor_v : 1.0f;
+            float mx = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r++)
-                *(float4 *)(dst + 4 * (8 * (r >> 2) + 4 * lh + (r & 3))) =
-                    make_float4(acc[0][r] * sv, acc[1][r] * sv, acc[2][r] * sv, acc[3][r] * sv);
-            if (lh == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) mx = fmaxf(mx, fabsf(acc[dt][r] * sv));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            const float sc = mx > 0.0f ? mx : 1.0f, inv = sv / sc;
+            uint16_t *dst = (uint16_t *)p.ws_acc + slot * D;
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                *(u32x2_t *)(dst + 4 * (8 * (r >> 2) + 4 * lh + (r & 3))) =
+                    u32x2_t{pack_f16(acc[0][r] * inv, acc[1][r] * inv), pack_f16(acc[2][r] * inv, acc[3][r] * inv)};
+            if (lh == 0) {
+                p.ws_ml[slot] = make_float2(m_run, l_tot);
+                p.ws_sc[slot] = sc;
+            }
         }
     };
 
