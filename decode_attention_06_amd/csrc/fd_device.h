@@ -30,6 +30,8 @@ constexpr float kRescaleSlack = 8.0f;
 // Largest finite float: m = max(m_run, -kMaxFloat) keeps exp2 of (score - m) at 0, not NaN, while a
 // column has seen no token (m_run = -inf).
 constexpr float kMaxFloat = 3.40282347e38f;
+// Smallest normal float: the floor of a 16-bit partial row's scale (its reciprocal is finite).
+constexpr float kMinNormal = 1.17549435e-38f;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 // ---------------------------------------------------------------- small helpers

@@ -605,7 +605,8 @@ void partition_kernel(Params p) {
                 mx = fmaxf(mx, shfl_xor_f(mx, 16));
                 mx = fmaxf(mx, shfl_xor_f(mx, 32));
                 if (hvalid) {
-                    const float sc = mx > 0.0f ? mx : 1.0f, inv = 1.0f / sc;
+                    // at least the smallest normal float: its reciprocal stays finite
+                    const float sc = fmaxf(mx, kMinNormal), inv = 1.0f / sc;
                     uint16_t *dst = (uint16_t *)p.ws_acc + slot * D;
 #pragma unroll
                     for (int r = 0; r < 4; r++) {

@@ -446,12 +446,14 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) mx = fmaxf(mx, fabsf(acc[dt][r] * sv));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            const float sc = mx > 0.0f ? mx : 1.0f, inv = sv / sc;
+            // at least the smallest normal float: its reciprocal stays finite
+            const float sc = fmaxf(mx, kMinNormal), inv = 1.0f / sc;
             uint16_t *dst = (uint16_t *)p.ws_acc + slot * D;
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 *(u32x2_t *)(dst + 4 * (8 * (r >> 2) + 4 * lh + (r & 3))) =
-                    u32x2_t{pack_f16(acc[0][r] * inv, acc[1][r] * inv), pack_f16(acc[2][r] * inv, acc[3][r] * inv)};
+                    u32x2_t{pack_f16(acc[0][r] * sv * inv, acc[1][r] * sv * inv),
+                            pack_f16(acc[2][r] * sv * inv, acc[3][r] * sv * inv)};
             if (lh == 0) {
                 p.ws_ml[slot] = make_float2(m_run, l_tot);
                 p.ws_sc[slot] = sc;
