@@ -181,6 +181,12 @@ void wide_partition_kernel(Params p) {
         tensor_v = p.v_scale[0];
     }
     const float qk_scale = p.qk_scale * tensor_k;
+    // floor of a 16-bit partial row's scale sc: sv / sc stays finite for any v scale sv (rows of
+    // denormal magnitude), and the stored values acc * sv / sc still lie in [-1, 1]
+    // (wave-uniform: kept in a scalar register for the whole kernel)
+    const float sc_floor = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                   uint32_t, fmaxf(fabsf(SCALE == SC_TENSOR ? tensor_v : 1.0f) * kMinNormal, kMinNormal))));
     const uint32_t row_bytes = (uint32_t)p.hkv * D;  // bytes per cache row (all kv heads)
 
     // ---- tile cursors: one issuing copies NSLOT-1 tiles ahead, one computing
@@ -446,14 +452,12 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) mx = fmaxf(mx, fabsf(acc[dt][r] * sv));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            // at least the smallest normal float: its reciprocal stays finite
-            const float sc = fmaxf(mx, kMinNormal), inv = 1.0f / sc;
+            const float sc = fmaxf(mx, sc_floor), inv = sv / sc;
             uint16_t *dst = (uint16_t *)p.ws_acc + slot * D;
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 *(u32x2_t *)(dst + 4 * (8 * (r >> 2) + 4 * lh + (r & 3))) =
-                    u32x2_t{pack_f16(acc[0][r] * sv * inv, acc[1][r] * sv * inv),
-                            pack_f16(acc[2][r] * sv * inv, acc[3][r] * sv * inv)};
+                    u32x2_t{pack_f16(acc[0][r] * inv, acc[1][r] * inv), pack_f16(acc[2][r] * inv, acc[3][r] * inv)};
             if (lh == 0) {
                 p.ws_ml[slot] = make_float2(m_run, l_tot);
                 p.ws_sc[slot] = sc;
