@@ -267,6 +267,21 @@ def test_partition_kernel_batch_beyond_lds_prefix_table():
         check_case(f"batch4100/p{parts}", case, num_partitions=parts)
 
 
+@pytest.mark.parametrize("k_mult,v_mult", [(-1.0, 1.0), (-1.0, -1.0), (0.0, 1.0)])
+@pytest.mark.parametrize("hq", [16, 128])
+def test_per_tensor_scale_signs(k_mult, v_mult, hq):
+    # negative or zero per-tensor scales (hq 128: the wide kernel, which scales scores inside the
+    # exponent and flips q's sign for a negative scale; hq 16: the 16-head kernel).  A zero k
+    # scale makes every score 0: out is the plain mean of the dequantised V rows
+    case = workloads.custom_case(seed=31, device="cuda", batch=2, hq=hq, hkv=1, d=128,
+                                 seq_lens=[3000, 77], kv="fp8_e4m3", q="bf16", scale="tensor",
+                                 block_size=64)
+    case.k_scale = case.k_scale * k_mult
+    case.v_scale = case.v_scale * v_mult
+    for parts in (0, 7):
+        check_case(f"scale_signs k{k_mult} v{v_mult} hq{hq}/p{parts}", case, num_partitions=parts)
+
+
 def test_peaky_scores():
     case = workloads.custom_case(seed=10, device="cuda", batch=2, hq=16, hkv=2, d=128,
                                  seq_lens=[3000, 700], kv="fp8_e4m3", q="bf16", scale="token_head",
