@@ -129,9 +129,11 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
 
 /*
  * fd_workspace_bytes -- workspace size fd_decode_attention needs for these sizes (partial
- * states: 2 slots x 16 (wide-group kernel: 32) heads x (head_dim + 2) fp32 per partition and
- * unit of a group).  The same arguments must be passed to fd_decode_attention.  Returns
- * (size_t)-1 for arguments fd_decode_attention would reject as invalid.
+ * states: 2 slots x 16 (wide-group kernel: 32) heads x (head_dim + 3) fp32 per partition and
+ * unit of a group -- max, sum, a row scale and the accumulator row; with E4M3 / INT8 KV the
+ * accumulator rows are stored as f16 of value / row scale in the first half of their space).
+ * The same arguments must be passed to fd_decode_attention.  Returns (size_t)-1 for arguments
+ * fd_decode_attention would reject as invalid.
  */
 size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                           int max_seq_len, int block_size, int kv_dtype, int num_partitions);
