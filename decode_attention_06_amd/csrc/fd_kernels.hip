@@ -194,7 +194,7 @@ void partition_kernel(Params p) {
     constexpr bool QCVT = (KVT == KV_I8 && QT == KV_BF16);
     // quantised KV: partial outputs in 16 bits (the host sets Params::part16 by the same rule)
     constexpr bool PART16 = (KVT == KV_FP8 || KVT == KV_I8);
-    __shared__ float sh_scale_all[kMaxWavesPerGroup][64];
+    __shared__ __attribute__((aligned(16))) float sh_scale_all[kMaxWavesPerGroup][64];
     __shared__ int sh_prefix[kLdsBatch + 1];  // tiles of the sequences before b (b <= batch)
 
     const int wave = uni((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;  // wave index kept scalar
@@ -707,7 +707,8 @@ void partition_kernel(Params p) {
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
     constexpr int PER = D / 8;  // output elements per lane
-    __shared__ float sh_state[NW > 1 ? NW : 1][D + 2];
+    // per-wave merged state: D outputs, then m and l; rows padded to a 16-byte multiple
+    __shared__ __attribute__((aligned(16))) float sh_state[NW > 1 ? NW : 1][D + 4];
     const int mq = blockIdx.x / p.hq, h = blockIdx.x % p.hq, b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = NW > 1 ? uni((int)(threadIdx.x >> 6)) : 0;
     const int j = lane >> 3, k = lane & 7;
