@@ -13,7 +13,7 @@ import threading
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfd.so")
 
-FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_LAUNCH = 0, 1, 2, 3, 4
+FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_LAUNCH, FD_ERR_CONTRACT = 0, 1, 2, 3, 4, 5
 FD_F32, FD_F16, FD_BF16, FD_FP8_E4M3, FD_INT8 = 0, 1, 2, 3, 4
 FD_SCALE_NONE, FD_SCALE_PER_TENSOR, FD_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 

@@ -3,6 +3,7 @@
 // Nothing here reads device memory or synchronises (no per-step host sync, as the ch.15
 // profiling page's section 15.17 asks; no allocation on the hot path, section 15.22).
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -88,9 +89,19 @@ Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, i
 // group per head.  Acc rows are fp32 (f16 and bf16 KV) or f16 (quantised KV: half the bytes).
 size_t ws_slots(const Plan &pl) { return (size_t)pl.nparts * 2 * pl.wpg * pl.hb; }
 
+// The last kCheckBytes hold the debug-mode validator's result (FD_CHECK=1).
+constexpr size_t kCheckBytes = 256;
+
 size_t ws_bytes(const Plan &pl, int head_dim) {
     const size_t slots = ws_slots(pl);
-    return align256(slots * sizeof(float) * 2) + align256(slots * sizeof(float)) + slots * head_dim * sizeof(float);
+    return align256(slots * sizeof(float) * 2) + align256(slots * sizeof(float)) +
+           align256(slots * head_dim * sizeof(float)) + kCheckBytes;
+}
+
+// Debug mode: FD_CHECK=1 in the environment, read on every call (no cached state).
+bool debug_check_enabled() {
+    const char *v = getenv("FD_CHECK");
+    return v && v[0] == '1' && v[1] == 0;
 }
 
 }  // namespace
@@ -125,6 +136,7 @@ const char *fd_status_string(int status) {
     case FD_ERR_UNSUPPORTED: return "FD_ERR_UNSUPPORTED";
     case FD_ERR_WORKSPACE: return "FD_ERR_WORKSPACE";
     case FD_ERR_LAUNCH: return "FD_ERR_LAUNCH";
+    case FD_ERR_CONTRACT: return "FD_ERR_CONTRACT";
     default: return "FD_UNKNOWN_STATUS";
     }
 }
@@ -201,6 +213,20 @@ int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, co
     const size_t need = ws_bytes(pl, head_dim);
     if (!workspace || workspace_bytes < need) return FD_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255) return FD_ERR_WORKSPACE;
+
+    if (debug_check_enabled()) {
+        // validate the device-side contract first: result in the workspace's last 256 bytes,
+        // then a synchronous read of it (debug mode only)
+        int32_t *res = (int32_t *)((char *)workspace + need - kCheckBytes);
+        if (fd::launch_check(seq_len, block_table, max_blocks_per_seq, kv_start, batch, max_seq_len,
+                             block_table ? block_size : 0, (int64_t)INT64_MAX, res, stream) != hipSuccess)
+            return FD_ERR_LAUNCH;
+        int32_t host[4];
+        if (hipMemcpyAsync(host, res, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return FD_ERR_LAUNCH;
+        if (host[0] != 0) return FD_ERR_CONTRACT;
+    }
 
     fd::Params p;
     memset(&p, 0, sizeof(p));

@@ -46,7 +46,8 @@ typedef enum {
     FD_ERR_INVALID_ARG = 1, /* null pointer, bad count, inconsistent dtype / scale mode      */
     FD_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, block_size not 16/32/64, dtype combination */
     FD_ERR_WORKSPACE = 3,   /* workspace missing, too small or not 256-byte aligned           */
-    FD_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch                        */
+    FD_ERR_LAUNCH = 4,      /* the HIP runtime refused a kernel launch                        */
+    FD_ERR_CONTRACT = 5     /* debug mode (FD_CHECK=1) found the device-side contract broken  */
 } fd_status;
 
 typedef enum {
@@ -110,7 +111,14 @@ typedef enum {
  * Device-side contract (not checked by the step; violating it is undefined; fd_check_inputs
  * validates it for debugging): seq_len[b] <= max_seq_len, block_table entries for logical
  * blocks < ceil(seq_len[b] / block_size) are valid block ids, kv_start[b] + seq_len[b] rows
- * exist.  The kernels read only those entries and rows, so
+ * exist.
+ *
+ * Debug mode: with the environment variable FD_CHECK=1 (read on every call), the call first runs
+ * the fd_check_inputs pass on `stream` (its result in the last 256 bytes of the workspace, which
+ * fd_workspace_bytes includes), synchronises the stream and, if the contract is broken, returns
+ * FD_ERR_CONTRACT without launching the step.  The cache's block count is not an argument here,
+ * so table entries are checked for >= 0 only (contiguous mode: kv_start >= 0).  Synchronising,
+ * so not for graph capture; off by default.  The kernels read only those entries and rows, so
  * unused table entries and unused slots of a last block may hold anything.
  *
  * Returns FD_OK or an fd_status.

@@ -41,6 +41,7 @@ def test_version_and_status_strings():
     assert fd.version() == 1
     assert fd.status_string(0) == "FD_OK"
     assert fd.status_string(3) == "FD_ERR_WORKSPACE"
+    assert fd.status_string(5) == "FD_ERR_CONTRACT"
     assert fd.status_string(99) == "FD_UNKNOWN_STATUS"
 
 

@@ -107,3 +107,33 @@ def test_result_rewritten_on_every_call():
     assert check(case, seq_len=sl, result=res)["violations"] == 1
     # the same buffer again: the previous verdict is overwritten, not accumulated
     assert check(case, result=res) == {"violations": 0, "first_sequence": -1, "kind": "none", "value": 0}
+
+
+def test_debug_mode_rejects_a_broken_contract_before_launching(monkeypatch):
+    # FD_CHECK=1: the step validates first, synchronises, and refuses a broken contract with
+    # FD_ERR_CONTRACT without launching.  The first broken input (seq_len past max_seq_len) is one
+    # the kernels would clamp safely anyway: it proves the mode is on before the second one (a -1
+    # table entry in a used position, never safe to launch on) is handed over.
+    case = paged_case()
+    out_plain = fd.decode_case(case).clone()
+    monkeypatch.setenv("FD_CHECK", "1")
+    out_checked = fd.decode_case(case)
+    torch.cuda.synchronize()
+    assert torch.equal(out_plain, out_checked)   # a valid step is unchanged
+    sl = case.seq_len.clone()
+    sl[2] = case.max_seq_len + 1
+    good_sl = case.seq_len
+    case.seq_len = sl
+    with pytest.raises(fd.FdError) as e:
+        fd.decode_case(case)
+    assert e.value.status == fd.FD_ERR_CONTRACT
+    case.seq_len = good_sl
+    t = case.block_table.clone()
+    t[0, 3] = -1                                 # used by the 700-token sequence
+    good_t = case.block_table
+    case.block_table = t
+    with pytest.raises(fd.FdError) as e:
+        fd.decode_case(case)
+    assert e.value.status == fd.FD_ERR_CONTRACT
+    case.block_table = good_t
+    assert torch.equal(fd.decode_case(case), out_plain)
