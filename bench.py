@@ -12,7 +12,8 @@ that the GPU clocks have ramped (reported as `settle`). A step is one fd_decode_
 resident in HBM. Each step reads a different copy of the KV cache (the copies are rotated) so no
 step is served from the 256 MB Infinity Cache left warm by the previous one.
 
-value           = KV-read bytes (K + V payload + scales) per step / mean step time, in GB/s.
+value           = KV-read bytes (K + V payload + scales) per step / mean step time, in GB/s;
+                  step_us_p10_p50_p90 = the spread of single steps timed with events each.
 roofline        = the partition kernel: the same algorithmic bytes / its mean duration from
                   HIP events recorded around it on its stream, against 8 TB/s HBM peak; traffic =
                   HBM bytes per launch from committed rocprofv3 counter runs of the same sources.
@@ -364,6 +365,15 @@ def main():
     torch.cuda.synchronize()
     kdur_ms = [a.elapsed_time(b) for a, b in evs]
     kmean_ms = float(np.mean(kdur_ms))
+
+    # ---- each step on its own: events around every whole step (partition + combine); the events
+    # leave gaps between steps, so this gives the spread, not `value`
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    sdur_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
     k_achieved = kv_bytes / (kmean_ms * 1e-3) / 1e9
 
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -378,6 +388,7 @@ def main():
                    "what": "untimed steps after the warmup until the clocks reach steady state"},
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_us_p10_p50_p90": [round(float(np.percentile(sdur_us, q)), 2) for q in (10, 50, 90)],
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
