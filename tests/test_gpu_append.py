@@ -5,6 +5,8 @@ byte results decided in fp32, the same precision on both sides.  Every byte of t
 every scale is compared (rows not appended must be left untouched).  An end-to-end case appends
 a token to every sequence of a decode batch and runs the attention over the grown sequences.
 """
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -104,7 +106,33 @@ APPEND_CASES = [
 
 @pytest.mark.parametrize("name,kw", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
 def test_kv_append_bitwise_equals_oracle(name, kw):
-    c = _append_case(7, **kw)
+    _check_append(name, kw, 7)
+
+
+def _random_append_configs(n, seed):
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        kv = rng.choice(["fp8_e4m3", "int8", "f16", "bf16"])
+        paged = rng.random() < 0.75
+        out.append(dict(batch=rng.randint(1, 12), hkv=rng.choice([1, 2, 3, 4, 8]), d=rng.choice([64, 128]), kv=kv,
+                        scale="none" if kv in ("f16", "bf16") else rng.choice(["tensor", "token_head"]),
+                        new=rng.choice(["f32", "f16", "bf16"]), paged=paged,
+                        bs=rng.choice([16, 32, 64]) if paged else 64))
+    return out
+
+
+RANDOM_APPEND = _random_append_configs(60, 20261203)
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM_APPEND)))
+def test_kv_append_random_configs_bitwise(idx):
+    # seeded random (cache dtype, scale mode, input dtype, head_dim, kv heads, batch, paging)
+    _check_append(f"random{idx} {RANDOM_APPEND[idx]}", RANDOM_APPEND[idx], 100 + idx)
+
+
+def _check_append(name, kw, seed):
+    c = _append_case(seed, **kw)
     print(f"[{name}] pos={c['pos'].tolist()}", flush=True)
     want_k, want_v, want_ks, want_vs = oracle.kv_append(
         k_new=c["k_new"], v_new=c["v_new"], k_cache=c["k"], v_cache=c["v"], pos=c["pos"],
