@@ -141,6 +141,77 @@ def _require_cuda(**tensors):
             raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
 
 
+def _cache_dtypes(kv_dtype):
+    import torch
+
+    return {"f16": (torch.float16,), "bf16": (torch.bfloat16,),
+            "fp8_e4m3": (torch.uint8, torch.float8_e4m3fn), "int8": (torch.int8,)}[kv_dtype]
+
+
+def _int32_vector(name, t, n):
+    import torch
+
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous int32 tensor of {n} elements "
+                         f"(got {t.dtype}, {tuple(t.shape)}, contiguous={t.is_contiguous()})")
+
+
+def check_decode_args(q, k_cache, v_cache, seq_len, *, block_table, kv_start, kv_dtype, scale_mode,
+                      k_scale, v_scale, num_kv_heads, block_size, max_seq_len):
+    """Host-side checks of what the kernels assume of the tensors but the C ABI (plain pointers)
+    cannot see: dtypes, contiguity, shapes and element counts.  Raises ValueError; launches
+    nothing and needs no GPU (the tensors may live anywhere)."""
+    import torch
+
+    if kv_dtype not in DTYPE_CODES or kv_dtype == "f32":
+        raise ValueError(f"kv_dtype must be one of f16, bf16, fp8_e4m3, int8 (got {kv_dtype!r})")
+    if scale_mode not in SCALE_CODES:
+        raise ValueError(f"scale_mode must be one of {tuple(SCALE_CODES)} (got {scale_mode!r})")
+    if q.dtype not in (torch.float16, torch.bfloat16) or not q.is_contiguous() or q.dim() not in (3, 4):
+        raise ValueError(f"q must be a contiguous f16/bf16 tensor [batch][heads][head_dim] or "
+                         f"[batch][num_query][heads][head_dim] (got {q.dtype}, {tuple(q.shape)})")
+    batch, d = q.shape[0], q.shape[-1]
+    hkv = num_kv_heads if num_kv_heads is not None else k_cache.shape[-2]
+    if (block_table is None) == (kv_start is None):
+        raise ValueError("give exactly one of block_table (paged cache) and kv_start (contiguous cache)")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in _cache_dtypes(kv_dtype):
+            raise ValueError(f"{name} dtype {t.dtype} does not hold kv_dtype {kv_dtype!r}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        want = 4 if block_table is not None else 3
+        if t.dim() != want or t.shape[-1] != d or t.shape[-2] != hkv:
+            raise ValueError(f"{name} must be [{'num_blocks][block_size' if want == 4 else 'rows'}]"
+                             f"[{hkv}][{d}] (got {tuple(t.shape)})")
+        if block_table is not None and t.shape[1] != block_size:
+            raise ValueError(f"{name} blocks hold {t.shape[1]} tokens, block_size is {block_size}")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError(f"k_cache and v_cache shapes differ ({tuple(k_cache.shape)} vs {tuple(v_cache.shape)})")
+    _int32_vector("seq_len", seq_len, batch)
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2 \
+                or block_table.shape[0] != batch:
+            raise ValueError(f"block_table must be a contiguous int32 tensor [{batch}][max_blocks_per_seq] "
+                             f"(got {block_table.dtype}, {tuple(block_table.shape)})")
+        if max_seq_len > block_table.shape[1] * block_size:
+            raise ValueError(f"max_seq_len {max_seq_len} exceeds the table's {block_table.shape[1]} "
+                             f"blocks of {block_size} tokens")
+    else:
+        _int32_vector("kv_start", kv_start, batch)
+    rows = k_cache.numel() // max(1, hkv * d)  # cache rows (tokens), all kv heads
+    quant = kv_dtype in ("fp8_e4m3", "int8")
+    if quant and scale_mode == "none":
+        raise ValueError(f"kv_dtype {kv_dtype!r} needs k and v scales (scale_mode 'tensor' or 'token_head')")
+    if not quant and scale_mode != "none":
+        raise ValueError(f"kv_dtype {kv_dtype!r} takes no scales (scale_mode must be 'none')")
+    if quant:
+        n = 1 if scale_mode == "tensor" else rows * hkv
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t is None or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+                raise ValueError(f"{name} must be a contiguous fp32 tensor of {n} elements for scale_mode "
+                                 f"{scale_mode!r} (got {None if t is None else (t.dtype, tuple(t.shape))})")
+
+
 def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_table=None,
                      kv_start=None, kv_dtype: str, scale_mode: str = "none", k_scale=None,
                      v_scale=None, softmax_scale: float, num_kv_heads: int | None = None,
@@ -153,6 +224,9 @@ def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_ta
     Returns ``out``."""
     import torch
 
+    check_decode_args(q, k_cache, v_cache, seq_len, block_table=block_table, kv_start=kv_start,
+                      kv_dtype=kv_dtype, scale_mode=scale_mode, k_scale=k_scale, v_scale=v_scale,
+                      num_kv_heads=num_kv_heads, block_size=block_size, max_seq_len=max_seq_len)
     _require_cuda(q=q, k_cache=k_cache, v_cache=v_cache, seq_len=seq_len, block_table=block_table,
                   kv_start=kv_start, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse,
                   workspace=workspace)
@@ -174,6 +248,8 @@ def decode_attention(q, k_cache, v_cache, seq_len, *, max_seq_len: int, block_ta
         raise ValueError(f"out must be a contiguous tensor of q's shape {tuple(q.shape)} (got {tuple(out.shape)})")
     if lse is not None and (lse.numel() != q.numel() // d or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError(f"lse must be a contiguous fp32 tensor of {q.numel() // d} elements")
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
     max_blocks = 0 if block_table is None else block_table.shape[1]
     need = workspace_bytes(batch, hq, hkv, d, max_seq_len, block_size, kv_dtype, num_partitions, nq)
     if workspace is None:
@@ -237,12 +313,36 @@ def kv_append(k_new, v_new, k_cache, v_cache, pos, *, kv_dtype: str, block_table
     per-token E4M3 / INT8 scales are written too).  Layouts and codes as ``include/fd.h``."""
     import torch
 
-    _require_cuda(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, pos=pos,
-                  block_table=block_table, kv_start=kv_start, k_scale=k_scale, v_scale=v_scale)
+    if k_new.dim() != 3 or k_new.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise ValueError(f"k_new must be an f32/f16/bf16 tensor [batch][num_kv_heads][head_dim] "
+                         f"(got {k_new.dtype}, {tuple(k_new.shape)})")
     batch, hkv, d = k_new.shape
     new_code = {torch.float32: FD_F32, torch.float16: FD_F16, torch.bfloat16: FD_BF16}[k_new.dtype]
     if v_new.dtype != k_new.dtype or v_new.shape != k_new.shape:
         raise ValueError("k_new and v_new must have the same shape and dtype")
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous")
+    _int32_vector("pos", pos, batch)
+    if (block_table is None) == (kv_start is None):
+        raise ValueError("give exactly one of block_table (paged cache) and kv_start (contiguous cache)")
+    if block_table is not None and (block_table.dtype != torch.int32 or block_table.dim() != 2
+                                    or not block_table.is_contiguous() or block_table.shape[0] != batch):
+        raise ValueError(f"block_table must be a contiguous int32 tensor [{batch}][max_blocks_per_seq]")
+    if kv_start is not None:
+        _int32_vector("kv_start", kv_start, batch)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in _cache_dtypes(kv_dtype) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor holding kv_dtype {kv_dtype!r} (got {t.dtype})")
+        if t.shape[-1] != d or t.shape[-2] != hkv:
+            raise ValueError(f"{name} rows must be [{hkv}][{d}] like k_new (got {tuple(t.shape)})")
+    if kv_dtype in ("fp8_e4m3", "int8"):
+        rows = k_cache.numel() // (hkv * d)
+        n = 1 if scale_mode == "tensor" else rows * hkv
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t is None or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+                raise ValueError(f"{name} must be a contiguous fp32 tensor of {n} elements")
+    _require_cuda(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, pos=pos,
+                  block_table=block_table, kv_start=kv_start, k_scale=k_scale, v_scale=v_scale)
     max_blocks = 0 if block_table is None else block_table.shape[1]
     if stream is None:
         stream = torch.cuda.current_stream(k_new.device).cuda_stream

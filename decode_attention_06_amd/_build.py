@@ -1,4 +1,5 @@
 """Build libfd.so (the C-ABI HIP library) in-tree with hipcc for gfx950."""
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -29,7 +30,7 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libfd.so (always recompiles)."""
     out_dir = os.path.join(PKG, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(out_dir, src + ".o")
         cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -37,8 +38,16 @@ def build(verbose: bool = False) -> str:
             cmd[1:1] = ["-x", "hip"]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+        cmds.append(cmd)
         objs.append(obj)
+    # the sources compile independently: one process each, at most one per host core
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        for r in ex.map(lambda c: subprocess.run(c, stderr=None if verbose else subprocess.PIPE), cmds):
+            if r.returncode != 0:
+                if r.stderr:
+                    print(r.stderr.decode(errors="replace"), flush=True)
+                raise subprocess.CalledProcessError(r.returncode, r.args)
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)

@@ -32,6 +32,27 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr float kMaxFloat = 3.40282347e38f;
 // Smallest normal float: the floor of a 16-bit partial row's scale (its reciprocal is finite).
 constexpr float kMinNormal = 1.17549435e-38f;
+
+// Per-(token, head) v scales enter p.V through the f16 P operand, whose range (normal numbers
+// 2^-14 .. 65504) is narrower than that of the scales.  A wave therefore keeps a power-of-two
+// reference 2^ev near the largest |v scale| it has seen and forms 2^(s - m - ev) * v_scale, the
+// weight times v_scale / 2^ev; the accumulator holds the sum divided by 2^ev, which is multiplied
+// back when the segment ends.  ev moves (an exact power-of-two rescale of the accumulator, merged
+// with the running-max rescale) when a tile's largest |v scale| leaves
+// [2^(ev - kVrefLow), 2^(ev + kVrefHigh)]: the f16 operand then stays below
+// 2^(kRescaleSlack + kVrefHigh) = 2^14, and the largest-scale tokens of a tile with weights down to
+// 2^-5 stay f16-normal, whatever the magnitude of the data.
+constexpr int kVrefHigh = 6;
+constexpr int kVrefLow = 8;
+constexpr int kVrefLimit = 100;  // |ev| bound: 2^(s - m - ev) stays finite
+
+// e with x <= 2^e < 2x for a positive normal float x, clamped to [-kVrefLimit, kVrefLimit]
+// (denormals give the lower bound; inf and NaN the upper one).
+__device__ __forceinline__ int exp2_ceil(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu;
+    const int e = (int)((u + 0x007FFFFFu) >> 23) - 127;
+    return min(max(e, -kVrefLimit), kVrefLimit);
+}
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 // ---------------------------------------------------------------- small helpers
@@ -73,9 +94,13 @@ __device__ __forceinline__ uint32_t i8x2_to_f16x2(uint32_t x) {
     return __builtin_bit_cast(uint32_t, biased - f16x2_t{(_Float16)1152.0f, (_Float16)1152.0f});
 }
 
-// bf16 pair -> f16 pair (exact for |x| in the f16 normal range; used for q against INT8 KV).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-    const float lo = __builtin_bit_cast(float, w << 16), hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+// bf16 pair times 2^e -> f16 pair, for a bf16 q against INT8 KV.  The caller picks e so that the
+// largest |q| of the column lands in [2^14, 2^15): every value within 2^28 of it is then an f16
+// normal number and converts exactly (bf16's 8-bit significand fits f16's 11 bits); smaller ones
+// keep an absolute error below 2^-25 of the largest.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w, int e) {
+    const float lo = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, w << 16), e);
+    const float hi = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, w & 0xFFFF0000u), e);
     f16x2_t v = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, v);
 }

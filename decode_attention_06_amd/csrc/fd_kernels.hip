@@ -189,7 +189,7 @@ void partition_kernel(Params p) {
     using G = Geometry<D, KVT>;
     constexpr int EB = G::EB, E = G::E, KSTEPS = G::KSTEPS, KLOADS = G::KLOADS, DT = G::DT, VDW = G::VDW;
     // q.k^T operand type: q's own, except against INT8 KV (codes become f16 exactly; a bf16 q is
-    // converted to f16 once per segment)
+    // scaled by a power of two into f16's range and converted once per segment)
     constexpr int QM = (KVT == KV_I8) ? KV_F16 : QT;
     constexpr bool QCVT = (KVT == KV_I8 && QT == KV_BF16);
     // quantised KV: partial outputs in 16 bits (the host sets Params::part16 by the same rule)
@@ -335,6 +335,10 @@ void partition_kernel(Params p) {
     u32x4_t qop[KSTEPS], qnext[KSTEPS];  // q operand of the current segment / of the next one
     f32x4_t acc[DT];
     float m_run = -INFINITY, l_run = 0.0f;
+    // per-token v scales: the accumulator holds values / 2^ev (wave-uniform reference exponent)
+    int ev = 0;
+    // score multiplier of the lane's column: qk_scale, times 2^-eq when q was scaled by 2^eq
+    float qk_col = qk_scale;
     // Lane column c of unit u_in: column col = hb * 16 + c of its kv head, i.e. query row
     // m = col / group of the sequence's window and head hl = col % group of the kv head's group
     struct Col {
@@ -369,15 +373,32 @@ void partition_kernel(Params p) {
         for (int i = 0; i < DT; i++) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;
         l_run = 0.0f;
+        ev = 0;
     };
     auto convert_q = [&](u32x4_t (&dst)[KSTEPS], const u32x4_t (&src)[KSTEPS]) {
+        if constexpr (QCVT) {
+            // largest |q| of column c (its D values lie in the four lane groups): the bf16 bit
+            // patterns with the sign cleared order like the magnitudes
+            uint32_t mx = 0;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; kk++) {
-            if constexpr (QCVT)
-                dst[kk] = u32x4_t{bf16x2_to_f16x2(src[kk][0]), bf16x2_to_f16x2(src[kk][1]),
-                                  bf16x2_to_f16x2(src[kk][2]), bf16x2_to_f16x2(src[kk][3])};
-            else
-                dst[kk] = src[kk];
+            for (int kk = 0; kk < KSTEPS; kk++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t w = src[kk][i] & 0x7FFF7FFFu;
+                    mx = max(mx, max(w & 0xFFFFu, w >> 16));
+                }
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+            // 2^eq puts the largest |q| in [2^14, 2^15) (bf16 biased exponent in bits 7..14)
+            const int eq = mx == 0 ? 0 : 141 - (int)(mx >> 7);
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++)
+                dst[kk] = u32x4_t{bf16x2_to_f16x2_scaled(src[kk][0], eq), bf16x2_to_f16x2_scaled(src[kk][1], eq),
+                                  bf16x2_to_f16x2_scaled(src[kk][2], eq), bf16x2_to_f16x2_scaled(src[kk][3], eq)};
+            qk_col = __builtin_amdgcn_ldexpf(qk_scale, -eq);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++) dst[kk] = src[kk];
         }
     };
     auto next_segment = [&]() {
@@ -452,8 +473,8 @@ void partition_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             float x = sacc[j >> 2][j & 3];
-            if constexpr (SCALE == SC_TOKEN_HEAD) x *= ksc[j] * p.qk_scale;
-            else x *= qk_scale;
+            if constexpr (SCALE == SC_TOKEN_HEAD) x *= ksc[j] * qk_col;
+            else x *= qk_col;
             s[j] = x;
         }
         // last token of this tile column c may see: query row m of a window of nq rows stops
@@ -469,25 +490,42 @@ void partition_kernel(Params p) {
         for (int j = 1; j < 8; j++) mt = fmaxf(mt, s[j]);
         mt = fmaxf(mt, shfl_xor_f(mt, 16));
         mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        // per-token v scales: reference exponent of the tile's largest |v scale| (all 32 tokens:
+        // the lane's 8, then the four lane groups); it replaces ev when out of ev's window
+        int evt = ev;
+        if constexpr (SCALE == SC_TOKEN_HEAD) {
+            float vm = fmaxf(fmaxf(fabsf(vsc[0]), fabsf(vsc[1])), fmaxf(fabsf(vsc[2]), fabsf(vsc[3])));
+            vm = fmaxf(vm, fmaxf(fmaxf(fabsf(vsc[4]), fabsf(vsc[5])), fmaxf(fabsf(vsc[6]), fabsf(vsc[7]))));
+            vm = fmaxf(vm, shfl_xor_f(vm, 16));
+            vm = fmaxf(vm, shfl_xor_f(vm, 32));
+            evt = uni(vm > 0.0f ? exp2_ceil(vm) : ev);  // all-zero scales: keep ev
+        }
+        const bool emove = evt > ev + kVrefHigh || evt < ev - kVrefLow;
         // move the reference max only when some head exceeds it by more than kRescaleSlack
         // (a column with no visible token yet keeps m_run = -inf: the max with -kMaxFloat below keeps
         // its weights 0 and its alpha 1 instead of NaN)
-        if (__any(mt > m_run + kRescaleSlack)) {  // wave-uniform; always taken on a segment's first tile
+        if (__any(mt > m_run + kRescaleSlack) || emove) {  // wave-uniform
             const float m_new = fmaxf(m_run, mt);
-            const float alpha = __builtin_amdgcn_exp2f(fmaxf(m_run, -kMaxFloat) - fmaxf(m_new, -kMaxFloat));
+            const float dm = fmaxf(m_run, -kMaxFloat) - fmaxf(m_new, -kMaxFloat);
+            const float alpha = __builtin_amdgcn_exp2f(dm);
+            // the accumulator also moves from units of 2^ev to units of 2^evt (exact for a power of two)
+            const float alpha_acc = SCALE == SC_TOKEN_HEAD ? __builtin_amdgcn_exp2f(dm + (float)(ev - evt)) : alpha;
             l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < DT; i++) acc[i] *= alpha;
+            for (int i = 0; i < DT; i++) acc[i] *= alpha_acc;
             m_run = m_new;
+            ev = evt;
         }
+        // token-head scales: weights 2^(s - m - ev), i.e. divided by 2^ev (their sum is scaled back
+        // for l, which stays in units of 2^m)
         float pj[8], psum = 0.0f;
-        const float m_ref = fmaxf(m_run, -kMaxFloat);
+        const float m_ref = fmaxf(m_run, -kMaxFloat) + (SCALE == SC_TOKEN_HEAD ? (float)ev : 0.0f);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             pj[j] = __builtin_amdgcn_exp2f(s[j] - m_ref);
             psum += pj[j];
         }
-        l_run += psum;
+        l_run += SCALE == SC_TOKEN_HEAD ? __builtin_amdgcn_ldexpf(psum, ev) : psum;
 
         // ---- p.V
         if constexpr (KVT == KV_BF16) {
@@ -577,11 +615,15 @@ void partition_kernel(Params p) {
         f32x4_t o[DT];
 #pragma unroll
         for (int i = 0; i < DT; i++) o[i] = (SCALE == SC_TENSOR) ? acc[i] * tensor_v : acc[i];
-        // lane (g, c) holds d = DT*(4g + r) + dt in o[dt][r]
+        // lane (g, c) holds d = DT*(4g + r) + dt in o[dt][r]; with per-token scales the values are
+        // o * 2^ev
         if (d.whole) {
             if (hvalid) {
                 const size_t orow = orow_idx * D;
-                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // 0: a window row with no token
+                // 0: a window row with no token.  l_tot >= 1 otherwise (the weight of the token
+                // that set m is 1), so the factor stays finite
+                float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                if constexpr (SCALE == SC_TOKEN_HEAD) inv = __builtin_amdgcn_ldexpf(inv, ev);
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     float v[DT];
@@ -618,7 +660,7 @@ void partition_kernel(Params p) {
                     }
                     if (g == 0) {
                         p.ws_ml[slot] = make_float2(m_run, l_tot);
-                        p.ws_sc[slot] = sc;
+                        p.ws_sc[slot] = SCALE == SC_TOKEN_HEAD ? __builtin_amdgcn_ldexpf(sc, ev) : sc;
                     }
                 }
             } else if (hvalid) {

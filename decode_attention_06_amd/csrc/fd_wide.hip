@@ -305,6 +305,8 @@ void wide_partition_kernel(Params p) {
     u32x4_t qop[8];
     f32x16_t acc[4];
     float m_run = -INFINITY, l_run = 0.0f;
+    // per-token v scales: the accumulator holds values / 2^ev (wave-uniform reference exponent)
+    int ev = 0;
     auto load_q = [&](int b, int grp) {
         const int u_in = grp * WPG + wave;
         const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
@@ -323,6 +325,7 @@ void wide_partition_kernel(Params p) {
             for (int r = 0; r < 16; r++) acc[i][r] = 0.0f;
         m_run = -INFINITY;
         l_run = 0.0f;
+        ev = 0;
     };
 
     auto compute = [&](int si, int last) {
@@ -367,21 +370,43 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
         for (int r = 1; r < 16; r++) mt = fmaxf(mt, s[r]);
         mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        if (__any(mt > m_run + kRescaleSlack)) {  // wave-uniform; always taken on a segment's first tile
+        // per-token v scales: reference exponent of the tile's largest |v scale| (the lane's 16
+        // tokens, then the other lane half); it replaces ev when out of ev's window
+        int evt = ev;
+        if constexpr (SCALE == SC_TOKEN_HEAD) {
+            // (read here for the max only and again per k-step below: holding all 16 across the
+            // softmax costs registers the kernel does not have)
+            float vsc[16];
+            read_scales(vsc, sbase + soff + 128);  // v scales lie 128 bytes after the k scales
+            float vm = fabsf(vsc[0]);
+#pragma unroll
+            for (int r = 1; r < 16; r++) vm = fmaxf(vm, fabsf(vsc[r]));
+            vm = fmaxf(vm, shfl_xor_f(vm, 32));
+            evt = uni(vm > 0.0f ? exp2_ceil(vm) : ev);  // all-zero scales: keep ev
+        }
+        const bool emove = evt > ev + kVrefHigh || evt < ev - kVrefLow;
+        if (__any(mt > m_run + kRescaleSlack) || emove) {  // wave-uniform; always taken on a segment's first tile
             const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float dm = m_run - m_new;
+            const float alpha = __builtin_amdgcn_exp2f(dm);
+            // the accumulator also moves from units of 2^ev to units of 2^evt (exact for a power of two)
+            const float alpha_acc = SCALE == SC_TOKEN_HEAD ? __builtin_amdgcn_exp2f(dm + (float)(ev - evt)) : alpha;
             l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < 4; i++) acc[i] *= alpha;
+            for (int i = 0; i < 4; i++) acc[i] *= alpha_acc;
             m_run = m_new;
+            ev = evt;
         }
+        // token-head scales: weights 2^(s - m - ev), i.e. divided by 2^ev (their sum is scaled back
+        // for l, which stays in units of 2^m)
         float pj[16], psum = 0.0f;
+        const float m_ref = m_run + (SCALE == SC_TOKEN_HEAD ? (float)ev : 0.0f);
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            pj[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
+            pj[r] = __builtin_amdgcn_exp2f(s[r] - m_ref);
             psum += pj[r];
         }
-        l_run += psum;
+        l_run += SCALE == SC_TOKEN_HEAD ? __builtin_amdgcn_ldexpf(psum, ev) : psum;
         // ---- p.V, two 16-token k-steps
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
@@ -431,9 +456,12 @@ void wide_partition_kernel(Params p) {
         const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
         const int head = kvh * p.group + hb * kWideHeadBlock + li;
         const float l_tot = l_run + shfl_xor_f(l_run, 32);
+        // factor of the accumulator: the tensor v scale, or 2^ev with per-token scales
+        // (2^ev is a normal float: |ev| <= 100)
+        const float sv = (SCALE == SC_TENSOR) ? tensor_v : __builtin_bit_cast(float, (uint32_t)(ev + 127) << 23);
         if (whole) {
             const size_t orow = ((size_t)k.b * p.hq + head) * D;
-            const float inv = ((SCALE == SC_TENSOR) ? tensor_v : 1.0f) / l_tot;
+            const float inv = sv / l_tot;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const float v[4] = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
@@ -445,14 +473,15 @@ void wide_partition_kernel(Params p) {
             // E4M3 KV: f16 of value / (largest |value| of the head's row, spread over the two lane
             // halves), the scale beside it
             const size_t slot = (((size_t)wg * 2 + (seg == 0 ? 0 : 1)) * WPG + wave) * kWideHeadBlock + li;
-            const float sv = (SCALE == SC_TENSOR) ? tensor_v : 1.0f;
             float mx = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r++)
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) mx = fmaxf(mx, fabsf(acc[dt][r] * sv));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            const float sc = fmaxf(mx, sc_floor), inv = sv / sc;
+            // per-token scales: the floor follows 2^ev like sc_floor follows the tensor v scale
+            const float floor_sc = SCALE == SC_TENSOR ? sc_floor : fmaxf(sv * kMinNormal, kMinNormal);
+            const float sc = fmaxf(mx, floor_sc), inv = sv / sc;
             uint16_t *dst = (uint16_t *)p.ws_acc + slot * D;
 #pragma unroll
             for (int r = 0; r < 16; r++)

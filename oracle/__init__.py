@@ -152,6 +152,20 @@ class Problem:
                    nq=getattr(case, "nq", 1))
 
 
+def host_threads() -> int:
+    """Threads for the oracle: the CPUs this process may run on (its affinity mask), capped by
+    OMP_NUM_THREADS when the environment sets one (a machine that shares its cores between jobs
+    gives each its count there)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
 def decode_attention(prob: Problem, seqs=None, nthreads: int | None = None):
     """(out [B][Hq][D], lse [B][Hq]) in float64 -- or [B][nq][Hq][D], [B][nq][Hq] for a window of
     nq > 1 query tokens per sequence.  ``seqs``: optional iterable of sequence ids to compute
@@ -164,7 +178,7 @@ def decode_attention(prob: Problem, seqs=None, nthreads: int | None = None):
     if seqs is not None:
         mask = np.zeros(prob.batch, dtype=np.uint8)
         mask[list(seqs)] = 1
-    nthreads = nthreads or os.cpu_count() or 1
+    nthreads = nthreads or host_threads()
     rc = lib.orc_decode_attention(ctypes.byref(prob.s), None if mask is None else mask.ctypes.data,
                                   out.ctypes.data, lse.ctypes.data, int(nthreads))
     if rc != 0:

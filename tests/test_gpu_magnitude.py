@@ -1,0 +1,117 @@
+"""GPU parity at data magnitudes far from unit size.
+
+The quantised paths carry the K/V scales through the kernels' arithmetic: a per-(token, head)
+k scale multiplies the fp32 score, a per-token v scale enters the f16 P operand of p.V (relative
+to the wave's power-of-two reference), a per-tensor scale is folded into the score scale and the
+final multiply; a bf16 q against INT8 KV is scaled by a power of two into f16's range.  None of
+this may depend on the magnitude of the data.  Each case multiplies the N(0, 1) sources of K and V
+separately by 1e-4, 1e-2, 1 or 1e2 before row-absmax quantisation (so the stored codes are the
+same and only the scales change) and compares the HIP path with the fp64 oracle at the same bar as
+every other quantised case: max_abs 5e-3 and rel_l2 3e-3, with the outputs measured in units of
+the V sources' standard deviation (out / v_mag), since the bar is stated for unit-sized data.
+Both partition kernels (a group of 8: 16-head kernel; 128: wide kernel for E4M3), E4M3 and INT8,
+per-token and per-tensor scales.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_06_amd as fd
+import oracle
+import workloads
+from test_gpu_parity import TOL
+
+pytestmark = pytest.mark.gpu
+
+MAGS = (1e-4, 1e-2, 1.0, 1e2)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    fd.lib()
+    yield
+
+
+def check_scaled(name, case, num_partitions=0, unit=1.0):
+    """Compare GPU and oracle outputs in units of ``unit`` (a number: the V sources' magnitude;
+    "row": each output row's own largest |value|); lse is compared in absolute terms (it is a
+    log), relative to its own size beyond 1."""
+    print(f"[{name}] lens={case.seq_lens} G={case.group} kv={case.kv_dtype} scale={case.scale_mode} "
+          f"partitions={num_partitions}", flush=True)
+    lse = torch.empty(tuple(case.q.shape[:-1]), dtype=torch.float32, device="cuda")
+    out = fd.decode_case(case, lse=lse, num_partitions=num_partitions)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode_attention(oracle.Problem.from_case(case))
+    got = out.double().cpu().numpy()
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    if unit == "row":
+        u = np.max(np.abs(ref), axis=-1, keepdims=True)
+        assert np.all(u > 0)
+    else:
+        u = float(unit)
+    g, r = got / u, ref / u
+    max_abs = float(np.max(np.abs(g - r)))
+    rel_l2 = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    tol_abs, tol_rel = TOL[case.kv_dtype]
+    ok = max_abs <= tol_abs and rel_l2 <= tol_rel
+    print(f"[{name}] {'PASS' if ok else 'FAIL'} |out|max={float(np.max(np.abs(ref))):.3e} "
+          f"max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} (in units of {unit})", flush=True)
+    assert ok, f"{name}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} (tol {tol_abs}, {tol_rel})"
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lg)), f"{name}: lse finiteness differs"
+    assert np.max(np.abs(lg[fin] - ref_lse[fin])) < 1e-3 * max(1.0, float(np.max(np.abs(ref_lse[fin])))), \
+        f"{name}: lse mismatch"
+
+
+KERNELS = {
+    # a group of 8 (16-head kernel) and of 128 (the wide kernel for E4M3; INT8 takes 16-head blocks)
+    "g8": dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[700, 33, 2100], block_size=64),
+    "g128": dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1500, 97], block_size=64),
+}
+
+CASES = [(kern, kv, scale, km, vm)
+         for kern in KERNELS for kv in ("fp8_e4m3", "int8") for scale in ("token_head", "tensor")
+         for km, vm in itertools.product(MAGS, MAGS)]
+
+
+@pytest.mark.parametrize("kern,kv,scale,k_mag,v_mag", CASES,
+                         ids=[f"{k}-{kv}-{s}-k{km:g}-v{vm:g}" for k, kv, s, km, vm in CASES])
+def test_kv_magnitudes(kern, kv, scale, k_mag, v_mag):
+    kw = dict(KERNELS[kern])
+    case = workloads.custom_case(seed=11, device="cuda", kv=kv, q="bf16", scale=scale,
+                                 k_mag=k_mag, v_mag=v_mag, **kw)
+    # two partition counts: whole units written directly, and pieces merged by the combine
+    check_scaled(f"{kern}-{kv}-{scale}-k{k_mag:g}-v{v_mag:g}", case, num_partitions=0, unit=v_mag)
+    check_scaled(f"{kern}-{kv}-{scale}-k{k_mag:g}-v{v_mag:g}-p7", case, num_partitions=7, unit=v_mag)
+
+
+def test_v_scales_spanning_many_octaves_within_a_sequence():
+    """Per-token v scales that change by 2^40 along one sequence (tiles of very different
+    magnitude, in both orders): the reference moves with them and the small-scale tokens keep
+    their precision."""
+    case = workloads.custom_case(seed=5, device="cuda", batch=2, hq=16, hkv=2, d=128,
+                                 seq_lens=[2000, 1300], kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=64)
+    nb, bs, hkv = case.v_scale.shape
+    rows = torch.arange(nb * bs, device="cuda").view(nb, bs, 1).float()
+    # a smooth ramp over the physical rows (the table shuffles them, so tiles see jumps too)
+    case.v_scale = case.v_scale * torch.exp2((rows / (nb * bs) - 0.5) * 40.0)
+    check_scaled("vscale-ramp-2^40", case, num_partitions=0, unit="row")
+    check_scaled("vscale-ramp-2^40-p5", case, num_partitions=5, unit="row")
+
+
+@pytest.mark.parametrize("q_mag", [1e-30, 1e-6, 1e3, 1e5, 1e20])
+@pytest.mark.parametrize("kv", ["int8", "fp8_e4m3"])
+def test_q_magnitudes(kv, q_mag):
+    """A bf16 q far outside f16's range (INT8 KV runs q.k on f16 MFMAs: q is scaled by a power of
+    two per column) and, for comparison, the E4M3 path (bf16 MFMAs)."""
+    case = workloads.custom_case(seed=3, device="cuda", batch=2, hq=16, hkv=2, d=128,
+                                 seq_lens=[900, 70], kv=kv, q="bf16", scale="token_head",
+                                 block_size=32, q_mag=q_mag)
+    check_scaled(f"q{q_mag:g}-{kv}", case)
+    check_scaled(f"q{q_mag:g}-{kv}-p3", case, num_partitions=3)

@@ -27,7 +27,9 @@ Recipe (readings where the pages leave the inputs open):
   inclusive; log-uniform is ``round(exp(U(ln a, ln b)))``; the ragged mix has exactly
   ``round(0.1 * batch)`` long sequences at seeded positions.
 * Q, K, V source values are N(0, 1) fp32 from ``torch.Generator(device).manual_seed(seed)``
-  (the stream depends on the device; every consumer gets the same tensors, so this is fine).
+  (the stream depends on the device; every consumer gets the same tensors, so this is fine),
+  times optional magnitudes ``q_mag`` / ``k_mag`` / ``v_mag`` (default 1) applied before
+  rounding or quantisation: range tests of the kernels at data far from unit size.
 * FP8 rows are quantised row-absmax style, the way activations are quantised in the
   "小算子融合 residual + RMSNorm + quant" passage of the ch.15 profiling page:
   ``scale = amax / 448`` (1 if amax is 0), ``byte = RNE(x / scale)`` via torch's own
@@ -191,8 +193,9 @@ def _quant_tensor_i8(x: torch.Tensor, amax: float):
 
 
 def _fill_store(n_rows: int, hkv: int, d: int, kv: str, scale: str, device, gen,
-                chunk_rows: int = 1 << 19):
-    """Generate K and V row stores ([n_rows][hkv][d]) plus scales, chunk by chunk."""
+                chunk_rows: int = 1 << 19, k_mag: float = 1.0, v_mag: float = 1.0):
+    """Generate K and V row stores ([n_rows][hkv][d]) plus scales, chunk by chunk; the N(0, 1)
+    sources are multiplied by k_mag / v_mag first."""
     storage_dtype = {"fp8_e4m3": torch.uint8, "int8": torch.int8}.get(kv) or _TORCH[kv]
     k = torch.empty((n_rows, hkv, d), dtype=storage_dtype, device=device)
     v = torch.empty_like(k)
@@ -202,8 +205,8 @@ def _fill_store(n_rows: int, hkv: int, d: int, kv: str, scale: str, device, gen,
         vs = torch.empty_like(ks)
     if scale == "tensor":
         # per-tensor amax needs the whole tensor: generate at once (sizes here allow it)
-        ksrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32)
-        vsrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32)
+        ksrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32) * k_mag
+        vsrc = torch.randn((n_rows, hkv, d), generator=gen, device=device, dtype=torch.float32) * v_mag
         quant = _quant_tensor_i8 if kv == "int8" else _quant_tensor
         kb, kscale = quant(ksrc, float(ksrc.abs().max()))
         vb, vscale = quant(vsrc, float(vsrc.abs().max()))
@@ -215,8 +218,10 @@ def _fill_store(n_rows: int, hkv: int, d: int, kv: str, scale: str, device, gen,
         return k, v, ks, vs
     for r0 in range(0, n_rows, chunk_rows):
         r1 = min(n_rows, r0 + chunk_rows)
-        for dst, sdst in ((k, ks), (v, vs)):
+        for dst, sdst, mag in ((k, ks, k_mag), (v, vs, v_mag)):
             src = torch.randn((r1 - r0, hkv, d), generator=gen, device=device, dtype=torch.float32)
+            if mag != 1.0:
+                src *= mag
             if kv in QUANTISED:
                 b, s = (_quant_rows_i8 if kv == "int8" else _quant_rows)(src)
                 dst[r0:r1] = b
@@ -263,7 +268,9 @@ def _build(name, cfg, seed, device, seq_lens) -> Case:
     gen = torch.Generator(device=device).manual_seed(seed)
     nq = int(cfg.get("nq", 1))
     qshape = (batch, nq, hq, d) if nq > 1 else (batch, hq, d)
-    q = torch.randn(qshape, generator=gen, device=device, dtype=torch.float32).to(_TORCH[qd])
+    q = (torch.randn(qshape, generator=gen, device=device, dtype=torch.float32) *
+         float(cfg.get("q_mag", 1.0))).to(_TORCH[qd])
+    mags = dict(k_mag=float(cfg.get("k_mag", 1.0)), v_mag=float(cfg.get("v_mag", 1.0)))
     nan = _nan_bits(kv)
     if paged:
         nb_per = [(n + bs - 1) // bs for n in seq_lens]
@@ -277,7 +284,7 @@ def _build(name, cfg, seed, device, seq_lens) -> Case:
             table[b, :nb] = perm[off:off + nb]
             off += nb
         spare = perm[live:]
-        k, v, ks, vs = _fill_store(num_blocks * bs, hkv, d, kv, scale, device, gen)
+        k, v, ks, vs = _fill_store(num_blocks * bs, hkv, d, kv, scale, device, gen, **mags)
         # poison rows that must never be read
         dead = [np.arange(p * bs, (p + 1) * bs) for p in spare]
         for b, n in enumerate(seq_lens):
@@ -303,7 +310,7 @@ def _build(name, cfg, seed, device, seq_lens) -> Case:
             starts.append(rows)
             rows += n
         rows += CONTIG_GAP_ROWS
-        k, v, ks, vs = _fill_store(rows, hkv, d, kv, scale, device, gen)
+        k, v, ks, vs = _fill_store(rows, hkv, d, kv, scale, device, gen, **mags)
         live = np.zeros(rows, dtype=bool)
         for s, n in zip(starts, seq_lens):
             live[s:s + n] = True
@@ -325,10 +332,13 @@ def _build(name, cfg, seed, device, seq_lens) -> Case:
 
 
 def custom_case(seed=0, device="cpu", *, batch, hq, hkv, d, seq_lens, kv="fp8_e4m3", q="bf16",
-                block_size=64, scale="token_head", paged=True, shuffle=True, max_seq_len=None, nq=1):
-    """A case with explicit shapes (edge cases and small parity sizes)."""
+                block_size=64, scale="token_head", paged=True, shuffle=True, max_seq_len=None, nq=1,
+                q_mag=1.0, k_mag=1.0, v_mag=1.0):
+    """A case with explicit shapes (edge cases and small parity sizes); ``*_mag`` multiply the
+    N(0, 1) sources of q, K and V."""
     cfg = dict(batch=batch, hq=hq, hkv=hkv, d=d, lens=("fixed_list", list(seq_lens)), kv=kv,
-               q=q, block_size=block_size, scale=scale, paged=paged, shuffle=shuffle, nq=nq)
+               q=q, block_size=block_size, scale=scale, paged=paged, shuffle=shuffle, nq=nq,
+               q_mag=q_mag, k_mag=k_mag, v_mag=v_mag)
     if max_seq_len is not None:
         cfg["max_seq_len"] = max_seq_len
     return _build("custom", cfg, seed, device, list(seq_lens))
