@@ -14,6 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_LAUNCH, FD_ERR_CONTRACT = 0, 1, 2, 3, 4, 5
+FD_ERR_SCRATCH = 6
+FD_SCRATCH_BYTES = 48 << 20  # include/fd.h
 FD_F32, FD_F16, FD_BF16, FD_FP8_E4M3, FD_INT8 = 0, 1, 2, 3, 4
 FD_SCALE_NONE, FD_SCALE_PER_TENSOR, FD_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 
@@ -22,7 +24,7 @@ SCALE_CODES = {"none": FD_SCALE_NONE, "tensor": FD_SCALE_PER_TENSOR, "token_head
 EXPORTS = ("fd_decode_attention", "fd_workspace_bytes", "fd_plan_partitions", "fd_status_string",
            "fd_version", "fd_fp8_e4m3_decode", "fd_set_profile_events", "fd_hbm_read_probe",
            "fd_kv_append", "fd_fp8_e4m3_encode", "fd_decode_attention_mq", "fd_workspace_bytes_mq",
-           "fd_plan_partitions_mq", "fd_check_inputs")
+           "fd_plan_partitions_mq", "fd_check_inputs", "fd_decode_attention_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -55,6 +57,10 @@ def lib() -> ctypes.CDLL:
                                           i32, vp]
         L.fd_decode_attention_mq.restype = i32
         L.fd_decode_attention_mq.argtypes = [vp, i32] + L.fd_decode_attention.argtypes[1:]
+        L.fd_decode_attention_noalloc.restype = i32
+        # the _mq arguments without (workspace, workspace_bytes)
+        L.fd_decode_attention_noalloc.argtypes = L.fd_decode_attention_mq.argtypes[:23] + \
+            L.fd_decode_attention_mq.argtypes[25:]
         L.fd_workspace_bytes_mq.restype = sz
         L.fd_workspace_bytes_mq.argtypes = [i32] * 9
         L.fd_plan_partitions_mq.restype = i32
@@ -129,6 +135,14 @@ def decode_attention_mq_raw(q, num_query, *args) -> int:
     a = list(args)
     a[17] = ctypes.c_float(a[17])  # softmax_scale
     return lib().fd_decode_attention_mq(q, num_query, *a)
+
+
+def decode_attention_noalloc_raw(q, num_query, *args) -> int:
+    """Direct call of fd_decode_attention_noalloc: the arguments of ``decode_attention_mq_raw``
+    without (workspace, workspace_bytes); returns the status."""
+    a = list(args)
+    a[17] = ctypes.c_float(a[17])  # softmax_scale
+    return lib().fd_decode_attention_noalloc(q, num_query, *a)
 
 
 def _ptr(t):

@@ -7,6 +7,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fd.h"
 #include "fd_check.h"
 #include "fd_internal.h"
@@ -92,10 +95,54 @@ size_t ws_slots(const Plan &pl) { return (size_t)pl.nparts * 2 * pl.wpg * pl.hb;
 // The last kCheckBytes hold the debug-mode validator's result (FD_CHECK=1).
 constexpr size_t kCheckBytes = 256;
 
-size_t ws_bytes(const Plan &pl, int head_dim) {
+// quantised KV keeps its partial outputs in 16 bits (the kernels take the same rule from
+// Params::part16)
+bool part16_of(int kv_dtype) { return kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8; }
+
+size_t ws_bytes(const Plan &pl, int head_dim, int kv_dtype) {
     const size_t slots = ws_slots(pl);
+    const size_t acc_elem = part16_of(kv_dtype) ? sizeof(uint16_t) : sizeof(float);
     return align256(slots * sizeof(float) * 2) + align256(slots * sizeof(float)) +
-           align256(slots * head_dim * sizeof(float)) + kCheckBytes;
+           align256(slots * head_dim * acc_elem) + kCheckBytes;
+}
+
+// ---- static scratch of the allocation-free entry point (fd_decode_attention_noalloc)
+//
+// One array per GPU, in the library's own code object, that holds the partial states instead of
+// a caller's workspace.  In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address comes from hipGetSymbolAddress, once per device with that device
+// current, and only that address is used.  Every call on a device shares its array.
+static __device__ __align__(256) unsigned char scratch[FD_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the scratch array on the device `stream` belongs to (the current device
+// for the null stream).
+hipError_t scratch_address(hipStream_t stream, void **addr) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *a = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!a) {
+        std::lock_guard<std::mutex> guard(g_scratch_mu);
+        a = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!a) {
+            int cur = -1;
+            if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+            e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+            const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+            if (e != hipSuccess) return e;
+            if (r != hipSuccess) return r;
+            if (!a) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(a, std::memory_order_release);
+        }
+    }
+    *addr = a;
+    return hipSuccess;
 }
 
 // Debug mode: FD_CHECK=1 in the environment, read on every call (no cached state).
@@ -137,6 +184,7 @@ const char *fd_status_string(int status) {
     case FD_ERR_WORKSPACE: return "FD_ERR_WORKSPACE";
     case FD_ERR_LAUNCH: return "FD_ERR_LAUNCH";
     case FD_ERR_CONTRACT: return "FD_ERR_CONTRACT";
+    case FD_ERR_SCRATCH: return "FD_ERR_SCRATCH";
     default: return "FD_UNKNOWN_STATUS";
     }
 }
@@ -164,7 +212,7 @@ size_t fd_workspace_bytes_mq(int batch, int num_query, int num_q_heads, int num_
     if (num_query < 1 || num_query > kMaxQueryWindow) return (size_t)-1;
     Plan pl = make_plan(batch, num_query, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len,
                         num_partitions);
-    return ws_bytes(pl, head_dim);
+    return ws_bytes(pl, head_dim, kv_dtype);
 }
 
 size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
@@ -173,17 +221,19 @@ size_t fd_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head
                                  kv_dtype, num_partitions);
 }
 
-int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, const void *v_cache,
-                           const int32_t *block_table, int max_blocks_per_seq,
-                           const int32_t *kv_start, const int32_t *seq_len,
-                           int batch, int max_seq_len,
-                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                           int kv_dtype, int q_dtype, int scale_mode,
-                           const float *k_scale, const float *v_scale,
-                           float softmax_scale,
-                           void *out, int out_dtype, float *lse,
-                           void *workspace, size_t workspace_bytes,
-                           int num_partitions, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// One step.  use_scratch: the partial states go to the device's static scratch array instead of
+// the caller's workspace (which is then ignored).
+int step(const void *q, int num_query, const void *k_cache, const void *v_cache,
+         const int32_t *block_table, int max_blocks_per_seq, const int32_t *kv_start,
+         const int32_t *seq_len, int batch, int max_seq_len, int num_q_heads, int num_kv_heads,
+         int head_dim, int block_size, int kv_dtype, int q_dtype, int scale_mode,
+         const float *k_scale, const float *v_scale, float softmax_scale, void *out, int out_dtype,
+         float *lse, void *workspace, size_t workspace_bytes, int num_partitions, hipStream_t stream,
+         bool use_scratch) {
     // ---- argument validation (host only, nothing launched on failure)
     if (!q || !k_cache || !v_cache || !seq_len || !out) return FD_ERR_INVALID_ARG;
     if (!sizes_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len)) return FD_ERR_INVALID_ARG;
@@ -210,7 +260,12 @@ int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, co
     }
     const Plan pl = make_plan(batch, num_query, num_q_heads, num_kv_heads, head_dim, kv_dtype, max_seq_len,
                               num_partitions);
-    const size_t need = ws_bytes(pl, head_dim);
+    const size_t need = ws_bytes(pl, head_dim, kv_dtype);
+    if (use_scratch) {
+        if (need > (size_t)FD_SCRATCH_BYTES) return FD_ERR_SCRATCH;
+        if (scratch_address(stream, &workspace) != hipSuccess) return FD_ERR_LAUNCH;
+        workspace_bytes = FD_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need) return FD_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255) return FD_ERR_WORKSPACE;
 
@@ -258,7 +313,7 @@ int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, co
     p.out_dtype = out_dtype;
     // quantised KV (parity bar 5e-3 / 3e-3) keeps its partial outputs in 16 bits: f16 of the value
     // over its row's largest magnitude, relative rounding 2^-12 of that magnitude per piece
-    p.part16 = (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) ? 1 : 0;
+    p.part16 = part16_of(kv_dtype) ? 1 : 0;
     p.qk_scale = (float)((double)softmax_scale * 1.4426950408889634074);  // log2(e)
     {
         const size_t slots = ws_slots(pl);
@@ -274,6 +329,42 @@ int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, co
     if (t_prof_end) (void)hipEventRecord(t_prof_end, stream);
     if (fd::launch_combine(p, stream) != hipSuccess) return FD_ERR_LAUNCH;
     return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *kv_start, const int32_t *seq_len,
+                           int batch, int max_seq_len,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int kv_dtype, int q_dtype, int scale_mode,
+                           const float *k_scale, const float *v_scale,
+                           float softmax_scale,
+                           void *out, int out_dtype, float *lse,
+                           void *workspace, size_t workspace_bytes,
+                           int num_partitions, hipStream_t stream) {
+    return step(q, num_query, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start, seq_len, batch,
+                max_seq_len, num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype, q_dtype, scale_mode,
+                k_scale, v_scale, softmax_scale, out, out_dtype, lse, workspace, workspace_bytes,
+                num_partitions, stream, false);
+}
+
+int fd_decode_attention_noalloc(const void *q, int num_query, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, int max_blocks_per_seq,
+                                const int32_t *kv_start, const int32_t *seq_len,
+                                int batch, int max_seq_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int kv_dtype, int q_dtype, int scale_mode,
+                                const float *k_scale, const float *v_scale,
+                                float softmax_scale,
+                                void *out, int out_dtype, float *lse,
+                                int num_partitions, hipStream_t stream) {
+    return step(q, num_query, k_cache, v_cache, block_table, max_blocks_per_seq, kv_start, seq_len, batch,
+                max_seq_len, num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype, q_dtype, scale_mode,
+                k_scale, v_scale, softmax_scale, out, out_dtype, lse, nullptr, 0, num_partitions, stream, true);
 }
 
 int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,

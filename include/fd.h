@@ -47,8 +47,15 @@ typedef enum {
     FD_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, block_size not 16/32/64, dtype combination */
     FD_ERR_WORKSPACE = 3,   /* workspace missing, too small or not 256-byte aligned           */
     FD_ERR_LAUNCH = 4,      /* the HIP runtime refused a kernel launch                        */
-    FD_ERR_CONTRACT = 5     /* debug mode (FD_CHECK=1) found the device-side contract broken  */
+    FD_ERR_CONTRACT = 5,    /* debug mode (FD_CHECK=1) found the device-side contract broken  */
+    FD_ERR_SCRATCH = 6      /* fd_decode_attention_noalloc: the step's partial states need more
+                               than FD_SCRATCH_BYTES                                           */
 } fd_status;
+
+/* Bytes of the static per-GPU scratch array of fd_decode_attention_noalloc (48 MiB): above every
+ * default plan's workspace (at most ~35 MB for head_dim 128: the 16-head kernel's 65536 fp32
+ * partial rows, or the wide-group kernel's 131072 f16 rows). */
+#define FD_SCRATCH_BYTES (48u << 20)
 
 typedef enum {
     FD_F32 = 0,      /* output only                                                       */
@@ -137,9 +144,9 @@ int fd_decode_attention(const void *q, const void *k_cache, const void *v_cache,
 
 /*
  * fd_workspace_bytes -- workspace size fd_decode_attention needs for these sizes (partial
- * states: 2 slots x 16 (wide-group kernel: 32) heads x (head_dim + 3) fp32 per partition and
- * unit of a group -- max, sum, a row scale and the accumulator row; with E4M3 / INT8 KV the
- * accumulator rows are stored as f16 of value / row scale in the first half of their space).
+ * states: 2 slots x 16 (wide-group kernel: 32) heads per partition and unit of a group, each
+ * max and sum (2 fp32), a row scale (fp32) and the accumulator row: head_dim fp32 for f16 / bf16
+ * KV, head_dim f16 of value / row scale for E4M3 / INT8 KV; plus 256 bytes for debug mode).
  * The same arguments must be passed to fd_decode_attention.  Returns (size_t)-1 for arguments
  * fd_decode_attention would reject as invalid.
  */
@@ -181,6 +188,32 @@ int fd_decode_attention_mq(const void *q, int num_query, const void *k_cache, co
                            void *out, int out_dtype, float *lse,
                            void *workspace, size_t workspace_bytes,
                            int num_partitions, hipStream_t stream);
+
+/*
+ * fd_decode_attention_noalloc -- fd_decode_attention_mq without a workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The partial states go to a static array of FD_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends; its device address is looked up
+ * once per device on the first call there (hipGetSymbolAddress), and no call allocates or frees
+ * anything.  The caller still passes q, the caches, out and lse.  Arguments, results and status
+ * codes are those of fd_decode_attention_mq (num_query = 1: fd_decode_attention), plus
+ * FD_ERR_SCRATCH, before anything is launched, when the step would need more than
+ * FD_SCRATCH_BYTES (fd_workspace_bytes_mq tells; every default plan fits; a forced
+ * num_partitions may not).  Nothing in the array needs to start at zero.  All calls on one GPU
+ * share its array: calls that may overlap on one GPU (different streams without ordering) race
+ * and must not be made; calls on one stream are ordered and safe.  The device is the stream's
+ * (the current device for the null stream).
+ */
+int fd_decode_attention_noalloc(const void *q, int num_query, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, int max_blocks_per_seq,
+                                const int32_t *kv_start, const int32_t *seq_len,
+                                int batch, int max_seq_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int kv_dtype, int q_dtype, int scale_mode,
+                                const float *k_scale, const float *v_scale,
+                                float softmax_scale,
+                                void *out, int out_dtype, float *lse,
+                                int num_partitions, hipStream_t stream);
 
 /* fd_workspace_bytes_mq / fd_plan_partitions_mq -- fd_workspace_bytes / fd_plan_partitions for a
  * window of num_query query tokens ((size_t)-1 / -1 also when num_query is outside 1..64). */

@@ -48,10 +48,16 @@ def test_version_and_status_strings():
 def test_plan_and_workspace_sizes():
     W = fd.plan_partitions(32, 64, 8, 128, 32768, 64, "fp8_e4m3")
     assert W == 256                       # 8 kv heads -> 8 waves per workgroup, 2048 waves
-    assert fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3") >= W * 8 * 2 * 16 * 130 * 4
+    # per slot: max and sum (8 bytes), a row scale (4) and the accumulator row: f16 for quantised
+    # KV, fp32 for f16 / bf16 KV
+    slots = W * 8 * 2 * 16
+    assert slots * (12 + 128 * 2) <= fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3") \
+        <= slots * (12 + 128 * 2) + 4 * 256
+    assert slots * (12 + 128 * 4) <= fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "bf16") \
+        <= slots * (12 + 128 * 4) + 4 * 256
     # E4M3 group of 128 heads: wide kernel, 4 waves of 32 heads per workgroup, 2048 waves
     assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3") == 512
-    assert fd.workspace_bytes(4, 128, 1, 128, 131072, 64, "fp8_e4m3") >= 512 * 2 * 4 * 32 * 130 * 4
+    assert fd.workspace_bytes(4, 128, 1, 128, 131072, 64, "fp8_e4m3") >= 512 * 2 * 4 * 32 * (12 + 128 * 2)
     # same group with bf16 KV: 16-head kernel, 8 head blocks per workgroup
     assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "bf16") == 256
     # group of 64 on 2 kv heads: wide kernel with 2 waves per workgroup, capped by 2*2*128 tiles
@@ -267,3 +273,42 @@ def test_check_inputs_bad_arguments_rejected_before_launch(change, expect):
 def test_check_inputs_accepted_up_to_the_launch(change):
     # without a GPU the launch itself fails: the host checks passed
     assert fd.check_inputs_raw(**good_check_args(**change)) == fd.FD_ERR_LAUNCH
+
+
+# ------------------------------------------------------------------ allocation-free entry point
+def _noalloc(**kw):
+    a = good_args(**kw)
+    a.pop("workspace"), a.pop("workspace_bytes_")
+    q = a.pop("q")
+    order = ("k_cache", "v_cache", "block_table", "max_blocks_per_seq", "kv_start", "seq_len", "batch",
+             "max_seq_len", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "kv_dtype", "q_dtype",
+             "scale_mode", "k_scale", "v_scale", "softmax_scale", "out", "out_dtype", "lse",
+             "num_partitions", "stream")
+    return fd.decode_attention_noalloc_raw(q, 1, *[a[k] for k in order])
+
+
+def test_noalloc_every_default_plan_fits_the_scratch():
+    for args in [(32, 64, 8, 128, 32768, 64, "fp8_e4m3"), (4, 128, 1, 128, 131072, 64, "fp8_e4m3"),
+                 (256, 32, 8, 128, 131072, 32, "fp8_e4m3"), (16, 32, 8, 128, 4096, 64, "bf16"),
+                 (64, 128, 8, 128, 1 << 20, 64, "f16"), (4, 256, 2, 128, 1 << 20, 64, "fp8_e4m3")]:
+        assert fd.workspace_bytes(*args) <= fd.FD_SCRATCH_BYTES, args
+    for nq in (2, 4, 64):
+        assert fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "bf16", num_query=nq) <= fd.FD_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_a_step_larger_than_the_scratch_before_launch():
+    # forced partitions whose partial states exceed the static array: FD_ERR_SCRATCH, found on
+    # the host before the device is touched (no GPU here)
+    big = 100000
+    assert fd.workspace_bytes(2, 8, 2, 128, 1 << 20, 64, "fp8_e4m3", num_partitions=big) > fd.FD_SCRATCH_BYTES
+    assert _noalloc(max_seq_len=1 << 20, max_blocks_per_seq=1 << 14, num_partitions=big) == fd.FD_ERR_SCRATCH
+    assert fd.status_string(fd.FD_ERR_SCRATCH) == "FD_ERR_SCRATCH"
+
+
+def test_noalloc_validates_arguments_as_the_workspace_entry_point():
+    for change, expect in BAD:
+        if "workspace" in change or "workspace_bytes_" in change:
+            continue
+        assert _noalloc(**change) == expect, change
+    # valid sizes get past every host check to the device (FD_ERR_LAUNCH without a GPU)
+    assert _noalloc() == fd.FD_ERR_LAUNCH
