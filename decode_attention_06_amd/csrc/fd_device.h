@@ -16,6 +16,8 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 
 enum { KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3, KV_I8 = 4 };
 enum { SC_NONE = 0, SC_TENSOR = 1, SC_TOKEN_HEAD = 2 };

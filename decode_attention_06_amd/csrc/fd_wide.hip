@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fd_device.h"
 
 namespace fd {
@@ -129,6 +131,16 @@ __device__ __forceinline__ void lds_read_v8(uint32_t (&w)[8], uint32_t a) {
         : "memory");
 }
 
+// x = 0 unless thr >= lh4 (a token is kept when its offset within the lane's run, subtracted from
+// the tile's last valid token, is still at least the lane-half offset 4 lh).  Inline, so that the
+// compare stays inside the rarely taken branch of a partial tile instead of being hoisted into
+// every tile.  x may come straight from a transcendental op (v_exp_f32), whose result a following
+// VALU read must wait for: the asm starts with wait states of its own (the compiler does not pad
+// inline asm for that hazard).
+__device__ __forceinline__ void keep_if_ge(float &x, int thr, int lh4) {
+    asm volatile("s_nop 1\n\tv_cmp_ge_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, 0, %0, vcc" : "+v"(x) : "s"(thr), "v"(lh4) : "vcc");
+}
+
 // Workgroup barrier that the compiler may not move memory operations across.
 __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
@@ -139,7 +151,7 @@ __device__ __forceinline__ void wg_barrier() {
 }  // namespace
 
 template <int WPG, int NSLOT, int QT, int SCALE, bool PAGED, bool B16>
-__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
 void wide_partition_kernel(Params p) {
     using LY = WideLayout<WPG, SCALE>;
     constexpr int D = 128;
@@ -295,14 +307,21 @@ void wide_partition_kernel(Params p) {
 
     // ---- per-lane LDS offsets within a slot
     const uint32_t ring0 = lds_addr(ring);
+    // K operand of the FP8 q.k^T MFMA of k-step ks: token li, d = 64 ks + 32 lh + 0..31, i.e. the
+    // row's 16-byte chunks 4 ks + 2 lh and 4 ks + 2 lh + 1 (stored at chunk ^ (li & 7))
     uint32_t koff[4];
 #pragma unroll
-    for (int q = 0; q < 4; q++) koff[q] = li * LY::ROWB + 16 * ((4 * lh + q) ^ (li & 7));
+    for (int q = 0; q < 4; q++) koff[q] = li * LY::ROWB + 16 * ((4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
     const uint32_t voff = LY::KV_BYTES + (4 * lh) * LY::ROWB + 4 * li;
     const uint32_t soff = 2 * LY::KV_BYTES + wave * LY::SC_BYTES + 16 * lh;
 
     // ---- per-segment state
-    u32x4_t qop[8];
+    // q operand of q.k^T: NQT E4M3 terms whose sum is q * 2^eq exactly (bf16 q: 2 terms, f16 q: 3),
+    // for head li at d = 64 ks + 32 lh + j in byte j of qf8[t][ks]; the head's score multiplier
+    // qk_head carries 2^-eq (and, for a negative per-tensor k scale, q carries the sign)
+    constexpr int NQT = QT == KV_BF16 ? 2 : 3;
+    i32x8_t qf8[NQT][2];
+    float qk_head = qk_scale;
     f32x16_t acc[4];
     float m_run = -INFINITY, l_run = 0.0f;
     // per-token v scales: the accumulator holds values / 2^ev (wave-uniform reference exponent)
@@ -311,12 +330,64 @@ void wide_partition_kernel(Params p) {
         const int u_in = grp * WPG + wave;
         const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
         const int head = kvh * p.group + hb * kWideHeadBlock + li;
-        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + 64 * lh;
+        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + 32 * lh;
+        u32x4_t raw[8];  // raw[4 ks + c]: d = 64 ks + 32 lh + 8 c + 0..7
 #pragma unroll
-        for (int kk = 0; kk < 8; kk++) qop[kk] = *(const u32x4_t *)(qrow + 8 * kk);
+        for (int i = 0; i < 8; i++) raw[i] = *(const u32x4_t *)(qrow + 64 * (i >> 2) + 8 * (i & 3));
         // complete here (a drain, once per segment), so that no load is pending at the top of the
         // tile loop and the compiler adds no wait on the in-flight tile copies there
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        // largest |q| of head li over its 128 values (this lane's 64 and lane li + 32 * (1 - lh)'s):
+        // bf16 / f16 bit patterns with the sign cleared order like the magnitudes
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t w = raw[i][e] & 0x7FFF7FFFu;
+                mx = max(mx, max(w & 0xFFFFu, w >> 16));
+            }
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+        // 2^eq puts the largest |q| in [2^7, 2^8), inside E4M3's range (largest finite 448)
+        int eq = 0;
+        if (mx != 0) eq = QT == KV_BF16 ? 134 - (int)(mx >> 7) : 22 - (int)(mx >> 10);
+        // per-tensor scale: the multiplier is kept >= 0 (the tile max is then taken on raw scores)
+        const bool flip = SCALE == SC_TENSOR && qk_scale < 0.0f;
+        qk_head = __builtin_amdgcn_ldexpf(flip ? -qk_scale : qk_scale, -eq);
+        auto to_f32 = [](uint32_t h) -> float {
+            if constexpr (QT == KV_BF16) return __builtin_bit_cast(float, h << 16);
+            else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+        };
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int e2 = 0; e2 < 2; e2++) {
+                // values 4 e2 .. 4 e2 + 3 of raw[i]: d = 8 c + 4 e2 + 0..3 -> dword 2 c + e2 of a term
+                float x[4];
+#pragma unroll
+                for (int h = 0; h < 4; h++) {
+                    const uint32_t w = raw[i][2 * e2 + (h >> 1)];
+                    const float v = to_f32((h & 1) ? (w >> 16) : (w & 0xFFFFu));
+                    x[h] = __builtin_amdgcn_ldexpf(flip ? -v : v, eq);
+                }
+#pragma unroll
+                for (int t = 0; t < NQT; t++) {
+                    // nearest E4M3 values (exact hardware convert, ties to even); the remainder is
+                    // exact in fp32 and has few enough significant bits for the next term
+                    i16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[0], x[1], 1.0f, false);
+                    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[2], x[3], 1.0f, true);
+                    const uint32_t cw = __builtin_bit_cast(uint32_t, c);
+                    qf8[t][i >> 2][2 * (i & 3) + e2] = (int)cw;
+                    if (t + 1 < NQT) {
+                        const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, false);
+                        const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, true);
+                        x[0] -= lo[0];
+                        x[1] -= lo[1];
+                        x[2] -= hi[0];
+                        x[3] -= hi[1];
+                    }
+                }
+            }
     };
     auto reset_state = [&]() {
 #pragma unroll
@@ -328,6 +399,7 @@ void wide_partition_kernel(Params p) {
         ev = 0;
     };
 
+    const int lh4 = 4 * lh;
     auto compute = [&](int si, int last) {
         const uint32_t sbase = ring0 + si * LY::SLOT;
         u32x4_t kr[4];
@@ -344,32 +416,37 @@ void wide_partition_kernel(Params p) {
             }
         };
 
-        // ---- scores S[token][head]
+        // ---- scores S[token][head] = K . (q * 2^eq) on FP8 MFMAs straight from the ring's E4M3
+        // bytes (no conversion): two 64-deep k-steps, NQT terms of q each
         f32x16_t S;
 #pragma unroll
         for (int r = 0; r < 16; r++) S[r] = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 8; kk++) {
-            const uint32_t w0 = kr[kk >> 1][2 * (kk & 1)], w1 = kr[kk >> 1][2 * (kk & 1) + 1];
-            const u32x4_t a = {cvt_fp8x2<QT, false>(w0), cvt_fp8x2<QT, true>(w0),
-                               cvt_fp8x2<QT, false>(w1), cvt_fp8x2<QT, true>(w1)};
-            S = mfma32_qk<QT>(a, qop[kk], S);
+        for (int ks = 0; ks < 2; ks++) {
+            const u32x4_t k0 = kr[2 * ks], k1 = kr[2 * ks + 1];
+            const i32x8_t a = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                               (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+#pragma unroll
+            for (int t = 0; t < NQT; t++)  // E4M3 x E4M3, both block scales 2^0 (E8M0 127)
+                S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[t][ks], S, 0, 0, 0, 127, 0, 127);
         }
         float ksc[16];
         if constexpr (SCALE == SC_TOKEN_HEAD) read_scales(ksc, sbase + soff);
-        // ---- online softmax (log2 units); lane holds tokens 8(r/4) + 4lh + r%4 of head li
+        // ---- online softmax (log2 units); lane holds tokens 8(r/4) + 4lh + r%4 of head li.
+        // Per-tensor scale: s = S * qk_head with qk_head >= 0, so the tile max is qk_head times the
+        // max of the raw scores and the multiply folds into the exponent's FMA below; per-token
+        // scales: s = S * k_scale * qk_head per token.
+        // A partial tile's rows past `last` are copies of row `last` (the copies clamp the row), so
+        // they cannot raise the tile max; only their weights are zeroed below.
         float s[16];
 #pragma unroll
-        for (int r = 0; r < 16; r++) s[r] = (SCALE == SC_TOKEN_HEAD) ? S[r] * (ksc[r] * p.qk_scale) : S[r] * qk_scale;
-        if (last < kTile - 1) {
+        for (int r = 0; r < 16; r++) s[r] = (SCALE == SC_TOKEN_HEAD) ? S[r] * (ksc[r] * qk_head) : S[r];
+        float mt = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-            for (int r = 0; r < 16; r++)
-                if (8 * (r >> 2) + 4 * lh + (r & 3) > last) s[r] = -INFINITY;
-        }
-        float mt = s[0];
-#pragma unroll
-        for (int r = 1; r < 16; r++) mt = fmaxf(mt, s[r]);
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        for (int r = 3; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[r]), s[r + 1]);
+        mt = fmaxf(mt, s[15]);
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));  // finite: token 0 of the tile is valid
+        if constexpr (SCALE != SC_TOKEN_HEAD) mt *= qk_head;
         // per-token v scales: reference exponent of the tile's largest |v scale| (the lane's 16
         // tokens, then the other lane half); it replaces ev when out of ev's window
         int evt = ev;
@@ -393,20 +470,37 @@ void wide_partition_kernel(Params p) {
             const float alpha_acc = SCALE == SC_TOKEN_HEAD ? __builtin_amdgcn_exp2f(dm + (float)(ev - evt)) : alpha;
             l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < 4; i++) acc[i] *= alpha_acc;
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[i][r] *= alpha_acc;
             m_run = m_new;
             ev = evt;
         }
         // token-head scales: weights 2^(s - m - ev), i.e. divided by 2^ev (their sum is scaled back
         // for l, which stays in units of 2^m)
-        float pj[16], psum = 0.0f;
+        float pj[16];
         const float m_ref = m_run + (SCALE == SC_TOKEN_HEAD ? (float)ev : 0.0f);
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            pj[r] = __builtin_amdgcn_exp2f(s[r] - m_ref);
-            psum += pj[r];
+        for (int r = 0; r < 16; r++)
+            pj[r] = __builtin_amdgcn_exp2f((SCALE == SC_TOKEN_HEAD) ? s[r] - m_ref : __builtin_fmaf(S[r], qk_head, -m_ref));
+        if (last < kTile - 1) {  // a partial tile: weight 0 for tokens 8(r/4) + 4lh + r%4 past `last`
+#pragma unroll
+            for (int r = 0; r < 16; r++) keep_if_ge(pj[r], last - 8 * (r >> 2) - (r & 3), lh4);
         }
-        l_run += SCALE == SC_TOKEN_HEAD ? __builtin_amdgcn_ldexpf(psum, ev) : psum;
+        if constexpr (SCALE == SC_TOKEN_HEAD) {
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r++) psum += pj[r];
+            l_run += __builtin_amdgcn_ldexpf(psum, ev);
+        } else {
+            // l sums the f16 weights p.V multiplies (acc and l then carry the same rounded weights)
+            float psum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pack_f16(pj[2 * u], pj[2 * u + 1])),
+                                              f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, psum, false);
+            l_run += psum;
+        }
         // ---- p.V, two 16-token k-steps
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
