@@ -75,20 +75,6 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, void *dst) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_void_t *)p; }
 
-// Four 16-byte LDS reads, complete on return.
-__device__ __forceinline__ void lds_read_4x16(u32x4_t (&r)[4], uint32_t a0, uint32_t a1, uint32_t a2,
-                                              uint32_t a3) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-        : "memory");
-}
-
 // Four 16-byte LDS reads at a + 0, 32, 64, 96 bytes, complete on return.
 __device__ __forceinline__ void lds_read_4x16_s32(u32x4_t (&r)[4], uint32_t a) {
     asm volatile(
@@ -113,6 +99,30 @@ __device__ __forceinline__ void lds_read_2x16_s32(u32x4_t (&r)[2], uint32_t a) {
         : "memory");
 }
 
+// x = 0 unless thr >= lh4 (a token is kept when its offset within the lane's run, subtracted from
+// the tile's last valid token, is still at least the lane-half offset 4 lh).  Inline, so that the
+// compare stays inside the rarely taken branch of a partial tile instead of being hoisted into
+// every tile.  x may come straight from a transcendental op (v_exp_f32), whose result a following
+// VALU read must wait for: the asm starts with wait states of its own (the compiler does not pad
+// inline asm for that hazard).
+__device__ __forceinline__ void keep_if_ge(float &x, int thr, int lh4) {
+    asm volatile("s_nop 1\n\tv_cmp_ge_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, 0, %0, vcc" : "+v"(x) : "s"(thr), "v"(lh4) : "vcc");
+}
+
+// Four 16-byte LDS reads, complete on return.
+__device__ __forceinline__ void lds_read_4x16(u32x4_t (&r)[4], uint32_t a0, uint32_t a1, uint32_t a2,
+                                              uint32_t a3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
 // Eight 4-byte LDS reads from rows {0, 1, 2, 3, 8, 9, 10, 11} (128-byte rows) past a.
 __device__ __forceinline__ void lds_read_v8(uint32_t (&w)[8], uint32_t a) {
     asm volatile(
@@ -131,14 +141,14 @@ __device__ __forceinline__ void lds_read_v8(uint32_t (&w)[8], uint32_t a) {
         : "memory");
 }
 
-// x = 0 unless thr >= lh4 (a token is kept when its offset within the lane's run, subtracted from
-// the tile's last valid token, is still at least the lane-half offset 4 lh).  Inline, so that the
-// compare stays inside the rarely taken branch of a partial tile instead of being hoisted into
-// every tile.  x may come straight from a transcendental op (v_exp_f32), whose result a following
-// VALU read must wait for: the asm starts with wait states of its own (the compiler does not pad
-// inline asm for that hazard).
-__device__ __forceinline__ void keep_if_ge(float &x, int thr, int lh4) {
-    asm volatile("s_nop 1\n\tv_cmp_ge_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, 0, %0, vcc" : "+v"(x) : "s"(thr), "v"(lh4) : "vcc");
+// Largest of x over lanes i and i ^ 32 (the two lane halves): one v_permlane32_swap, no LDS.
+// (Elements of the returned pair are copied to scalars before any bit cast: a bit cast straight
+// from a vector element reads element 0 with this compiler.)
+__device__ __forceinline__ float max_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t a = r[0], b = r[1];
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 // Workgroup barrier that the compiler may not move memory operations across.
@@ -445,7 +455,7 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
         for (int r = 3; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[r]), s[r + 1]);
         mt = fmaxf(mt, s[15]);
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));  // finite: token 0 of the tile is valid
+        mt = max_halves(mt);  // finite: token 0 of the tile is valid
         if constexpr (SCALE != SC_TOKEN_HEAD) mt *= qk_head;
         // per-token v scales: reference exponent of the tile's largest |v scale| (the lane's 16
         // tokens, then the other lane half); it replaces ev when out of ev's window
@@ -458,7 +468,7 @@ void wide_partition_kernel(Params p) {
             float vm = fabsf(vsc[0]);
 #pragma unroll
             for (int r = 1; r < 16; r++) vm = fmaxf(vm, fabsf(vsc[r]));
-            vm = fmaxf(vm, shfl_xor_f(vm, 32));
+            vm = max_halves(vm);
             evt = uni(vm > 0.0f ? exp2_ceil(vm) : ev);  // all-zero scales: keep ev
         }
         const bool emove = evt > ev + kVrefHigh || evt < ev - kVrefLow;
