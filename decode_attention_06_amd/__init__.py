@@ -46,10 +46,14 @@ def lib() -> ctypes.CDLL:
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(LIB_PATH):
+        # FD_LIB: a separately built copy of the library (e.g. a host-sanitizer build) to load
+        path = os.environ.get("FD_LIB") or LIB_PATH
+        if not os.path.exists(path):
+            if path != LIB_PATH:
+                raise RuntimeError(f"FD_LIB names {path}, which does not exist")
             from . import _build
             _build.build()
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.fd_decode_attention.restype = i32
         L.fd_decode_attention.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -76,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.fd_fp8_e4m3_decode.restype = i32
         L.fd_fp8_e4m3_decode.argtypes = [vp, vp, i32, vp]
         L.fd_hbm_read_probe.restype = i32
-        L.fd_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
+        L.fd_hbm_read_probe.argtypes = [vp, sz, vp, i32, i32, vp]
         L.fd_set_profile_events.restype = i32
         L.fd_set_profile_events.argtypes = [vp, vp]
         L.fd_kv_append.restype = i32
@@ -431,9 +435,10 @@ def check_inputs(seq_len, *, max_seq_len: int, extent: int, block_table=None, kv
     return {"violations": n, "first_sequence": first, "kind": CHECK_KINDS.get(kind, kind), "value": value}
 
 
-def hbm_read_probe(buf, out, blocks: int, stream=None):
-    """Diagnostic: stream-read GPU tensor ``buf`` (uint8, 16-byte multiple) once; ``out`` is a
-    uint32 GPU tensor of at least blocks*256 elements."""
+def hbm_read_probe(buf, out, blocks: int, kind: int = 0, stream=None):
+    """Diagnostic: stream-read GPU tensor ``buf`` (uint8, 16-byte multiple; 1 KB multiple for
+    kinds 1 and 2) once with load design ``kind`` (see fd_hbm_read_probe); ``out`` is a uint32
+    GPU tensor of at least blocks*256 elements."""
     import torch
 
     _require_cuda(buf=buf, out=out)
@@ -442,6 +447,6 @@ def hbm_read_probe(buf, out, blocks: int, stream=None):
         raise ValueError("out too small")
     if stream is None:
         stream = torch.cuda.current_stream(buf.device).cuda_stream
-    st = lib().fd_hbm_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, stream)
+    st = lib().fd_hbm_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, kind, stream)
     if st != FD_OK:
         raise FdError(st, "fd_hbm_read_probe")

@@ -390,9 +390,10 @@ int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end) 
     return FD_OK;
 }
 
-int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, hipStream_t stream) {
+int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, int kind, hipStream_t stream) {
     if (!buf || !out || blocks <= 0 || (bytes & 15) || ((uintptr_t)buf & 15)) return FD_ERR_INVALID_ARG;
-    return fd::launch_read_probe(buf, bytes / 16, out, blocks, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
+    if (kind < 0 || kind > 2 || (kind > 0 && (bytes & 1023))) return FD_ERR_INVALID_ARG;
+    return fd::launch_read_probe(buf, bytes / 16, out, blocks, kind, stream) == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
 }
 
 int fd_kv_append(const void *k_new, const void *v_new, int new_dtype, void *k_cache, void *v_cache,

@@ -69,7 +69,7 @@ hipError_t launch_combine(const Params &p, hipStream_t stream);
 // wpg 2 or 4 head blocks of one kv head per workgroup.
 hipError_t launch_wide_partition(const Params &p, int q_dtype, int scale_mode, hipStream_t stream);
 hipError_t launch_fp8_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
-hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, hipStream_t stream);
+hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, int kind, hipStream_t stream);
 // fd_append.hip: new_dtype 0 f32 / 1 f16 / 2 bf16; kv_dtype and scale_mode as the FD_ codes.
 hipError_t launch_append(const AppendParams &a, int new_dtype, int kv_dtype, int scale_mode, hipStream_t stream);
 hipError_t launch_fp8_encode(const float *in, uint8_t *out, int n, hipStream_t stream);

@@ -958,6 +958,27 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t *__restri
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// Second probe design: each wave streams whole 1 KB chunks (lane i the 16 bytes at 16 i),
+// chunks c = 4 * block + wave + k * (4 * grid), INFL nontemporal loads per lane in flight.
+// Covers the first n1k * 1024 bytes.
+template <int INFL>
+__global__ __launch_bounds__(256) void read_probe_chunks_kernel(const u32x4_t *__restrict__ in, size_t n1k,
+                                                                uint32_t *__restrict__ out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const size_t nw = (size_t)gridDim.x * 4;
+    size_t c = (size_t)blockIdx.x * 4 + wave;
+    u32x4_t acc = {0, 0, 0, 0};
+    for (; c + (INFL - 1) * nw < n1k; c += INFL * nw) {
+        u32x4_t v[INFL];
+#pragma unroll
+        for (int i = 0; i < INFL; i++) v[i] = __builtin_nontemporal_load(in + (c + i * nw) * 64 + lane);
+#pragma unroll
+        for (int i = 0; i < INFL; i++) acc ^= v[i];
+    }
+    for (; c < n1k; c += nw) acc ^= __builtin_nontemporal_load(in + c * 64 + lane);
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 // ---------------------------------------------------------------- host-side dispatch
 template <int D, int KVT, int QT, int SCALE>
 static hipError_t launch_p(const Params &p, hipStream_t stream) {
@@ -1025,8 +1046,15 @@ hipError_t launch_combine(const Params &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4_t *)in, n16, out);
+hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, int kind, hipStream_t stream) {
+    if (kind == 0)
+        hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4_t *)in, n16, out);
+    else if (kind == 1)
+        hipLaunchKernelGGL(read_probe_chunks_kernel<4>, dim3(blocks), dim3(256), 0, stream, (const u32x4_t *)in,
+                           n16 / 64, out);
+    else
+        hipLaunchKernelGGL(read_probe_chunks_kernel<8>, dim3(blocks), dim3(256), 0, stream, (const u32x4_t *)in,
+                           n16 / 64, out);
     return hipGetLastError();
 }
 

@@ -278,13 +278,15 @@ int fd_set_profile_events(hipEvent_t partition_begin, hipEvent_t partition_end);
 
 /*
  * fd_hbm_read_probe -- diagnostic: reads `bytes` (a multiple of 16) from the device buffer `buf`
- * (16-byte aligned) with coalesced 128-bit loads, `blocks` workgroups of 256 lanes striding over
- * it, and writes one XOR fold per lane to out[blocks * 256] (uint32).  Timing it gives the read
- * bandwidth a plain stream reaches on the device, the practical ceiling for the attention
- * kernels' KV reads.  Asynchronous on `stream`.  Returns FD_OK, FD_ERR_INVALID_ARG or
- * FD_ERR_LAUNCH.
+ * (16-byte aligned) with coalesced 128-bit loads, `blocks` workgroups of 256 lanes, and writes one
+ * XOR fold per lane to out[blocks * 256] (uint32).  Timing it gives the read bandwidth a plain
+ * stream reaches on the device, the practical ceiling for the attention kernels' KV reads.
+ * `kind` picks the load design, so that the ceiling does not rest on one of them: 0 = plain
+ * loads, lanes striding over the buffer, 4 per lane in flight; 1 / 2 = nontemporal loads, each
+ * wave reading whole 1 KB chunks, 4 / 8 per lane in flight (`bytes` a multiple of 1024).
+ * Asynchronous on `stream`.  Returns FD_OK, FD_ERR_INVALID_ARG or FD_ERR_LAUNCH.
  */
-int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, hipStream_t stream);
+int fd_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int blocks, int kind, hipStream_t stream);
 
 /*
  * fd_check_inputs -- debug validation of the device-side contract of fd_decode_attention(_mq)

@@ -65,8 +65,12 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        # ORACLE_LIB: a separately built copy (e.g. a sanitizer build) to load instead
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            build()
+            path = _LIB
+        lib = ctypes.CDLL(path)
         lib.orc_e4m3_to_double.restype = ctypes.c_double
         lib.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
         lib.orc_f16_to_double.restype = ctypes.c_double

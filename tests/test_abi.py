@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = fd.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    out = subprocess.run(["nm", "-D", "--defined-only", fd.LIB_PATH], capture_output=True, text=True,
+    out = subprocess.run(["nm", "-D", "--defined-only", os.environ.get("FD_LIB") or fd.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (fd_[a-z0-9_]+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
@@ -150,9 +150,16 @@ def test_int8_kv_accepted_up_to_the_launch(scale, q_dtype):
 
 def test_read_probe_rejects_bad_arguments():
     L = fd.lib()
-    assert L.fd_hbm_read_probe(None, 16, 0x1000, 1, None) == fd.FD_ERR_INVALID_ARG
-    assert L.fd_hbm_read_probe(0x1000, 15, 0x2000, 1, None) == fd.FD_ERR_INVALID_ARG
-    assert L.fd_hbm_read_probe(0x1000, 16, 0x2000, 0, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_hbm_read_probe(None, 16, 0x1000, 1, 0, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_hbm_read_probe(0x1000, 15, 0x2000, 1, 0, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_hbm_read_probe(0x1000, 16, 0x2000, 0, 0, None) == fd.FD_ERR_INVALID_ARG
+    # unknown design; the chunked designs need whole 1 KB chunks
+    assert L.fd_hbm_read_probe(0x1000, 1024, 0x2000, 1, 3, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_hbm_read_probe(0x1000, 1024, 0x2000, 1, -1, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_hbm_read_probe(0x1000, 1040, 0x2000, 1, 1, None) == fd.FD_ERR_INVALID_ARG
+    # valid arguments reach the launch (FD_ERR_LAUNCH without a GPU)
+    for kind in (0, 1, 2):
+        assert L.fd_hbm_read_probe(0x1000, 2048, 0x2000, 1, kind, None) == fd.FD_ERR_LAUNCH
 
 
 def test_fp8_decode_rejects_bad_count():

@@ -2,7 +2,8 @@
 batch, per-sequence lengths (empty, single-token, short, long), paged (16/32/64-token pages) or
 contiguous, q dtype, scale mode and partition count are drawn per case from a fixed seed, so the
 set is the same on every run.  Complements the hand-picked shapes with combinations no single
-test names; every draw is a valid input."""
+test names; every draw is a valid input.  out, lse and the workspace sit between guard bytes that
+must be unchanged after every call."""
 import random
 
 import numpy as np
@@ -44,13 +45,43 @@ for _i in range(N_CASES):
     CASES.append(draw(_rng))
 
 
+GUARD = 4096  # guard bytes on each side of out, lse and the workspace
+GUARD_BYTE = 0xA5
+
+
+def guarded(nbytes):
+    """A uint8 GPU buffer of nbytes between two guard regions of GUARD bytes filled with
+    GUARD_BYTE; returns (whole buffer, interior view).  The interior starts 4 KB in, so it keeps
+    the 256-byte alignment the workspace needs."""
+    whole = torch.full((GUARD + nbytes + GUARD,), GUARD_BYTE, dtype=torch.uint8, device="cuda")
+    return whole, whole[GUARD:GUARD + nbytes]
+
+
+def guards_intact(whole):
+    g = torch.cat([whole[:GUARD], whole[-GUARD:]])
+    return bool((g == GUARD_BYTE).all())
+
+
 @pytest.mark.parametrize("idx", range(N_CASES))
 def test_random_shape(idx):
     kw, parts = CASES[idx]
     print(f"[random {idx}] {kw} partitions={parts}", flush=True)
     case = workloads.custom_case(seed=5000 + idx, device="cuda", **kw)
-    out = fd.decode_case(case, num_partitions=parts)
+    # out, lse and the workspace sit between guard bytes: no kernel may write outside them
+    q_shape = tuple(case.q.shape)
+    n_out, n_lse = int(np.prod(q_shape)), int(np.prod(q_shape[:-1]))
+    out_whole, out_bytes = guarded(4 * n_out)
+    lse_whole, lse_bytes = guarded(4 * n_lse)
+    need = fd.workspace_bytes(case.batch, case.hq, case.hkv, case.d, case.max_seq_len, case.block_size,
+                              case.kv_dtype, parts, case.nq)
+    ws_whole, ws = guarded(need)
+    out = out_bytes.view(torch.float32).view(q_shape)
+    lse = lse_bytes.view(torch.float32).view(q_shape[:-1])
+    fd.decode_case(case, out=out, lse=lse, workspace=ws, num_partitions=parts)
     torch.cuda.synchronize()
+    assert guards_intact(out_whole), "write outside out"
+    assert guards_intact(lse_whole), "write outside lse"
+    assert guards_intact(ws_whole), "write outside the workspace"
     ref, _ = oracle.decode_attention(oracle.Problem.from_case(case))
     got = out.double().cpu().numpy()
     assert np.isfinite(got).all()
