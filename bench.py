@@ -88,16 +88,19 @@ def kernel_hash() -> str:
 
 
 def partition_kernel_name(case) -> str:
-    """Which partition kernel the library's plan runs for this case (E4M3 KV, head_dim 128 and
-    a multiple of 64 query heads per kv head take the wide-group kernel, with one query token)."""
-    wide = case.kv_dtype == "fp8_e4m3" and case.d == 128 and case.group % 64 == 0 and case.nq == 1
+    """Which partition kernel the library's plan runs for this case (E4M3 or INT8 KV, head_dim 128
+    and a multiple of 64 query heads per kv head take the wide-group kernel, with one query token)."""
+    wide = case.kv_dtype in ("fp8_e4m3", "int8") and case.d == 128 and case.group % 64 == 0 and case.nq == 1
     return "wide_partition_kernel" if wide else "partition_kernel"
 
 
 def compute_note(case) -> str:
     """The arithmetic the partition kernel runs for this case's dtypes."""
-    qk = {"fp8_e4m3": f"E4M3 K -> {case.q_dtype} MFMA q.k, f16 MFMA p.v",
-          "int8": "INT8 K/V -> f16 (exact) MFMA q.k (q as f16) and p.v",
+    wide = partition_kernel_name(case) == "wide_partition_kernel"
+    qk = {"fp8_e4m3": ("E4M3 K on FP8 MFMAs with q as exact E4M3 terms, f16 MFMA p.v" if wide
+                       else f"E4M3 K -> {case.q_dtype} MFMA q.k, f16 MFMA p.v"),
+          "int8": ("INT8 K on int8 MFMAs with q as three int8 terms, V -> f16 (exact) MFMA p.v" if wide
+                   else "INT8 K/V -> f16 (exact) MFMA q.k (q scaled into f16) and p.v"),
           "f16": "f16 MFMA q.k and p.v",
           "bf16": "bf16 MFMA q.k, bf16 MFMA p.v (p split into two bf16 terms)"}[case.kv_dtype]
     return qk + ", f32 softmax and accumulate"

@@ -41,11 +41,14 @@ struct Plan {
     int nparts;  // partition workgroups
 };
 
-// Groups of 64+ query heads per kv head with E4M3 KV and head_dim 128 take the wide-group
-// kernel: 32 heads per wave, and 2 or 4 waves of one kv head share every K/V tile through LDS.
-// (A window of several query tokens per sequence takes the 16-column kernel.)
-bool use_wide(int group, int head_dim, int kv_dtype, int nq) {
-    return nq == 1 && kv_dtype == FD_FP8_E4M3 && head_dim == 128 && group % 64 == 0;
+// Groups of 64+ query heads per kv head with E4M3 or INT8 KV and head_dim 128 take the
+// wide-group kernel: 32 heads per wave, and 2 or 4 waves of one kv head share every K/V tile
+// through LDS.  (A window of several query tokens per sequence takes the 16-column kernel.)
+// (the wide kernel forms in-tile row offsets with 24-bit multiplies: a cache row of all kv
+// heads, hkv * 128 bytes, stays below 2^24)
+bool use_wide(int group, int hkv, int head_dim, int kv_dtype, int nq) {
+    return nq == 1 && (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) && head_dim == 128 && group % 64 == 0 &&
+           hkv < (1 << 16);
 }
 
 bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
@@ -65,7 +68,7 @@ Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, i
                int num_partitions) {
     Plan pl;
     const int group = hq / hkv, cols = group * nq;
-    pl.wide = use_wide(group, head_dim, kv_dtype, nq);
+    pl.wide = use_wide(group, hkv, head_dim, kv_dtype, nq);
     if (pl.wide) {
         pl.hb = fd::kWideHeadBlock;
         pl.nhb = group / pl.hb;
@@ -323,7 +326,7 @@ int step(const void *q, int num_query, const void *k_cache, const void *v_cache,
     }
 
     if (t_prof_begin) (void)hipEventRecord(t_prof_begin, stream);
-    const hipError_t perr = pl.wide ? fd::launch_wide_partition(p, q_dtype, scale_mode, stream)
+    const hipError_t perr = pl.wide ? fd::launch_wide_partition(p, kv_dtype, q_dtype, scale_mode, stream)
                                     : fd::launch_partition(p, kv_dtype, q_dtype, scale_mode, stream);
     if (perr != hipSuccess) return FD_ERR_LAUNCH;
     if (t_prof_end) (void)hipEventRecord(t_prof_end, stream);

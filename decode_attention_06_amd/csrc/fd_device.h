@@ -17,6 +17,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(16))) int i32x16_t;
 typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 
 enum { KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3, KV_I8 = 4 };

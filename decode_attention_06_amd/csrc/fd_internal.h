@@ -65,9 +65,9 @@ struct AppendParams {
 hipError_t launch_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode,
                             hipStream_t stream);
 hipError_t launch_combine(const Params &p, hipStream_t stream);
-// Wide-group variant (defined in fd_wide.hip): E4M3 KV, head_dim 128, hb = kWideHeadBlock,
+// Wide-group variant (defined in fd_wide.hip): E4M3 or INT8 KV, head_dim 128, hb = kWideHeadBlock,
 // wpg 2 or 4 head blocks of one kv head per workgroup.
-hipError_t launch_wide_partition(const Params &p, int q_dtype, int scale_mode, hipStream_t stream);
+hipError_t launch_wide_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode, hipStream_t stream);
 hipError_t launch_fp8_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
 hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, int kind, hipStream_t stream);
 // fd_append.hip: new_dtype 0 f32 / 1 f16 / 2 bf16; kv_dtype and scale_mode as the FD_ codes.

@@ -160,7 +160,7 @@ __device__ __forceinline__ void wg_barrier() {
 
 }  // namespace
 
-template <int WPG, int NSLOT, int QT, int SCALE, bool PAGED, bool B16>
+template <int KVT, int WPG, int NSLOT, int QT, int SCALE, bool PAGED, bool B16>
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
 void wide_partition_kernel(Params p) {
     using LY = WideLayout<WPG, SCALE>;
@@ -170,7 +170,8 @@ void wide_partition_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * LY::SLOT];
     __shared__ int sh_prefix[kWideLdsBatch + 1];
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // (the wave index is uniform: kept in a scalar register, so per-wave choices are scalar)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int li = lane & 31, lh = lane >> 5;
     const int64_t wg = blockIdx.x, W = gridDim.x;
     const int groups = p.groups;
@@ -212,10 +213,12 @@ void wide_partition_kernel(Params p) {
     const uint32_t row_bytes = (uint32_t)p.hkv * D;  // bytes per cache row (all kv heads)
 
     // ---- tile cursors: one issuing copies NSLOT-1 tiles ahead, one computing
+    // kvh: kv head of the unit group grp (kept with the cursor: it changes only with the group)
     struct Cursor {
         int64_t pos;
-        int b, Tb, grp, tt, n;
+        int b, Tb, grp, tt, n, kvh;
     };
+    auto group_kvh = [&](int grp) -> int { return uni((grp * WPG) / p.nhb); };
     auto locate = [&](Cursor &k, int64_t at) {
         k.pos = at;
         if (lds_prefix) {
@@ -253,6 +256,7 @@ void wide_partition_kernel(Params p) {
             }
         }
         k.n = max(0, min(ld_uniform(p.seq_len, k.b), p.max_seq_len));
+        k.kvh = group_kvh(k.grp);
     };
     // one tile forward (crossing unit groups and sequences); false, unmoved, at the range end
     auto step = [&](Cursor &k) -> bool {
@@ -267,70 +271,82 @@ void wide_partition_kernel(Params p) {
                 } while ((k.Tb = lds_prefix ? uni(sh_prefix[k.b + 1] - sh_prefix[k.b]) : seq_tiles_u(p, k.b)) == 0);
                 k.n = max(0, min(ld_uniform(p.seq_len, k.b), p.max_seq_len));
             }
+            k.kvh = group_kvh(k.grp);
         }
         return true;
     };
     auto next_slot = [](int si) -> int { return si + 1 == NSLOT ? 0 : si + 1; };
 
     // ---- copies of one tile into a ring slot (this wave's share)
+    // block sizes are 16, 32 or 64: block index and offset by shift and mask
+    const int bsh = PAGED ? (B16 ? 4 : uni(__builtin_ctz((unsigned)p.block_size))) : 0;
     auto issue = [&](const Cursor &k, int si) {
         const int t0 = k.tt * kTile;
         const int last = min(k.n - t0, kTile) - 1;  // rows past it repeat it (valid; masked later)
         // first cache rows of the tile's two 16-token halves (blocks of 16 tokens: two blocks)
         int64_t row0, row1;
         if constexpr (PAGED) {
-            row0 = (int64_t)ld_uniform(p.block_table, (size_t)k.b * p.max_blocks + t0 / p.block_size) *
-                       p.block_size + (t0 % p.block_size);
+            row0 = ((int64_t)ld_uniform(p.block_table, (size_t)k.b * p.max_blocks + (t0 >> bsh)) << bsh) +
+                   (t0 & ((1 << bsh) - 1));
             if constexpr (B16)
                 row1 = last < 16 ? row0 + 16
-                                 : (int64_t)ld_uniform(p.block_table, (size_t)k.b * p.max_blocks + (t0 + 16) / 16) * 16;
+                                 : (int64_t)ld_uniform(p.block_table, (size_t)k.b * p.max_blocks + (t0 >> 4) + 1) << 4;
             else
                 row1 = row0 + 16;
         } else {
             row0 = (int64_t)ld_uniform(p.kv_start, k.b) + t0;
             row1 = row0 + 16;
         }
-        auto cache_row = [&](int tok) -> int64_t {
-            if constexpr (!B16) return row0 + tok;
-            return tok < 16 ? row0 + tok : row1 + (tok - 16);
-        };
-        const int kvh = (k.grp * WPG) / p.nhb;
         uint8_t *slot = ring + si * LY::SLOT;
-        const uint8_t *kb = (const uint8_t *)p.k + (size_t)kvh * D;
-        const uint8_t *vb = (const uint8_t *)p.v + (size_t)kvh * D;
+        // uniform base of the tile's first row; each lane adds a 32-bit offset (a tile of 32 rows
+        // inside one block, or two 16-row blocks, each contiguous)
+        const uint8_t *kb = (const uint8_t *)p.k + (size_t)k.kvh * D + row0 * row_bytes;
+        const uint8_t *vb = (const uint8_t *)p.v + (size_t)k.kvh * D + row0 * row_bytes;
+        const int64_t jump = B16 ? (row1 - row0 - 16) * row_bytes : 0;  // second block's shift
 #pragma unroll
         for (int u = 0; u < LY::OPS_KV; u++) {
             const int o = wave * LY::OPS_KV + u;  // copies 0..3: K rows 8o..8o+7; 4..7: V rows
             const int row = 8 * (o & 3) + (lane >> 3);
-            const size_t src = (size_t)cache_row(min(row, last)) * row_bytes;
+            const int r = min(row, last);
+            const uint32_t off = __umul24((uint32_t)r, row_bytes);
+            const int64_t shift = (B16 && r >= 16) ? jump : 0;
             if (o < 4)
-                copy16_to_lds(kb + src + 16 * ((lane & 7) ^ (row & 7)), slot + o * 1024);
+                copy16_to_lds(kb + shift + off + 16 * ((lane & 7) ^ (row & 7)), slot + o * 1024);
             else
-                copy16_to_lds(vb + src + 16 * (lane & 7), slot + LY::KV_BYTES + (o - 4) * 1024);
+                copy16_to_lds(vb + shift + off + 16 * (lane & 7), slot + LY::KV_BYTES + (o - 4) * 1024);
         }
         if constexpr (SCALE == SC_TOKEN_HEAD) {
             const int t = min(lane & 31, last);
-            const float *sb = (lane < 32 ? p.k_scale : p.v_scale) + kvh + (size_t)cache_row(t) * p.hkv;
+            const int64_t crow = B16 && t >= 16 ? row1 + (t - 16) : row0 + t;
+            const float *sb = (lane < 32 ? p.k_scale : p.v_scale) + k.kvh + (size_t)crow * p.hkv;
             copy4_to_lds(sb, slot + 2 * LY::KV_BYTES + wave * LY::SC_BYTES);
         }
     };
 
     // ---- per-lane LDS offsets within a slot
     const uint32_t ring0 = lds_addr(ring);
-    // K operand of the FP8 q.k^T MFMA of k-step ks: token li, d = 64 ks + 32 lh + 0..31, i.e. the
-    // row's 16-byte chunks 4 ks + 2 lh and 4 ks + 2 lh + 1 (stored at chunk ^ (li & 7))
+    // K operand of the q.k^T MFMA: token li; E4M3 (32x32x64) k-step ks = q / 2: d = 64 ks + 32 lh
+    // + 0..31, the row's 16-byte chunks 4 ks + 2 lh and 4 ks + 2 lh + 1; INT8 (32x32x32) k-step
+    // ks = q: d = 32 ks + 16 lh + 0..15, chunk 2 ks + lh.  Chunk c of row r is stored at c ^ (r & 7).
+    constexpr bool I8 = KVT == KV_I8;
     uint32_t koff[4];
 #pragma unroll
-    for (int q = 0; q < 4; q++) koff[q] = li * LY::ROWB + 16 * ((4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
+    for (int q = 0; q < 4; q++)
+        koff[q] = li * LY::ROWB + 16 * ((I8 ? 2 * q + lh : 4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
     const uint32_t voff = LY::KV_BYTES + (4 * lh) * LY::ROWB + 4 * li;
     const uint32_t soff = 2 * LY::KV_BYTES + wave * LY::SC_BYTES + 16 * lh;
 
     // ---- per-segment state
-    // q operand of q.k^T: NQT E4M3 terms whose sum is q * 2^eq exactly (bf16 q: 2 terms, f16 q: 3),
-    // for head li at d = 64 ks + 32 lh + j in byte j of qf8[t][ks]; the head's score multiplier
-    // qk_head carries 2^-eq (and, for a negative per-tensor k scale, q carries the sign)
-    constexpr int NQT = QT == KV_BF16 ? 2 : 3;
-    i32x8_t qf8[NQT][2];
+    // q operand of q.k^T, for head li; the head's score multiplier qk_head carries 2^-eq (and, for
+    // a negative per-tensor k scale, q carries the sign):
+    //   E4M3 KV: NQT E4M3 terms whose sum is q * 2^eq exactly (bf16 q: 2 terms, f16 q: 3), d =
+    //            64 ks + 32 lh + j in byte j of qf8[t][ks] (32 bytes per term and k-step);
+    //   INT8 KV: three int8 terms, base-128 digits with 2^14 t1 + 2^7 t2 + t3 = q * 2^eq to within
+    //            0.5 (the largest |q * 2^eq| lies in [2^19, 2^20), so q is held to 2^-20 of its
+    //            largest value), d = 32 ks + 16 lh + j in byte j of qi8[t][ks].
+    constexpr int NQT = I8 ? 3 : (QT == KV_BF16 ? 2 : 3);
+    i32x8_t qf8[I8 ? 1 : NQT][2];
+    u32x4_t qi8[I8 ? 3 : 1][I8 ? 4 : 1];
     float qk_head = qk_scale;
     f32x16_t acc[4];
     float m_run = -INFINITY, l_run = 0.0f;
@@ -340,10 +356,13 @@ void wide_partition_kernel(Params p) {
         const int u_in = grp * WPG + wave;
         const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
         const int head = kvh * p.group + hb * kWideHeadBlock + li;
-        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + 32 * lh;
-        u32x4_t raw[8];  // raw[4 ks + c]: d = 64 ks + 32 lh + 8 c + 0..7
+        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + (I8 ? 16 : 32) * lh;
+        // E4M3: raw[4 ks + c] holds d = 64 ks + 32 lh + 8 c + 0..7; INT8: raw[2 ks + c] holds
+        // d = 32 ks + 16 lh + 8 c + 0..7
+        u32x4_t raw[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) raw[i] = *(const u32x4_t *)(qrow + 64 * (i >> 2) + 8 * (i & 3));
+        for (int i = 0; i < 8; i++)
+            raw[i] = *(const u32x4_t *)(qrow + (I8 ? 32 * (i >> 1) + 8 * (i & 1) : 64 * (i >> 2) + 8 * (i & 3)));
         // complete here (a drain, once per segment), so that no load is pending at the top of the
         // tile loop and the compiler adds no wait on the in-flight tile copies there
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -358,9 +377,11 @@ void wide_partition_kernel(Params p) {
                 mx = max(mx, max(w & 0xFFFFu, w >> 16));
             }
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
-        // 2^eq puts the largest |q| in [2^7, 2^8), inside E4M3's range (largest finite 448)
+        // 2^eq puts the largest |q| in [2^7, 2^8), inside E4M3's range (largest finite 448); for the
+        // INT8 terms in [2^19, 2^20)
+        const int target = I8 ? 19 : 7;
         int eq = 0;
-        if (mx != 0) eq = QT == KV_BF16 ? 134 - (int)(mx >> 7) : 22 - (int)(mx >> 10);
+        if (mx != 0) eq = QT == KV_BF16 ? target + 127 - (int)(mx >> 7) : target + 15 - (int)(mx >> 10);
         // per-tensor scale: the multiplier is kept >= 0 (the tile max is then taken on raw scores)
         const bool flip = SCALE == SC_TENSOR && qk_scale < 0.0f;
         qk_head = __builtin_amdgcn_ldexpf(flip ? -qk_scale : qk_scale, -eq);
@@ -380,21 +401,40 @@ void wide_partition_kernel(Params p) {
                     const float v = to_f32((h & 1) ? (w >> 16) : (w & 0xFFFFu));
                     x[h] = __builtin_amdgcn_ldexpf(flip ? -v : v, eq);
                 }
+                if constexpr (I8) {
+                    // signed base-128 digits, each the nearest integer to what is left (|t| <= 64; the
+                    // remainders are exact in fp32); bytes j = 8 c + 4 e2 + h of k-step i / 2
+                    uint32_t w1 = 0, w2 = 0, w3 = 0;
 #pragma unroll
-                for (int t = 0; t < NQT; t++) {
-                    // nearest E4M3 values (exact hardware convert, ties to even); the remainder is
-                    // exact in fp32 and has few enough significant bits for the next term
-                    i16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[0], x[1], 1.0f, false);
-                    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[2], x[3], 1.0f, true);
-                    const uint32_t cw = __builtin_bit_cast(uint32_t, c);
-                    qf8[t][i >> 2][2 * (i & 3) + e2] = (int)cw;
-                    if (t + 1 < NQT) {
-                        const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, false);
-                        const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, true);
-                        x[0] -= lo[0];
-                        x[1] -= lo[1];
-                        x[2] -= hi[0];
-                        x[3] -= hi[1];
+                    for (int h = 0; h < 4; h++) {
+                        const float t1 = __builtin_rintf(x[h] * (1.0f / 16384.0f));
+                        const float r1 = x[h] - 16384.0f * t1;
+                        const float t2 = __builtin_rintf(r1 * (1.0f / 128.0f));
+                        const float t3 = __builtin_rintf(r1 - 128.0f * t2);
+                        w1 |= ((uint32_t)(int)t1 & 0xFFu) << (8 * h);
+                        w2 |= ((uint32_t)(int)t2 & 0xFFu) << (8 * h);
+                        w3 |= ((uint32_t)(int)t3 & 0xFFu) << (8 * h);
+                    }
+                    qi8[0][i >> 1][2 * (i & 1) + e2] = w1;
+                    qi8[1][i >> 1][2 * (i & 1) + e2] = w2;
+                    qi8[2][i >> 1][2 * (i & 1) + e2] = w3;
+                } else {
+#pragma unroll
+                    for (int t = 0; t < NQT; t++) {
+                        // nearest E4M3 values (exact hardware convert, ties to even); the remainder is
+                        // exact in fp32 and has few enough significant bits for the next term
+                        i16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[0], x[1], 1.0f, false);
+                        c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[2], x[3], 1.0f, true);
+                        const uint32_t cw = __builtin_bit_cast(uint32_t, c);
+                        qf8[t][i >> 2][2 * (i & 3) + e2] = (int)cw;
+                        if (t + 1 < NQT) {
+                            const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, false);
+                            const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, true);
+                            x[0] -= lo[0];
+                            x[1] -= lo[1];
+                            x[2] -= hi[0];
+                            x[3] -= hi[1];
+                        }
                     }
                 }
             }
@@ -426,19 +466,49 @@ void wide_partition_kernel(Params p) {
             }
         };
 
-        // ---- scores S[token][head] = K . (q * 2^eq) on FP8 MFMAs straight from the ring's E4M3
-        // bytes (no conversion): two 64-deep k-steps, NQT terms of q each
+        // ---- scores S[token][head] = K . (q * 2^eq) straight from the ring's bytes (no conversion)
         f32x16_t S;
+        if constexpr (I8) {
+            // INT8: 2^14 (K . t1) + (128 (K . t2) + K . t3) on 32x32x32 int8 MFMAs, four 32-deep
+            // k-steps per term; each dot product is exact in int32 (|K . t| <= 128 * 127 * 64 <
+            // 2^20), so is 128 (K . t2) + K . t3 (< 2^28), and the two parts meet in one fp32 fma
+            i32x16_t Si, Sl;
 #pragma unroll
-        for (int r = 0; r < 16; r++) S[r] = 0.0f;
+            for (int r = 0; r < 16; r++) Si[r] = 0;
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            const u32x4_t k0 = kr[2 * ks], k1 = kr[2 * ks + 1];
-            const i32x8_t a = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
-                               (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+            for (int r = 0; r < 16; r++) Sl[r] = 0;
 #pragma unroll
-            for (int t = 0; t < NQT; t++)  // E4M3 x E4M3, both block scales 2^0 (E8M0 127)
-                S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[t][ks], S, 0, 0, 0, 127, 0, 127);
+            for (int ks = 0; ks < 4; ks++)
+                Si = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, kr[ks]),
+                                                           __builtin_bit_cast(i32x4_t, qi8[0][ks]), Si, 0, 0, 0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++)
+                Sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, kr[ks]),
+                                                           __builtin_bit_cast(i32x4_t, qi8[1][ks]), Sl, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; r++) Sl[r] <<= 7;
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++)
+                Sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, kr[ks]),
+                                                           __builtin_bit_cast(i32x4_t, qi8[2][ks]), Sl, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int hi = Si[r], lo = Sl[r];  // (elements to scalars before converting)
+                S[r] = __builtin_fmaf((float)hi, 16384.0f, (float)lo);
+            }
+        } else {
+            // E4M3: FP8 MFMAs, two 64-deep k-steps, NQT terms of q each
+#pragma unroll
+            for (int r = 0; r < 16; r++) S[r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const u32x4_t k0 = kr[2 * ks], k1 = kr[2 * ks + 1];
+                const i32x8_t a = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                                   (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+#pragma unroll
+                for (int t = 0; t < NQT; t++)  // E4M3 x E4M3, both block scales 2^0 (E8M0 127)
+                    S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[t][ks], S, 0, 0, 0, 127, 0, 127);
+            }
         }
         float ksc[16];
         if constexpr (SCALE == SC_TOKEN_HEAD) read_scales(ksc, sbase + soff);
@@ -541,12 +611,21 @@ void wide_partition_kernel(Params p) {
             uint32_t a[4][4];
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                const uint32_t x = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x05010400u);
-                const uint32_t y = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x07030602u);
-                a[0][u] = cvt_fp8x2<KV_F16, false>(x);
-                a[1][u] = cvt_fp8x2<KV_F16, true>(x);
-                a[2][u] = cvt_fp8x2<KV_F16, false>(y);
-                a[3][u] = cvt_fp8x2<KV_F16, true>(y);
+                if constexpr (I8) {
+                    // byte k of rows 2u, 2u+1 -> bytes 0 and 2 of a dword (zeros between: selector
+                    // 0x0C) -> the exact f16 pair of the two codes
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        a[k][u] = i8x2_to_f16x2(__builtin_amdgcn_perm(w[2 * u + 1], w[2 * u],
+                                                                      0x0C000C00u | ((4u + k) << 16) | (uint32_t)k));
+                } else {
+                    const uint32_t x = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x05010400u);
+                    const uint32_t y = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x07030602u);
+                    a[0][u] = cvt_fp8x2<KV_F16, false>(x);
+                    a[1][u] = cvt_fp8x2<KV_F16, true>(x);
+                    a[2][u] = cvt_fp8x2<KV_F16, false>(y);
+                    a[3][u] = cvt_fp8x2<KV_F16, true>(y);
+                }
             }
 #pragma unroll
             for (int dt = 0; dt < 4; dt++)
@@ -647,36 +726,41 @@ void wide_partition_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- host-side dispatch
-template <int WPG, int QT, int SCALE>
+template <int KVT, int WPG, int QT, int SCALE>
 static hipError_t launch_w(const Params &p, hipStream_t stream) {
     // tiles in flight per workgroup: NSLOT-1; the ring is sized so that three workgroups fit
     // in one CU's 160 KB of LDS
     constexpr int NSLOT = WPG == 2 ? 3 : (SCALE == SC_TOKEN_HEAD ? 5 : 6);
     dim3 grid(p.nparts), block(64 * WPG);
     if (p.block_table && p.block_size == 16)  // 32-token tiles span two blocks
-        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
     else if (p.block_table)
-        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, true, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, false>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((wide_partition_kernel<WPG, NSLOT, QT, SCALE, false, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, false, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
-template <int WPG>
+template <int KVT, int WPG>
 static hipError_t launch_wq(const Params &p, int qt, int sc, hipStream_t stream) {
     if (qt == KV_BF16) {
-        if (sc == SC_TENSOR) return launch_w<WPG, KV_BF16, SC_TENSOR>(p, stream);
-        return launch_w<WPG, KV_BF16, SC_TOKEN_HEAD>(p, stream);
+        if (sc == SC_TENSOR) return launch_w<KVT, WPG, KV_BF16, SC_TENSOR>(p, stream);
+        return launch_w<KVT, WPG, KV_BF16, SC_TOKEN_HEAD>(p, stream);
     }
-    if (sc == SC_TENSOR) return launch_w<WPG, KV_F16, SC_TENSOR>(p, stream);
-    return launch_w<WPG, KV_F16, SC_TOKEN_HEAD>(p, stream);
+    if (sc == SC_TENSOR) return launch_w<KVT, WPG, KV_F16, SC_TENSOR>(p, stream);
+    return launch_w<KVT, WPG, KV_F16, SC_TOKEN_HEAD>(p, stream);
 }
 
-hipError_t launch_wide_partition(const Params &p, int q_dtype, int scale_mode, hipStream_t stream) {
+hipError_t launch_wide_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode, hipStream_t stream) {
     if (p.d != 128 || p.hb != kWideHeadBlock || (p.wpg != 2 && p.wpg != 4) || p.nhb % p.wpg)
         return hipErrorInvalidValue;
-    if (p.wpg == 4) return launch_wq<4>(p, q_dtype, scale_mode, stream);
-    return launch_wq<2>(p, q_dtype, scale_mode, stream);
+    if (kv_dtype != KV_FP8 && kv_dtype != KV_I8) return hipErrorInvalidValue;
+    if (kv_dtype == KV_I8) {
+        if (p.wpg == 4) return launch_wq<KV_I8, 4>(p, q_dtype, scale_mode, stream);
+        return launch_wq<KV_I8, 2>(p, q_dtype, scale_mode, stream);
+    }
+    if (p.wpg == 4) return launch_wq<KV_FP8, 4>(p, q_dtype, scale_mode, stream);
+    return launch_wq<KV_FP8, 2>(p, q_dtype, scale_mode, stream);
 }
 
 }  // namespace fd

@@ -59,9 +59,9 @@ def test_partition_and_combine_kernels_do_not_spill():
 def test_wide_kernel_spills():
     sp = kernel_spills(os.path.join(BUILD, "fd_wide.hip.o"))
     assert sp
-    # template arguments <WPG, NSLOT, QT, SCALE, PAGED, B16>: SCALE 1 = per tensor, 2 = per token
+    # template arguments <KVT, WPG, NSLOT, QT, SCALE, PAGED, B16>: SCALE 1 = per tensor, 2 = per token
     for k, v in sp.items():
-        m = re.search(r"wide_partition_kernelILi(\d)ELi(\d)ELi(\d)ELi(\d)E", k)
+        m = re.search(r"wide_partition_kernelILi(\d)ELi(\d)ELi(\d)ELi(\d)ELi(\d)E", k)
         assert m, k
-        scale = int(m.group(4))
+        scale = int(m.group(5))
         assert v <= (0 if scale == 1 else 8), (k, v)

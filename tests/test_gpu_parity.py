@@ -125,6 +125,15 @@ SMALL = [
                               scale="none", block_size=16)),
     ("bs16_wide_g128_tok", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1000, 31], kv="fp8_e4m3",
                                 q="bf16", scale="token_head", block_size=16)),
+    # wide-group kernel with INT8 KV (int8 MFMAs for q.k^T on the raw codes, q in three int8 terms)
+    ("wide_i8_g64_tok", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[1000, 33, 4097], kv="int8",
+                             q="bf16", scale="token_head", block_size=64)),
+    ("wide_i8_g128_tok_contig_f16q", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[300, 1], kv="int8",
+                                          q="f16", scale="token_head", paged=False, block_size=0)),
+    ("wide_i8_g256_tensor_bs32", dict(batch=2, hq=256, hkv=1, d=128, seq_lens=[700, 64], kv="int8",
+                                      q="bf16", scale="tensor", block_size=32)),
+    ("bs16_wide_i8_g128_tensor", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1000, 31], kv="int8",
+                                      q="bf16", scale="tensor", block_size=16)),
     ("bs16_wide_g64_tensor", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[65, 300, 1], kv="fp8_e4m3",
                                   q="bf16", scale="tensor", block_size=16)),
     # one long sequence over few units: many pieces per row, merged by several combine waves
@@ -177,14 +186,15 @@ def test_int8_length_edges(n, bs):
         check_case(f"i8_len{n}_bs{bs}/p{parts}", case, num_partitions=parts)
 
 
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
 @pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 191, 192, 193, 4095])
-def test_wide_length_edges(n):
+def test_wide_length_edges(n, kv):
     lens = [n, 7, n]
     case = workloads.custom_case(seed=100 + n, device="cuda", batch=3, hq=128, hkv=1, d=128, seq_lens=lens,
-                                 kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64,
+                                 kv=kv, q="bf16", scale="token_head", block_size=64,
                                  max_seq_len=max(lens + [1]))
     for parts in (0, 3):
-        check_case(f"wide_len{n}/p{parts}", case, num_partitions=parts)
+        check_case(f"wide_{kv}_len{n}/p{parts}", case, num_partitions=parts)
 
 
 @pytest.mark.parametrize("wide", [False, True])
@@ -208,13 +218,14 @@ def test_block16_ragged_mix():
         check_case(f"bs16_ragged/p{parts}", case, num_partitions=parts)
 
 
-def test_wide_ragged_mix():
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
+def test_wide_ragged_mix(kv):
     lens = [0, 1, 5000, 33, 0, 64, 2047, 12000, 31, 0, 700, 96]
     case = workloads.custom_case(seed=22, device="cuda", batch=len(lens), hq=128, hkv=2, d=128,
-                                 seq_lens=lens, kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 seq_lens=lens, kv=kv, q="bf16", scale="token_head",
                                  block_size=32)
     for parts in (1, 7, 100, 1024):
-        check_case(f"wide_ragged/p{parts}", case, num_partitions=parts)
+        check_case(f"wide_{kv}_ragged/p{parts}", case, num_partitions=parts)
 
 
 def test_more_partitions_than_tiles():
@@ -267,27 +278,31 @@ def test_partition_kernel_batch_beyond_lds_prefix_table():
         check_case(f"batch4100/p{parts}", case, num_partitions=parts)
 
 
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
 @pytest.mark.parametrize("k_mult,v_mult", [(-1.0, 1.0), (-1.0, -1.0), (0.0, 1.0)])
 @pytest.mark.parametrize("hq", [16, 128])
-def test_per_tensor_scale_signs(k_mult, v_mult, hq):
+def test_per_tensor_scale_signs(k_mult, v_mult, hq, kv):
     # negative or zero per-tensor scales (hq 128: the wide kernel, which scales scores inside the
     # exponent and flips q's sign for a negative scale; hq 16: the 16-head kernel).  A zero k
     # scale makes every score 0: out is the plain mean of the dequantised V rows
     case = workloads.custom_case(seed=31, device="cuda", batch=2, hq=hq, hkv=1, d=128,
-                                 seq_lens=[3000, 77], kv="fp8_e4m3", q="bf16", scale="tensor",
+                                 seq_lens=[3000, 77], kv=kv, q="bf16", scale="tensor",
                                  block_size=64)
     case.k_scale = case.k_scale * k_mult
     case.v_scale = case.v_scale * v_mult
     for parts in (0, 7):
-        check_case(f"scale_signs k{k_mult} v{v_mult} hq{hq}/p{parts}", case, num_partitions=parts)
+        check_case(f"scale_signs {kv} k{k_mult} v{v_mult} hq{hq}/p{parts}", case, num_partitions=parts)
 
 
-def test_peaky_scores():
-    case = workloads.custom_case(seed=10, device="cuda", batch=2, hq=16, hkv=2, d=128,
-                                 seq_lens=[3000, 700], kv="fp8_e4m3", q="bf16", scale="token_head",
+@pytest.mark.parametrize("hq,kv", [(16, "fp8_e4m3"), (128, "fp8_e4m3"), (128, "int8"), (16, "int8")])
+def test_peaky_scores(hq, kv):
+    # q x 4: scores four times larger, the running max moves and the softmax is sharp (hq 128:
+    # the wide kernel, whose q terms then carry more of the score)
+    case = workloads.custom_case(seed=10, device="cuda", batch=2, hq=hq, hkv=2, d=128,
+                                 seq_lens=[3000, 700], kv=kv, q="bf16", scale="token_head",
                                  block_size=64)
     case.q.mul_(4.0)
-    check_case("peaky_q4", case, num_partitions=0)
+    check_case(f"peaky_q4_hq{hq}_{kv}", case, num_partitions=0)
 
 
 @pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
@@ -365,6 +380,11 @@ def test_workload_int8_32k_full():
 def test_workload_mqa_fp8_128k_full():
     # every output row (4 sequences x 128 heads) against the oracle on the host's threads
     check_case("mqa_fp8_128k", workloads.make_case("mqa_fp8_128k", device="cuda"))
+
+
+def test_workload_mqa_i8_128k_full():
+    # INT8 KV, the same shape (the wide-group kernel's int8 path)
+    check_case("mqa_i8_128k", workloads.make_case("mqa_i8_128k", device="cuda"))
 
 
 def test_workload_ragged_fp8_full():

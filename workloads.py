@@ -18,6 +18,7 @@ Workloads (sizes as specified for the decode workloads this library targets):
 * ``ragged_fp8``        batch 256, 90 % seq_len ~ U[256, 2048] and 10 % ~ U[32K, 128K],
                         32 q / 8 kv heads, head_dim 128, E4M3 KV, block_size 32, shuffled blocks.
 * ``int8_32k``          ``fp8_32k`` with INT8 KV (per-(token, kv-head) scales).
+* ``mqa_i8_128k``       ``mqa_fp8_128k`` with INT8 KV (one per-tensor scale).
 * ``verify_fp8_32k``    ``fp8_32k`` with a window of 4 query tokens per sequence (a speculative-
                         decoding verify pass over 4 draft tokens already in the cache).
 
@@ -77,6 +78,8 @@ WORKLOADS = {
                        q="bf16", block_size=32, scale="token_head", paged=True),
     "int8_32k": dict(batch=32, hq=64, hkv=8, d=128, lens=("loguniform", 1024, 32768), kv="int8",
                      q="bf16", block_size=64, scale="token_head", paged=True),
+    "mqa_i8_128k": dict(batch=4, hq=128, hkv=1, d=128, lens=("fixed", 131072), kv="int8",
+                        q="bf16", block_size=64, scale="tensor", paged=True),
     "verify_fp8_32k": dict(batch=32, hq=64, hkv=8, d=128, lens=("loguniform", 1024, 32768),
                            kv="fp8_e4m3", q="bf16", block_size=64, scale="token_head", paged=True,
                            nq=4),
