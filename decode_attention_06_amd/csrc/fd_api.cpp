@@ -23,7 +23,8 @@ namespace {
 // workgroups per CU instead of three cut those bytes (written, then merged by the combine) by a
 // third, for a step measured ~3 % faster on the 128K MQA workload.
 constexpr long kDefaultWaves = 2048;
-constexpr long kDefaultWavesWide = 2048;
+constexpr long kDefaultWavesWide = 2048;    // 4-wave workgroups: two per CU
+constexpr long kDefaultWavesWide2 = 1536;   // 2-wave workgroups: three per CU (their LDS)
 constexpr int kMaxSeqLen = 1 << 24;
 constexpr int kMaxQueryWindow = 64;  // query tokens per sequence in one call
 
@@ -84,7 +85,9 @@ Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, i
         pl.groups = (int)(ups / pl.wpg);
     }
     const long tt_max = (long)batch * pl.groups * cdiv(max_seq_len, fd::kTile);
-    long W = num_partitions > 0 ? num_partitions : (pl.wide ? kDefaultWavesWide : kDefaultWaves) / pl.wpg;
+    long W = num_partitions > 0
+                 ? num_partitions
+                 : (pl.wide ? (pl.wpg == 2 ? kDefaultWavesWide2 : kDefaultWavesWide) : kDefaultWaves) / pl.wpg;
     if (W > tt_max) W = tt_max;
     if (W < 1) W = 1;
     pl.nparts = (int)W;

@@ -50,6 +50,12 @@ constexpr int kWideLdsBatch = 256;
 // s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 field layout:
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at bits 15:14).
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt lgkmcnt(0) alone
+constexpr int waitcnt_lgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+// f16 staging of a tile's V in p.V operand order: 2 k-steps x 4 d-tiles, 1 KB each
+constexpr int kVStageBlock = 1024;
+constexpr int kVStageBytes = 8 * kVStageBlock;
 
 template <int WPG, int SCALE>
 struct WideLayout {
@@ -123,22 +129,24 @@ __device__ __forceinline__ void lds_read_4x16(u32x4_t (&r)[4], uint32_t a0, uint
         : "memory");
 }
 
-// Eight 4-byte LDS reads from rows {0, 1, 2, 3, 8, 9, 10, 11} (128-byte rows) past a.
-__device__ __forceinline__ void lds_read_v8(uint32_t (&w)[8], uint32_t a) {
+// Four 4-byte LDS reads from four consecutive 128-byte rows past a, complete on return.
+__device__ __forceinline__ void lds_read_rows4(uint32_t (&w)[4], uint32_t a) {
     asm volatile(
-        "ds_read_b32 %0, %8 offset:0\n\t"
-        "ds_read_b32 %1, %8 offset:128\n\t"
-        "ds_read_b32 %2, %8 offset:256\n\t"
-        "ds_read_b32 %3, %8 offset:384\n\t"
-        "ds_read_b32 %4, %8 offset:1024\n\t"
-        "ds_read_b32 %5, %8 offset:1152\n\t"
-        "ds_read_b32 %6, %8 offset:1280\n\t"
-        "ds_read_b32 %7, %8 offset:1408\n\t"
+        "ds_read_b32 %0, %4 offset:0\n\t"
+        "ds_read_b32 %1, %4 offset:128\n\t"
+        "ds_read_b32 %2, %4 offset:256\n\t"
+        "ds_read_b32 %3, %4 offset:384\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]),
-          "=&v"(w[7])
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
         : "v"(a)
         : "memory");
+}
+
+// One 8-byte LDS write (not waited for here: LDS operations of a wave complete in order, and the
+// next LDS read's wait, or the wait before the workgroup barrier, covers it).
+__device__ __forceinline__ void lds_write_8(uint32_t a, uint32_t lo, uint32_t hi) {
+    const u32x2_t v = {lo, hi};
+    asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
 
 // Largest of x over lanes i and i ^ 32 (the two lane halves): one v_permlane32_swap, no LDS.
@@ -165,9 +173,13 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
 void wide_partition_kernel(Params p) {
     using LY = WideLayout<WPG, SCALE>;
     constexpr int D = 128;
-    static_assert(NSLOT >= 3, "the ring needs the slot being read, one being refilled and one in flight");
+    static_assert(NSLOT >= 4, "the ring holds the tile being read, the next one (being converted), one "
+                              "being refilled and at least one more in flight");
     static_assert((NSLOT - 2) * LY::OPS < 64, "vmcnt field is 6 bits");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * LY::SLOT];
+    // V of a tile as f16 in p.V's MFMA operand order, two buffers (the tile being computed and the
+    // next one, converted by all waves of the workgroup together, a quarter each)
+    __shared__ __attribute__((aligned(16))) uint8_t vstage[2 * kVStageBytes];
     __shared__ int sh_prefix[kWideLdsBatch + 1];
 
     // (the wave index is uniform: kept in a scalar register, so per-wave choices are scalar)
@@ -333,7 +345,7 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
     for (int q = 0; q < 4; q++)
         koff[q] = li * LY::ROWB + 16 * ((I8 ? 2 * q + lh : 4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
-    const uint32_t voff = LY::KV_BYTES + (4 * lh) * LY::ROWB + 4 * li;
+    const uint32_t vst0 = lds_addr(vstage);
     const uint32_t soff = 2 * LY::KV_BYTES + wave * LY::SC_BYTES + 16 * lh;
 
     // ---- per-segment state
@@ -450,10 +462,77 @@ void wide_partition_kernel(Params p) {
     };
 
     const int lh4 = 4 * lh;
-    auto compute = [&](int si, int last) {
+    // ---- V of the tile in ring slot si -> f16 staging buffer buf, this wave's share.  Operand
+    // layout: block (ks, dt) of 1 KB holds, for each lane l = (i, hh) of the reading wave, the 8 f16
+    // of d = 4i + dt at tokens 16 ks + 4 hh + {0, 1, 2, 3, 8, 9, 10, 11} (16 bytes at 16 l).  The
+    // tile is four passes j = (ks, hh): in a pass, lane L converts for reader lane 32 hh + L % 32 the
+    // four tokens 16 ks + 4 hh + 8 (L / 32) + 0..3 (one 4-byte read per token row, d = 4 (L % 32) +
+    // 0..3) and writes 8 bytes per d-tile.  Waves take 4 / WPG passes each.
+    auto convert_v = [&](int si, int buf) {
+        const uint32_t vsrc = ring0 + si * LY::SLOT + LY::KV_BYTES;
+        const uint32_t vdst = vst0 + buf * kVStageBytes;
+        const int th = lane >> 5, lv = lane & 31;
+#pragma unroll
+        for (int jj = 0; jj < 4 / WPG; jj++) {
+            const int j = wave * (4 / WPG) + jj;  // wave-uniform
+            const int ks = j >> 1, hh = j & 1;
+            uint32_t w[4];
+            lds_read_rows4(w, vsrc + (16 * ks + 4 * hh + 8 * th) * LY::ROWB + 4 * lv);
+            uint32_t o[4][2];  // [dt][token pair]
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                if constexpr (I8) {
+                    // byte k of rows 2u, 2u+1 -> bytes 0 and 2 of a dword (zeros between: selector
+                    // 0x0C) -> the exact f16 pair of the two codes
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        o[k][u] = i8x2_to_f16x2(__builtin_amdgcn_perm(w[2 * u + 1], w[2 * u],
+                                                                      0x0C000C00u | ((4u + k) << 16) | (uint32_t)k));
+                } else {
+                    const uint32_t x = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x05010400u);
+                    const uint32_t y = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x07030602u);
+                    o[0][u] = cvt_fp8x2<KV_F16, false>(x);
+                    o[1][u] = cvt_fp8x2<KV_F16, true>(x);
+                    o[2][u] = cvt_fp8x2<KV_F16, false>(y);
+                    o[3][u] = cvt_fp8x2<KV_F16, true>(y);
+                }
+            }
+            const uint32_t at = vdst + ks * 4 * kVStageBlock + 16 * (32 * hh + lv) + 8 * th;
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) lds_write_8(at + dt * kVStageBlock, o[dt][0], o[dt][1]);
+        }
+    };
+
+    // K operand of q.k^T for the tile about to be computed (read one tile ahead)
+    u32x4_t kr[4];
+    auto read_k = [&](int si) {
+        const uint32_t b = ring0 + si * LY::SLOT;
+        lds_read_4x16(kr, b + koff[0], b + koff[1], b + koff[2], b + koff[3]);
+    };
+    // the tile in ring slot si (its K already in kr), its V staged in buffer buf; the next tile's V
+    // (ring slot si_next) is converted into the other buffer while the q.k^T MFMAs run, and the
+    // next tile's K is read while the p.V MFMAs run (that tile has landed and was published by
+    // this step's barrier; its slot is refilled two steps later)
+    auto compute = [&](int si, int buf, int last, int si_next) {
         const uint32_t sbase = ring0 + si * LY::SLOT;
-        u32x4_t kr[4];
-        lds_read_4x16(kr, sbase + koff[0], sbase + koff[1], sbase + koff[2], sbase + koff[3]);
+        // p.V's A operands of both k-steps, read now (plain loads: the staging buffer is never a
+        // copy target, so the compiler waits for these reads only where p.V uses them)
+        u32x4_t va[2][4];
+        {
+            const u32x4_t *vp = (const u32x4_t *)(vstage + buf * kVStageBytes) + lane;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) va[ks][dt] = vp[(ks * 4 + dt) * (kVStageBlock / 16)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the next tile's V conversion, placed after the q.k^T MFMAs are issued: its LDS wait and
+        // VALU work run while the matrix unit is busy
+        auto convert_next = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            convert_v(si_next, buf ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+        };
         // per-token scales: element to a scalar before the bit cast (a bit cast straight from a
         // vector element reads element 0 with this compiler)
         auto read_scales = [&](float (&sc)[16], uint32_t at) {
@@ -485,6 +564,7 @@ void wide_partition_kernel(Params p) {
             for (int ks = 0; ks < 4; ks++)
                 Sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, kr[ks]),
                                                            __builtin_bit_cast(i32x4_t, qi8[1][ks]), Sl, 0, 0, 0);
+            convert_next();
 #pragma unroll
             for (int r = 0; r < 16; r++) Sl[r] <<= 7;
 #pragma unroll
@@ -509,6 +589,7 @@ void wide_partition_kernel(Params p) {
                 for (int t = 0; t < NQT; t++)  // E4M3 x E4M3, both block scales 2^0 (E8M0 127)
                     S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[t][ks], S, 0, 0, 0, 127, 0, 127);
             }
+            convert_next();
         }
         float ksc[16];
         if constexpr (SCALE == SC_TOKEN_HEAD) read_scales(ksc, sbase + soff);
@@ -606,31 +687,12 @@ void wide_partition_kernel(Params p) {
                 pp[u] = pack_f16(p0, p1);
             }
             const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
-            uint32_t w[8];
-            lds_read_v8(w, sbase + voff + 16 * ks * LY::ROWB);
-            uint32_t a[4][4];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                if constexpr (I8) {
-                    // byte k of rows 2u, 2u+1 -> bytes 0 and 2 of a dword (zeros between: selector
-                    // 0x0C) -> the exact f16 pair of the two codes
-#pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        a[k][u] = i8x2_to_f16x2(__builtin_amdgcn_perm(w[2 * u + 1], w[2 * u],
-                                                                      0x0C000C00u | ((4u + k) << 16) | (uint32_t)k));
-                } else {
-                    const uint32_t x = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x05010400u);
-                    const uint32_t y = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x07030602u);
-                    a[0][u] = cvt_fp8x2<KV_F16, false>(x);
-                    a[1][u] = cvt_fp8x2<KV_F16, true>(x);
-                    a[2][u] = cvt_fp8x2<KV_F16, false>(y);
-                    a[3][u] = cvt_fp8x2<KV_F16, true>(y);
-                }
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++)
-                acc[dt] = mfma32_f16(u32x4_t{a[dt][0], a[dt][1], a[dt][2], a[dt][3]}, pop, acc[dt]);
+            for (int dt = 0; dt < 4; dt++) acc[dt] = mfma32_f16(va[ks][dt], pop, acc[dt]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        read_k(si_next);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- segment result (lane (li, lh) holds d = 4i + dt, i = 8(r/4) + 4lh + r%4, in acc[dt][r])
@@ -678,9 +740,10 @@ void wide_partition_kernel(Params p) {
     };
 
     // ---- pipeline: copies of tiles lo .. lo+NSLOT-2 in flight before the first compute; each
-    // step waits for its tile, barriers, refills the slot freed by the previous tile (past the
-    // range end the issue cursor repeats its last tile, so every wave always has the same number
-    // of copies in flight) and computes.
+    // step waits for the tile after its own, barriers, refills the slot freed by the previous
+    // tile (past the range end the issue cursor repeats its last tile, so every wave always has
+    // the same number of copies in flight), converts its share of the next tile's V and computes
+    // its tile from the ring's K and the staged V.
     Cursor ic, cc;
     locate(ic, lo);
     cc = ic;
@@ -692,22 +755,33 @@ void wide_partition_kernel(Params p) {
     }
     int seg = 0, seg_start = cc.tt;
     int slot_c = 0, slot_i = NSLOT - 1;  // ring slots of the computed tile and of the next copies
+    int buf = 0;                         // staging buffer holding the computed tile's V
     bool stores_pending = false;
-    load_q(cc.b, cc.grp);
+    load_q(cc.b, cc.grp);  // (drains this wave's copies: the first tiles have landed)
     reset_state();
+    // the first tile's V and K, once every wave's copies of it have landed
+    wg_barrier();
+    convert_v(slot_c, buf);
+    read_k(slot_c);
     for (;;) {
-        // own copies of tile cc.pos done (the NSLOT-2 younger tiles may still be in flight); after
-        // stores, wait for everything (loads and stores need not retire in order)
+        // own copies of the next tile done (the NSLOT-3 younger tiles may still be in flight);
+        // after stores, wait for everything (loads and stores need not retire in order).  The
+        // barrier then publishes the next tile and this tile's converted V, and frees the ring
+        // slot and staging buffer of the previous tile.
         if (stores_pending) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSLOT - 2) * LY::OPS));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSLOT - 3) * LY::OPS));
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);  // this wave's staging writes
         stores_pending = false;
         wg_barrier();
         step(ic);
         issue(ic, slot_i);
         slot_i = next_slot(slot_i);
+        // (computing converts the next tile's V; past the range end that slot holds a repeat of the
+        // last tile: converted, never read)
         const int t0 = cc.tt * kTile;
-        compute(slot_c, min(cc.n - t0, kTile) - 1);
+        compute(slot_c, buf, min(cc.n - t0, kTile) - 1, next_slot(slot_c));
         slot_c = next_slot(slot_c);
+        buf ^= 1;
         const bool end_unit = cc.tt + 1 == cc.Tb;
         if (end_unit || cc.pos + 1 == hi) {
             finalize(cc, seg, seg_start == 0 && end_unit);
@@ -728,9 +802,9 @@ void wide_partition_kernel(Params p) {
 // ---------------------------------------------------------------- host-side dispatch
 template <int KVT, int WPG, int QT, int SCALE>
 static hipError_t launch_w(const Params &p, hipStream_t stream) {
-    // tiles in flight per workgroup: NSLOT-1; the ring is sized so that three workgroups fit
-    // in one CU's 160 KB of LDS
-    constexpr int NSLOT = WPG == 2 ? 3 : (SCALE == SC_TOKEN_HEAD ? 5 : 6);
+    // tiles in flight per workgroup: up to NSLOT-1; ring + V staging (16 KB) fit two 4-wave
+    // workgroups, or three 2-wave ones, in one CU's 160 KB of LDS
+    constexpr int NSLOT = WPG == 2 ? 4 : (SCALE == SC_TOKEN_HEAD ? 5 : 6);
     dim3 grid(p.nparts), block(64 * WPG);
     if (p.block_table && p.block_size == 16)  // 32-token tiles span two blocks
         hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
