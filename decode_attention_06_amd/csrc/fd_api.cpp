@@ -24,7 +24,8 @@ namespace {
 // third, for a step measured ~3 % faster on the 128K MQA workload.
 constexpr long kDefaultWaves = 2048;
 constexpr long kDefaultWavesWide = 2048;    // 4-wave workgroups: two per CU
-constexpr long kDefaultWavesWide2 = 1536;   // 2-wave workgroups: three per CU (their LDS)
+constexpr long kDefaultWavesWide2 = 1536;   // 2-wave workgroups: three per CU (their LDS),
+constexpr long kDefaultWavesWide2I8 = 1024; // two with INT8 KV (its K staging)
 constexpr int kMaxSeqLen = 1 << 24;
 constexpr int kMaxQueryWindow = 64;  // query tokens per sequence in one call
 
@@ -87,7 +88,9 @@ Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, i
     const long tt_max = (long)batch * pl.groups * cdiv(max_seq_len, fd::kTile);
     long W = num_partitions > 0
                  ? num_partitions
-                 : (pl.wide ? (pl.wpg == 2 ? kDefaultWavesWide2 : kDefaultWavesWide) : kDefaultWaves) / pl.wpg;
+                 : (pl.wide ? (pl.wpg == 2 ? (kv_dtype == FD_INT8 ? kDefaultWavesWide2I8 : kDefaultWavesWide2)
+                                           : kDefaultWavesWide)
+                            : kDefaultWaves) / pl.wpg;
     if (W > tt_max) W = tt_max;
     if (W < 1) W = 1;
     pl.nparts = (int)W;

@@ -56,6 +56,9 @@ constexpr int waitcnt_lgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 // f16 staging of a tile's V in p.V operand order: 2 k-steps x 4 d-tiles, 1 KB each
 constexpr int kVStageBlock = 1024;
 constexpr int kVStageBytes = 8 * kVStageBlock;
+// INT8 KV: f16 staging of a tile's K in q.k^T operand order: 8 k-steps of 16 d, 1 KB each
+constexpr int kKStageBlock = 1024;
+constexpr int kKStageBytes = 8 * kKStageBlock;
 
 template <int WPG, int SCALE>
 struct WideLayout {
@@ -142,6 +145,17 @@ __device__ __forceinline__ void lds_read_rows4(uint32_t (&w)[4], uint32_t a) {
         : "memory");
 }
 
+// One 16-byte LDS read, complete on return.
+__device__ __forceinline__ void lds_read_1x16(u32x4_t (&r)[1], uint32_t a) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a) : "memory");
+}
+
+// One 16-byte LDS write (not waited for here, as the 8-byte one below).
+__device__ __forceinline__ void lds_write_16(uint32_t a, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+    const u32x4_t v = {x0, x1, x2, x3};
+    asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+
 // One 8-byte LDS write (not waited for here: LDS operations of a wave complete in order, and the
 // next LDS read's wait, or the wait before the workgroup barrier, covers it).
 __device__ __forceinline__ void lds_write_8(uint32_t a, uint32_t lo, uint32_t hi) {
@@ -180,6 +194,8 @@ void wide_partition_kernel(Params p) {
     // V of a tile as f16 in p.V's MFMA operand order, two buffers (the tile being computed and the
     // next one, converted by all waves of the workgroup together, a quarter each)
     __shared__ __attribute__((aligned(16))) uint8_t vstage[2 * kVStageBytes];
+    // INT8 KV: K the same way, as exact f16 for q.k^T on f16 MFMAs
+    __shared__ __attribute__((aligned(16))) uint8_t kstage[KVT == KV_I8 ? 2 * kKStageBytes : 16];
     __shared__ int sh_prefix[kWideLdsBatch + 1];
 
     // (the wave index is uniform: kept in a scalar register, so per-wave choices are scalar)
@@ -337,14 +353,14 @@ void wide_partition_kernel(Params p) {
 
     // ---- per-lane LDS offsets within a slot
     const uint32_t ring0 = lds_addr(ring);
-    // K operand of the q.k^T MFMA: token li; E4M3 (32x32x64) k-step ks = q / 2: d = 64 ks + 32 lh
-    // + 0..31, the row's 16-byte chunks 4 ks + 2 lh and 4 ks + 2 lh + 1; INT8 (32x32x32) k-step
-    // ks = q: d = 32 ks + 16 lh + 0..15, chunk 2 ks + lh.  Chunk c of row r is stored at c ^ (r & 7).
+    // K operand of the E4M3 q.k^T MFMA: token li; k-step ks = q / 2 (32x32x64): d = 64 ks + 32 lh
+    // + 0..31, the row's 16-byte chunks 4 ks + 2 lh and 4 ks + 2 lh + 1.  Chunk c of row r is
+    // stored at c ^ (r & 7).  (INT8 KV reads K from its f16 staging instead.)
     constexpr bool I8 = KVT == KV_I8;
     uint32_t koff[4];
 #pragma unroll
     for (int q = 0; q < 4; q++)
-        koff[q] = li * LY::ROWB + 16 * ((I8 ? 2 * q + lh : 4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
+        koff[q] = li * LY::ROWB + 16 * ((4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
     const uint32_t vst0 = lds_addr(vstage);
     const uint32_t soff = 2 * LY::KV_BYTES + wave * LY::SC_BYTES + 16 * lh;
 
@@ -353,12 +369,12 @@ void wide_partition_kernel(Params p) {
     // a negative per-tensor k scale, q carries the sign):
     //   E4M3 KV: NQT E4M3 terms whose sum is q * 2^eq exactly (bf16 q: 2 terms, f16 q: 3), d =
     //            64 ks + 32 lh + j in byte j of qf8[t][ks] (32 bytes per term and k-step);
-    //   INT8 KV: three int8 terms, base-128 digits with 2^14 t1 + 2^7 t2 + t3 = q * 2^eq to within
-    //            0.5 (the largest |q * 2^eq| lies in [2^19, 2^20), so q is held to 2^-20 of its
-    //            largest value), d = 32 ks + 16 lh + j in byte j of qi8[t][ks].
-    constexpr int NQT = I8 ? 3 : (QT == KV_BF16 ? 2 : 3);
+    //   INT8 KV: f16 of q * 2^eq (the largest |q * 2^eq| lies in [2^14, 2^15): every value within
+    //            2^28 of it is an f16 normal number and converts exactly, bf16's 8-bit or f16's
+    //            11-bit significand fitting f16's), d = 16 ks + 8 lh + j in half j of qh[ks].
+    constexpr int NQT = QT == KV_BF16 ? 2 : 3;
     i32x8_t qf8[I8 ? 1 : NQT][2];
-    u32x4_t qi8[I8 ? 3 : 1][I8 ? 4 : 1];
+    u32x4_t qh[I8 ? 8 : 1];
     float qk_head = qk_scale;
     f32x16_t acc[4];
     float m_run = -INFINITY, l_run = 0.0f;
@@ -368,13 +384,13 @@ void wide_partition_kernel(Params p) {
         const int u_in = grp * WPG + wave;
         const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
         const int head = kvh * p.group + hb * kWideHeadBlock + li;
-        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + (I8 ? 16 : 32) * lh;
-        // E4M3: raw[4 ks + c] holds d = 64 ks + 32 lh + 8 c + 0..7; INT8: raw[2 ks + c] holds
-        // d = 32 ks + 16 lh + 8 c + 0..7
+        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + (I8 ? 8 : 32) * lh;
+        // E4M3: raw[4 ks + c] holds d = 64 ks + 32 lh + 8 c + 0..7; INT8: raw[ks] holds
+        // d = 16 ks + 8 lh + 0..7
         u32x4_t raw[8];
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            raw[i] = *(const u32x4_t *)(qrow + (I8 ? 32 * (i >> 1) + 8 * (i & 1) : 64 * (i >> 2) + 8 * (i & 3)));
+            raw[i] = *(const u32x4_t *)(qrow + (I8 ? 16 * i : 64 * (i >> 2) + 8 * (i & 3)));
         // complete here (a drain, once per segment), so that no load is pending at the top of the
         // tile loop and the compiler adds no wait on the in-flight tile copies there
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -389,9 +405,9 @@ void wide_partition_kernel(Params p) {
                 mx = max(mx, max(w & 0xFFFFu, w >> 16));
             }
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
-        // 2^eq puts the largest |q| in [2^7, 2^8), inside E4M3's range (largest finite 448); for the
-        // INT8 terms in [2^19, 2^20)
-        const int target = I8 ? 19 : 7;
+        // 2^eq puts the largest |q| in [2^7, 2^8), inside E4M3's range (largest finite 448); for
+        // INT8 KV (f16 q) in [2^14, 2^15)
+        const int target = I8 ? 14 : 7;
         int eq = 0;
         if (mx != 0) eq = QT == KV_BF16 ? target + 127 - (int)(mx >> 7) : target + 15 - (int)(mx >> 10);
         // per-tensor scale: the multiplier is kept >= 0 (the tile max is then taken on raw scores)
@@ -414,22 +430,9 @@ void wide_partition_kernel(Params p) {
                     x[h] = __builtin_amdgcn_ldexpf(flip ? -v : v, eq);
                 }
                 if constexpr (I8) {
-                    // signed base-128 digits, each the nearest integer to what is left (|t| <= 64; the
-                    // remainders are exact in fp32); bytes j = 8 c + 4 e2 + h of k-step i / 2
-                    uint32_t w1 = 0, w2 = 0, w3 = 0;
-#pragma unroll
-                    for (int h = 0; h < 4; h++) {
-                        const float t1 = __builtin_rintf(x[h] * (1.0f / 16384.0f));
-                        const float r1 = x[h] - 16384.0f * t1;
-                        const float t2 = __builtin_rintf(r1 * (1.0f / 128.0f));
-                        const float t3 = __builtin_rintf(r1 - 128.0f * t2);
-                        w1 |= ((uint32_t)(int)t1 & 0xFFu) << (8 * h);
-                        w2 |= ((uint32_t)(int)t2 & 0xFFu) << (8 * h);
-                        w3 |= ((uint32_t)(int)t3 & 0xFFu) << (8 * h);
-                    }
-                    qi8[0][i >> 1][2 * (i & 1) + e2] = w1;
-                    qi8[1][i >> 1][2 * (i & 1) + e2] = w2;
-                    qi8[2][i >> 1][2 * (i & 1) + e2] = w3;
+                    // exact f16 pairs (d = 8 lh + 4 e2 + 0..3 of k-step i)
+                    qh[i][2 * e2] = pack_f16(x[0], x[1]);
+                    qh[i][2 * e2 + 1] = pack_f16(x[2], x[3]);
                 } else {
 #pragma unroll
                     for (int t = 0; t < NQT; t++) {
@@ -472,7 +475,7 @@ void wide_partition_kernel(Params p) {
         const uint32_t vsrc = ring0 + si * LY::SLOT + LY::KV_BYTES;
         const uint32_t vdst = vst0 + buf * kVStageBytes;
         const int th = lane >> 5, lv = lane & 31;
-#pragma unroll
+#pragma unroll 1  // (2-wave workgroups: one pass after the other, not both held in registers)
         for (int jj = 0; jj < 4 / WPG; jj++) {
             const int j = wave * (4 / WPG) + jj;  // wave-uniform
             const int ks = j >> 1, hh = j & 1;
@@ -509,6 +512,33 @@ void wide_partition_kernel(Params p) {
         const uint32_t b = ring0 + si * LY::SLOT;
         lds_read_4x16(kr, b + koff[0], b + koff[1], b + koff[2], b + koff[3]);
     };
+    // ---- INT8 KV: K of the tile in ring slot si -> exact f16 staging buffer buf, this wave's share.
+    // Operand layout: block ks of 1 KB holds, for each lane l = (i, hh) of the reading wave, the 8
+    // f16 of token i at d = 16 ks + 8 hh + 0..7 (16 bytes at 16 l).  The ring's row t holds 16-byte
+    // chunk c (d = 16 c .. 16 c + 15) at c ^ (t & 7); lane L converts token L % 32's chunk
+    // c = 2 j + L / 32 in each of its passes j and writes both halves (hh = 0, 1) of block c.
+    auto convert_k = [&](int si, int buf) {
+        const uint32_t ksrc = ring0 + si * LY::SLOT;
+        const uint32_t kdst = lds_addr(kstage) + buf * kKStageBytes;
+        const int t = lane & 31, half = lane >> 5;
+#pragma unroll 1
+        for (int jj = 0; jj < 4 / WPG; jj++) {
+            const int c = 2 * (wave * (4 / WPG) + jj) + half;
+            u32x4_t w[1];
+            lds_read_1x16(w, ksrc + t * LY::ROWB + 16 * (c ^ (t & 7)));
+            uint32_t o[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                // bytes 0, 1 and 2, 3 of the dword -> bytes 0 and 2 of a dword (zeros between)
+                o[2 * e] = i8x2_to_f16x2(__builtin_amdgcn_perm(w[0][e], w[0][e], 0x0C010C00u));
+                o[2 * e + 1] = i8x2_to_f16x2(__builtin_amdgcn_perm(w[0][e], w[0][e], 0x0C030C02u));
+            }
+            const uint32_t at = kdst + c * kKStageBlock + 16 * t;
+            lds_write_16(at, o[0], o[1], o[2], o[3]);
+            lds_write_16(at + 16 * 32, o[4], o[5], o[6], o[7]);
+        }
+    };
+
     // the tile in ring slot si (its K already in kr), its V staged in buffer buf; the next tile's V
     // (ring slot si_next) is converted into the other buffer while the q.k^T MFMAs run, and the
     // next tile's K is read while the p.V MFMAs run (that tile has landed and was published by
@@ -526,11 +556,20 @@ void wide_partition_kernel(Params p) {
                 for (int dt = 0; dt < 4; dt++) va[ks][dt] = vp[(ks * 4 + dt) * (kVStageBlock / 16)];
         }
         __builtin_amdgcn_sched_barrier(0);
-        // the next tile's V conversion, placed after the q.k^T MFMAs are issued: its LDS wait and
+        // INT8 KV: the tile's K operands, exact f16 (plain loads, as V's)
+        u32x4_t kf[I8 ? 8 : 1];
+        if constexpr (I8) {
+            const u32x4_t *kp = (const u32x4_t *)(kstage + buf * kKStageBytes) + lane;
+#pragma unroll
+            for (int ks = 0; ks < 8; ks++) kf[ks] = kp[ks * (kKStageBlock / 16)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the next tile's conversions, placed after the q.k^T MFMAs are issued: their LDS waits and
         // VALU work run while the matrix unit is busy
         auto convert_next = [&]() {
             __builtin_amdgcn_sched_barrier(0);
             convert_v(si_next, buf ^ 1);
+            if constexpr (I8) convert_k(si_next, buf ^ 1);
             __builtin_amdgcn_sched_barrier(0);
         };
         // per-token scales: element to a scalar before the bit cast (a bit cast straight from a
@@ -548,34 +587,12 @@ void wide_partition_kernel(Params p) {
         // ---- scores S[token][head] = K . (q * 2^eq) straight from the ring's bytes (no conversion)
         f32x16_t S;
         if constexpr (I8) {
-            // INT8: 2^14 (K . t1) + (128 (K . t2) + K . t3) on 32x32x32 int8 MFMAs, four 32-deep
-            // k-steps per term; each dot product is exact in int32 (|K . t| <= 128 * 127 * 64 <
-            // 2^20), so is 128 (K . t2) + K . t3 (< 2^28), and the two parts meet in one fp32 fma
-            i32x16_t Si, Sl;
+            // INT8: exact f16 K (staged) times exact f16 q on 32x32x16 f16 MFMAs, eight 16-deep k-steps
 #pragma unroll
-            for (int r = 0; r < 16; r++) Si[r] = 0;
+            for (int r = 0; r < 16; r++) S[r] = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; r++) Sl[r] = 0;
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++)
-                Si = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, kr[ks]),
-                                                           __builtin_bit_cast(i32x4_t, qi8[0][ks]), Si, 0, 0, 0);
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++)
-                Sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, kr[ks]),
-                                                           __builtin_bit_cast(i32x4_t, qi8[1][ks]), Sl, 0, 0, 0);
+            for (int ks = 0; ks < 8; ks++) S = mfma32_f16(kf[ks], qh[ks], S);
             convert_next();
-#pragma unroll
-            for (int r = 0; r < 16; r++) Sl[r] <<= 7;
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++)
-                Sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, kr[ks]),
-                                                           __builtin_bit_cast(i32x4_t, qi8[2][ks]), Sl, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int hi = Si[r], lo = Sl[r];  // (elements to scalars before converting)
-                S[r] = __builtin_fmaf((float)hi, 16384.0f, (float)lo);
-            }
         } else {
             // E4M3: FP8 MFMAs, two 64-deep k-steps, NQT terms of q each
 #pragma unroll
@@ -690,9 +707,11 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
             for (int dt = 0; dt < 4; dt++) acc[dt] = mfma32_f16(va[ks][dt], pop, acc[dt]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        read_k(si_next);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!I8) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_k(si_next);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // ---- segment result (lane (li, lh) holds d = 4i + dt, i = 8(r/4) + 4lh + r%4, in acc[dt][r])
@@ -762,7 +781,8 @@ void wide_partition_kernel(Params p) {
     // the first tile's V and K, once every wave's copies of it have landed
     wg_barrier();
     convert_v(slot_c, buf);
-    read_k(slot_c);
+    if constexpr (I8) convert_k(slot_c, buf);
+    else read_k(slot_c);
     for (;;) {
         // own copies of the next tile done (the NSLOT-3 younger tiles may still be in flight);
         // after stores, wait for everything (loads and stores need not retire in order).  The
@@ -803,8 +823,9 @@ void wide_partition_kernel(Params p) {
 template <int KVT, int WPG, int QT, int SCALE>
 static hipError_t launch_w(const Params &p, hipStream_t stream) {
     // tiles in flight per workgroup: up to NSLOT-1; ring + V staging (16 KB) fit two 4-wave
-    // workgroups, or three 2-wave ones, in one CU's 160 KB of LDS
-    constexpr int NSLOT = WPG == 2 ? 4 : (SCALE == SC_TOKEN_HEAD ? 5 : 6);
+    // workgroups, or three 2-wave ones, in one CU's 160 KB of LDS; with INT8's K staging (16 KB
+    // more) two workgroups of either size
+    constexpr int NSLOT = WPG == 2 ? 4 : ((SCALE == SC_TOKEN_HEAD || KVT == KV_I8) ? 5 : 6);
     dim3 grid(p.nparts), block(64 * WPG);
     if (p.block_table && p.block_size == 16)  // 32-token tiles span two blocks
         hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
