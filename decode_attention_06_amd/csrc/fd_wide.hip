@@ -187,8 +187,10 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
 void wide_partition_kernel(Params p) {
     using LY = WideLayout<WPG, SCALE>;
     constexpr int D = 128;
-    static_assert(NSLOT >= 4, "the ring holds the tile being read, the next one (being converted), one "
-                              "being refilled and at least one more in flight");
+    // tiles whose data is consumed ahead of the computed one: V one tile ahead; INT8 K two
+    constexpr int AHEAD = KVT == KV_I8 ? 2 : 1;
+    static_assert(NSLOT >= 3 + AHEAD, "the ring holds the tile being read, the ones being converted, one "
+                                      "being refilled and at least one more in flight");
     static_assert((NSLOT - 2) * LY::OPS < 64, "vmcnt field is 6 bits");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * LY::SLOT];
     // V of a tile as f16 in p.V's MFMA operand order, two buffers (the tile being computed and the
@@ -506,8 +508,15 @@ void wide_partition_kernel(Params p) {
         }
     };
 
-    // K operand of q.k^T for the tile about to be computed (read one tile ahead)
+    // K operand of q.k^T for the tile about to be computed (read one tile ahead): E4M3 raw bytes
+    // from the ring; INT8 exact f16 from its staging buffer
     u32x4_t kr[4];
+    u32x4_t kf[KVT == KV_I8 ? 8 : 1];
+    auto read_kf = [&](int kbuf) {
+        const u32x4_t *kp = (const u32x4_t *)(kstage + kbuf * kKStageBytes) + lane;
+#pragma unroll
+        for (int ks = 0; ks < 8; ks++) kf[ks] = kp[ks * (kKStageBlock / 16)];
+    };
     auto read_k = [&](int si) {
         const uint32_t b = ring0 + si * LY::SLOT;
         lds_read_4x16(kr, b + koff[0], b + koff[1], b + koff[2], b + koff[3]);
@@ -556,20 +565,14 @@ void wide_partition_kernel(Params p) {
                 for (int dt = 0; dt < 4; dt++) va[ks][dt] = vp[(ks * 4 + dt) * (kVStageBlock / 16)];
         }
         __builtin_amdgcn_sched_barrier(0);
-        // INT8 KV: the tile's K operands, exact f16 (plain loads, as V's)
-        u32x4_t kf[I8 ? 8 : 1];
-        if constexpr (I8) {
-            const u32x4_t *kp = (const u32x4_t *)(kstage + buf * kKStageBytes) + lane;
-#pragma unroll
-            for (int ks = 0; ks < 8; ks++) kf[ks] = kp[ks * (kKStageBlock / 16)];
-        }
         __builtin_amdgcn_sched_barrier(0);
         // the next tile's conversions, placed after the q.k^T MFMAs are issued: their LDS waits and
         // VALU work run while the matrix unit is busy
         auto convert_next = [&]() {
             __builtin_amdgcn_sched_barrier(0);
             convert_v(si_next, buf ^ 1);
-            if constexpr (I8) convert_k(si_next, buf ^ 1);
+            // INT8: K two tiles ahead, into the K buffer this tile's K was read from
+            if constexpr (I8) convert_k(next_slot(si_next), buf);
             __builtin_amdgcn_sched_barrier(0);
         };
         // per-token scales: element to a scalar before the bit cast (a bit cast straight from a
@@ -707,11 +710,10 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
             for (int dt = 0; dt < 4; dt++) acc[dt] = mfma32_f16(va[ks][dt], pop, acc[dt]);
         }
-        if constexpr (!I8) {
-            __builtin_amdgcn_sched_barrier(0);
-            read_k(si_next);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (I8) read_kf(buf ^ 1);  // converted last step, published by this step's barrier
+        else read_k(si_next);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- segment result (lane (li, lh) holds d = 4i + dt, i = 8(r/4) + 4lh + r%4, in acc[dt][r])
@@ -781,15 +783,22 @@ void wide_partition_kernel(Params p) {
     // the first tile's V and K, once every wave's copies of it have landed
     wg_barrier();
     convert_v(slot_c, buf);
-    if constexpr (I8) convert_k(slot_c, buf);
-    else read_k(slot_c);
+    if constexpr (I8) {
+        convert_k(slot_c, 0);
+        convert_k(next_slot(slot_c), 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
+        wg_barrier();
+        read_kf(0);
+    } else {
+        read_k(slot_c);
+    }
     for (;;) {
-        // own copies of the next tile done (the NSLOT-3 younger tiles may still be in flight);
+        // own copies of the tile AHEAD of this one done (younger ones may still be in flight);
         // after stores, wait for everything (loads and stores need not retire in order).  The
-        // barrier then publishes the next tile and this tile's converted V, and frees the ring
-        // slot and staging buffer of the previous tile.
+        // barrier then publishes that tile, this tile's converted V (and INT8: the next tile's
+        // converted K), and frees the ring slot and staging buffers read in the previous step.
         if (stores_pending) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSLOT - 3) * LY::OPS));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSLOT - 2 - AHEAD) * LY::OPS));
         __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);  // this wave's staging writes
         stores_pending = false;
         wg_barrier();
@@ -825,7 +834,7 @@ static hipError_t launch_w(const Params &p, hipStream_t stream) {
     // tiles in flight per workgroup: up to NSLOT-1; ring + V staging (16 KB) fit two 4-wave
     // workgroups, or three 2-wave ones, in one CU's 160 KB of LDS; with INT8's K staging (16 KB
     // more) two workgroups of either size
-    constexpr int NSLOT = WPG == 2 ? 4 : ((SCALE == SC_TOKEN_HEAD || KVT == KV_I8) ? 5 : 6);
+    constexpr int NSLOT = KVT == KV_I8 ? 5 : (WPG == 2 ? 4 : (SCALE == SC_TOKEN_HEAD ? 5 : 6));
     dim3 grid(p.nparts), block(64 * WPG);
     if (p.block_table && p.block_size == 16)  // 32-token tiles span two blocks
         hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
