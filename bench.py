@@ -50,7 +50,7 @@ METRIC = "achieved KV-read HBM GB/s (% of peak) and µs per decode step"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 KERNEL_SRCS = [os.path.join(ROOT, "decode_attention_06_amd", "csrc", f)
-               for f in ("fd_kernels.hip", "fd_wide.hip", "fd_device.h", "fd_internal.h")]
+               for f in ("fd_kernels.hip", "fd_wide.hip", "fd_direct.hip", "fd_device.h", "fd_internal.h")]
 
 
 def strip_comments(src: str) -> str:
@@ -88,18 +88,25 @@ def kernel_hash() -> str:
 
 
 def partition_kernel_name(case) -> str:
-    """Which partition kernel the library's plan runs for this case (E4M3 or INT8 KV, head_dim 128
-    and a multiple of 64 query heads per kv head take the wide-group kernel, with one query token)."""
-    wide = case.kv_dtype in ("fp8_e4m3", "int8") and case.d == 128 and case.group % 64 == 0 and case.nq == 1
-    return "wide_partition_kernel" if wide else "partition_kernel"
+    """Which partition kernel the library's plan runs for this case: E4M3 or INT8 KV, head_dim 128
+    and a multiple of 64 query heads per kv head with one query token take the wide-group kernel;
+    otherwise E4M3 KV, head_dim 128 and a multiple of 32 MFMA columns per kv head (query heads x
+    query tokens) the 32-column kernel; everything else the 16-head kernel."""
+    if case.kv_dtype in ("fp8_e4m3", "int8") and case.d == 128 and case.group % 64 == 0 and case.nq == 1:
+        return "wide_partition_kernel"
+    if case.kv_dtype == "fp8_e4m3" and case.d == 128 and (case.group * case.nq) % 32 == 0:
+        return "direct_partition_kernel"
+    return "partition_kernel"
 
 
 def compute_note(case) -> str:
     """The arithmetic the partition kernel runs for this case's dtypes."""
-    wide = partition_kernel_name(case) == "wide_partition_kernel"
-    qk = {"fp8_e4m3": ("E4M3 K on FP8 MFMAs with q as exact E4M3 terms, f16 MFMA p.v" if wide
+    kern = partition_kernel_name(case)
+    wide_fp8 = kern in ("wide_partition_kernel", "direct_partition_kernel")
+    qk = {"fp8_e4m3": ("E4M3 K on FP8 MFMAs with q as exact E4M3 terms, f16 MFMA p.v" if wide_fp8
                        else f"E4M3 K -> {case.q_dtype} MFMA q.k, f16 MFMA p.v"),
-          "int8": ("INT8 K on int8 MFMAs with q as three int8 terms, V -> f16 (exact) MFMA p.v" if wide
+          "int8": ("INT8 K and V staged as exact f16 (once per workgroup), f16 MFMA q.k (q scaled "
+                   "exactly into f16) and p.v" if kern == "wide_partition_kernel"
                    else "INT8 K/V -> f16 (exact) MFMA q.k (q scaled into f16) and p.v"),
           "f16": "f16 MFMA q.k and p.v",
           "bf16": "bf16 MFMA q.k, bf16 MFMA p.v (p split into two bf16 terms)"}[case.kv_dtype]

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfd.so")
-SOURCES = ["fd_kernels.hip", "fd_wide.hip", "fd_append.hip", "fd_check.hip", "fd_api.cpp"]
+SOURCES = ["fd_kernels.hip", "fd_wide.hip", "fd_direct.hip", "fd_append.hip", "fd_check.hip", "fd_api.cpp"]
 ARCH = "gfx950"
 
 # -Xclang -target-feature -Xclang -packed-fp32-ops: keep the compiler from emitting packed

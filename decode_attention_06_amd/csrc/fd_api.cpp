@@ -36,6 +36,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
     bool wide;   // wide-group kernel (32-head blocks, LDS-shared tiles)
+    bool direct; // 32-column units with K/V straight into registers, one per wave
     int hb;      // heads per head block
     int nhb;     // head blocks per kv head
     int wpg;     // waves per partition workgroup (units processed side by side)
@@ -51,6 +52,13 @@ struct Plan {
 bool use_wide(int group, int hkv, int head_dim, int kv_dtype, int nq) {
     return nq == 1 && (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) && head_dim == 128 && group % 64 == 0 &&
            hkv < (1 << 16);
+}
+
+// Otherwise, E4M3 KV with head_dim 128 and a multiple of 32 MFMA columns per kv head (a window of
+// 4 query tokens x 8 heads, or 32 heads) takes the 32-column kernel: each wave loads and converts
+// its kv head's tiles once, where 16-column blocks would load them once per block.
+bool use_direct(int cols, int hkv, int head_dim, int kv_dtype) {
+    return kv_dtype == FD_FP8_E4M3 && head_dim == 128 && cols % 32 == 0 && hkv < (1 << 16);
 }
 
 bool sizes_ok(int batch, int hq, int hkv, int head_dim, int max_seq_len) {
@@ -71,13 +79,14 @@ Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, i
     Plan pl;
     const int group = hq / hkv, cols = group * nq;
     pl.wide = use_wide(group, hkv, head_dim, kv_dtype, nq);
+    pl.direct = !pl.wide && use_direct(cols, hkv, head_dim, kv_dtype);
     if (pl.wide) {
         pl.hb = fd::kWideHeadBlock;
         pl.nhb = group / pl.hb;
         pl.wpg = pl.nhb % 4 == 0 ? 4 : 2;
         pl.groups = hkv * pl.nhb / pl.wpg;
     } else {
-        pl.hb = fd::kHeadBlock;
+        pl.hb = pl.direct ? fd::kWideHeadBlock : fd::kHeadBlock;
         pl.nhb = (int)cdiv(cols, pl.hb);
         const long ups = (long)hkv * pl.nhb;
         pl.wpg = 1;
@@ -332,8 +341,9 @@ int step(const void *q, int num_query, const void *k_cache, const void *v_cache,
     }
 
     if (t_prof_begin) (void)hipEventRecord(t_prof_begin, stream);
-    const hipError_t perr = pl.wide ? fd::launch_wide_partition(p, kv_dtype, q_dtype, scale_mode, stream)
-                                    : fd::launch_partition(p, kv_dtype, q_dtype, scale_mode, stream);
+    const hipError_t perr = pl.wide     ? fd::launch_wide_partition(p, kv_dtype, q_dtype, scale_mode, stream)
+                            : pl.direct ? fd::launch_direct_partition(p, q_dtype, scale_mode, stream)
+                                        : fd::launch_partition(p, kv_dtype, q_dtype, scale_mode, stream);
     if (perr != hipSuccess) return FD_ERR_LAUNCH;
     if (t_prof_end) (void)hipEventRecord(t_prof_end, stream);
     if (fd::launch_combine(p, stream) != hipSuccess) return FD_ERR_LAUNCH;

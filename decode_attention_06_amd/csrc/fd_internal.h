@@ -68,6 +68,9 @@ hipError_t launch_combine(const Params &p, hipStream_t stream);
 // Wide-group variant (defined in fd_wide.hip): E4M3 or INT8 KV, head_dim 128, hb = kWideHeadBlock,
 // wpg 2 or 4 head blocks of one kv head per workgroup.
 hipError_t launch_wide_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode, hipStream_t stream);
+// 32-column units with K/V straight into registers (defined in fd_direct.hip): E4M3 KV, head_dim
+// 128, hb = kWideHeadBlock, one unit per wave, up to kMaxWavesPerGroup units per workgroup.
+hipError_t launch_direct_partition(const Params &p, int q_dtype, int scale_mode, hipStream_t stream);
 hipError_t launch_fp8_decode(const uint8_t *in, float *out, int n, hipStream_t stream);
 hipError_t launch_read_probe(const void *in, size_t n16, uint32_t *out, int blocks, int kind, hipStream_t stream);
 // fd_append.hip: new_dtype 0 f32 / 1 f16 / 2 bf16; kv_dtype and scale_mode as the FD_ codes.

@@ -62,8 +62,10 @@ def test_plan_and_workspace_sizes():
     assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "bf16") == 256
     # group of 64 on 2 kv heads: wide kernel with 2 waves per workgroup, capped by 2*2*128 tiles
     assert fd.plan_partitions(2, 128, 2, 128, 4096, 64, "fp8_e4m3") == 512
-    # group of 32: 16-head kernel (the wide one needs a multiple of 64)
-    assert fd.plan_partitions(64, 32, 1, 128, 4096, 64, "fp8_e4m3") == 1024
+    # group of 32 with E4M3: the 32-column kernel, one unit (one wave) per kv head, 2048 waves
+    assert fd.plan_partitions(64, 32, 1, 128, 4096, 64, "fp8_e4m3") == 2048
+    # ... with bf16 KV: the 16-head kernel, two head blocks (waves) per workgroup
+    assert fd.plan_partitions(64, 32, 1, 128, 4096, 64, "bf16") == 1024
     assert fd.plan_partitions(64, 6, 3, 128, 4096, 64, "fp8_e4m3") == 2048 // 3   # 3 waves per group
     assert fd.plan_partitions(2, 6, 3, 128, 4096, 64, "fp8_e4m3") == 2 * 128      # capped by tiles
     # tiny step: capped by its tile count (2 sequences x 1 unit x 4 tiles)

@@ -65,3 +65,13 @@ def test_wide_kernel_spills():
         assert m, k
         scale = int(m.group(5))
         assert v <= (0 if scale == 1 else 8), (k, v)
+
+
+def test_direct_kernel_spills():
+    # the 32-column kernel holds two register tiles (66 VGPRs) and the accumulator (64) across the
+    # loop (q's E4M3 terms live in LDS): a reload from scratch inside the loop would also wait for
+    # the next tile's loads (scratch shares their counter), so none is allowed
+    sp = kernel_spills(os.path.join(BUILD, "fd_direct.hip.o"))
+    assert sp
+    assert all(v == 0 for v in sp.values()), {k: v for k, v in sp.items() if v}
+

@@ -69,8 +69,10 @@ def check_scaled(name, case, num_partitions=0, unit=1.0):
 
 
 KERNELS = {
-    # a group of 8 (16-head kernel) and of 128 (the wide kernel for E4M3; INT8 takes 16-head blocks)
+    # a group of 8 (16-head kernel), of 32 (the 32-column kernel for E4M3; INT8 takes two 16-head
+    # blocks) and of 128 (the wide kernel)
     "g8": dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[700, 33, 2100], block_size=64),
+    "g32": dict(batch=2, hq=64, hkv=2, d=128, seq_lens=[1300, 60], block_size=64),
     "g128": dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1500, 97], block_size=64),
 }
 

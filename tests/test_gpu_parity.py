@@ -126,6 +126,15 @@ SMALL = [
     ("bs16_wide_g128_tok", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1000, 31], kv="fp8_e4m3",
                                 q="bf16", scale="token_head", block_size=16)),
     # wide-group kernel with INT8 KV (int8 MFMAs for q.k^T on the raw codes, q in three int8 terms)
+    # 32-column units, K/V straight into registers (E4M3 KV, head_dim 128, 32 MFMA columns per kv head)
+    ("direct_g32_tok", dict(batch=3, hq=64, hkv=2, d=128, seq_lens=[1000, 33, 4097], kv="fp8_e4m3",
+                            q="bf16", scale="token_head", block_size=64)),
+    ("direct_g32_tensor_bs16", dict(batch=2, hq=32, hkv=1, d=128, seq_lens=[700, 31], kv="fp8_e4m3",
+                                    q="bf16", scale="tensor", block_size=16)),
+    ("direct_g32_tok_contig_f16q", dict(batch=2, hq=64, hkv=2, d=128, seq_lens=[300, 1], kv="fp8_e4m3",
+                                        q="f16", scale="token_head", paged=False, block_size=0)),
+    ("direct_g96_tok_bs32", dict(batch=2, hq=96, hkv=1, d=128, seq_lens=[1500, 64], kv="fp8_e4m3",
+                                 q="bf16", scale="token_head", block_size=32)),
     ("wide_i8_g64_tok", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[1000, 33, 4097], kv="int8",
                              q="bf16", scale="token_head", block_size=64)),
     ("wide_i8_g128_tok_contig_f16q", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[300, 1], kv="int8",
@@ -280,10 +289,11 @@ def test_partition_kernel_batch_beyond_lds_prefix_table():
 
 @pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
 @pytest.mark.parametrize("k_mult,v_mult", [(-1.0, 1.0), (-1.0, -1.0), (0.0, 1.0)])
-@pytest.mark.parametrize("hq", [16, 128])
+@pytest.mark.parametrize("hq", [16, 32, 128])
 def test_per_tensor_scale_signs(k_mult, v_mult, hq, kv):
     # negative or zero per-tensor scales (hq 128: the wide kernel, which scales scores inside the
-    # exponent and flips q's sign for a negative scale; hq 16: the 16-head kernel).  A zero k
+    # exponent and flips q's sign for a negative scale; hq 32 with E4M3: the 32-column kernel, which
+    # flips it the same way; hq 16: the 16-head kernel).  A zero k
     # scale makes every score 0: out is the plain mean of the dequantised V rows
     case = workloads.custom_case(seed=31, device="cuda", batch=2, hq=hq, hkv=1, d=128,
                                  seq_lens=[3000, 77], kv=kv, q="bf16", scale="tensor",

@@ -71,6 +71,13 @@ WINDOW = [
                                    q="bf16", scale="tensor", block_size=64)),
     ("g8_nq5_i8_bs16", dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[3, 100, 48], nq=5, kv="int8", q="f16",
                             scale="token_head", block_size=16)),
+    # 32 columns per kv head with E4M3 (the 32-column kernel): 16 heads x 2 rows, 4 x 8, 8 x 8 (two units)
+    ("g16_nq2_fp8_tok_bs16", dict(batch=3, hq=32, hkv=2, d=128, seq_lens=[600, 17, 2], nq=2, kv="fp8_e4m3",
+                                  q="bf16", scale="token_head", block_size=16)),
+    ("g4_nq8_fp8_tensor_contig", dict(batch=2, hq=8, hkv=2, d=128, seq_lens=[300, 5], nq=8, kv="fp8_e4m3",
+                                      q="bf16", scale="tensor", paged=False, block_size=0)),
+    ("g8_nq8_fp8_f16q_bs32", dict(batch=2, hq=16, hkv=2, d=128, seq_lens=[1000, 70], nq=8, kv="fp8_e4m3",
+                                  q="f16", scale="token_head", block_size=32)),
     ("g6_nq3_fp8_f16q_bs32", dict(batch=2, hq=12, hkv=2, d=128, seq_lens=[95, 64], nq=3, kv="fp8_e4m3",
                                   q="f16", scale="tensor", block_size=32)),
 ]
@@ -105,19 +112,26 @@ def test_window_of_one_equals_the_single_token_step_bitwise():
     assert torch.equal(a, b[:, 0])
 
 
-def test_window_rows_match_single_token_steps_on_prefixes():
-    # row m of the window = the plain step over the first seq_len - nq + m + 1 tokens (GPU vs GPU)
+@pytest.mark.parametrize("nq", [3, 4])
+def test_window_rows_match_single_token_steps_on_prefixes(nq):
+    # row m of the window = the plain step over the first seq_len - nq + m + 1 tokens (GPU vs GPU;
+    # nq 4 with 8 heads: the window runs on the 32-column kernel, the single rows on the 16-head one)
     case = workloads.custom_case(seed=42, device="cuda", batch=2, hq=16, hkv=2, d=128, seq_lens=[1000, 77],
-                                 nq=3, kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64)
+                                 nq=nq, kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64)
     win = fd.decode_case(case)
-    for m in range(3):
+    for m in range(nq):
         c = workloads.Case(**{k: getattr(case, k) for k in case.__dataclass_fields__})
         c.q, c.nq = case.q[:, m].contiguous(), 1
-        c.seq_len = case.seq_len - (3 - 1 - m)
+        c.seq_len = case.seq_len - (nq - 1 - m)
         one = fd.decode_case(c)
         torch.cuda.synchronize()
         err = (win[:, m] - one).abs().max().item()
-        assert err < 2e-4, (m, err)
+        # same kernel family (nq 3): only the running-max schedule differs, 2e-4.  nq 4: the two
+        # sides run different kernels, each rounding its softmax weights to f16 (relative 2^-11)
+        # against its own reference max, with q.k^T in different exact forms; each side is held to
+        # the oracle's bar in its own tests, and two independent roundings of that size stay
+        # below 1e-3 here
+        assert err < (2e-4 if nq == 3 else 1e-3), (m, err)
 
 
 def test_workload_verify_fp8_32k_full():

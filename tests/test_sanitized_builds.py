@@ -69,7 +69,8 @@ def test_oracle_pins_under_asan_ubsan(tmp_path):
 def test_abi_host_side_under_asan_ubsan(tmp_path):
     rt = _clang_asan_runtime()
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    objs = [os.path.join(BUILD, f + ".o") for f in ("fd_kernels.hip", "fd_wide.hip", "fd_append.hip", "fd_check.hip")]
+    objs = [os.path.join(BUILD, f + ".o") for f in ("fd_kernels.hip", "fd_wide.hip", "fd_direct.hip", "fd_append.hip",
+                                                  "fd_check.hip")]
     if not rt or not os.path.exists(hipcc) or not all(os.path.exists(o) for o in objs):
         pytest.skip("clang ASan runtime, hipcc or the built device objects not available")
     api_o = str(tmp_path / "fd_api.o")
