@@ -196,6 +196,7 @@ void partition_kernel(Params p) {
     constexpr bool PART16 = (KVT == KV_FP8 || KVT == KV_I8);
     __shared__ __attribute__((aligned(16))) float sh_scale_all[kMaxWavesPerGroup][64];
     __shared__ int sh_prefix[kLdsBatch + 1];  // tiles of the sequences before b (b <= batch)
+    __shared__ int sh_len[kLdsBatch];         // the sequences' lengths, clamped to max_seq_len
 
     const int wave = uni((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;  // wave index kept scalar
     float *sh_scale = sh_scale_all[wave];
@@ -210,15 +211,29 @@ void partition_kernel(Params p) {
             int base = 0;
             for (int b0 = 0; b0 < p.batch; b0 += 64) {
                 const int bb = b0 + lane;
-                const int t = bb < p.batch ? seq_tiles(p, bb) : 0;
+                const int nb = bb < p.batch ? max(0, min(p.seq_len[bb], p.max_seq_len)) : 0;
+                const int t = (nb + kTile - 1) / kTile;
                 const int incl = wave_incl_scan(t, lane);
-                if (bb < p.batch) sh_prefix[bb] = base + incl - t;
+                if (bb < p.batch) {
+                    sh_prefix[bb] = base + incl - t;
+                    sh_len[bb] = nb;
+                }
                 base += __shfl(incl, 63, 64);
             }
             if (lane == 0) sh_prefix[p.batch] = base;
         }
         __syncthreads();
     }
+    // length of (wave-uniform) sequence b, clamped: from LDS when the table is there
+    auto seq_n = [&](int bq) -> int {
+        return lds_prefix ? uni(sh_len[bq]) : max(0, min(ld_uniform(p.seq_len, bq), p.max_seq_len));
+    };
+    // block sizes are 16, 32 or 64: block index and offset by shift and mask
+    const int bsh = PAGED ? (B16 ? 4 : uni(__builtin_ctz((unsigned)p.block_size))) : 0;
+    // block-table entry of the next tile's block, read one tile ahead (its scalar load is then
+    // complete when that tile is described, instead of stalling the issue of its loads)
+    int pf_b = -1, pf_bi = -1;
+    int32_t pf_val = 0;
 
     // ---- this workgroup's tile range [lo, hi) of the concatenation of all unit groups
     const int64_t TT = uni(lds_prefix ? (int64_t)sh_prefix[p.batch] * groups : total_seq_tiles(p, lane) * groups);
@@ -255,7 +270,7 @@ void partition_kernel(Params p) {
             const int64_t rel = at - Pb * groups;
             grp = uni((int)(rel / Tb));
             tt = uni((int)(rel % Tb));
-            n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
+            n = seq_n(b);
             return;
         }
         int64_t base = 0;
@@ -279,7 +294,7 @@ void partition_kernel(Params p) {
             }
             base += uni(__shfl(incl, 63, 64));
         }
-        n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
+        n = seq_n(b);
     };
     struct Desc {
         int64_t row0, row1;       // first cache rows of the tile's two 16-token halves
@@ -294,15 +309,21 @@ void partition_kernel(Params p) {
         d.t0 = tt * kTile;
         d.nrel = n - d.t0;
         d.last = min(d.nrel, kTile) - 1;
-        if constexpr (PAGED) {
-            d.row0 = (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + d.t0 / p.block_size) *
-                         p.block_size + (d.t0 % p.block_size);
+        if constexpr (PAGED && !B16) {
+            const int bi = d.t0 >> bsh;
+            const int32_t e = (pf_b == b && pf_bi == bi) ? pf_val
+                                                        : ld_uniform(p.block_table, (size_t)b * p.max_blocks + bi);
+            d.row0 = ((int64_t)e << bsh) + (d.t0 & ((1 << bsh) - 1));
+            d.row1 = d.row0 + 16;
+            // the next tile's block (an entry of the same table row even past the sequence's end)
+            pf_b = b;
+            pf_bi = min((d.t0 + kTile) >> bsh, p.max_blocks - 1);
+            pf_val = ld_uniform(p.block_table, (size_t)b * p.max_blocks + pf_bi);
+        } else if constexpr (PAGED) {
+            d.row0 = (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 >> 4)) * 16;
             // blocks of 16 tokens: the second half sits in the next block (if the tile reaches it)
-            if constexpr (B16)
-                d.row1 = d.last < 16 ? d.row0 + 16
-                                     : (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 + 16) / 16) * 16;
-            else
-                d.row1 = d.row0 + 16;
+            d.row1 = d.last < 16 ? d.row0 + 16
+                                 : (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 >> 4) + 1) * 16;
         } else {
             d.row0 = (int64_t)ld_uniform(p.kv_start, b) + d.t0;
             d.row1 = d.row0 + 16;
@@ -324,7 +345,7 @@ void partition_kernel(Params p) {
                 do {
                     b++;
                 } while ((Tb = lds_prefix ? uni(sh_prefix[b + 1] - sh_prefix[b]) : seq_tiles_u(p, b)) == 0);
-                n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
+                n = seq_n(b);
             }
         }
         describe(d);
