@@ -32,13 +32,20 @@ namespace {
 // sequences whose tile prefix sums the workgroup keeps in LDS (larger batches: a wave scan)
 constexpr int kDirectLdsBatch = 256;
 
-// Plain (cached) loads: a K row's 128-byte line is read by four load instructions of the wave (32
-// bytes of each of 32 rows per instruction), which find it cached; nontemporal loads, which do not
-// keep it, streamed this pattern at 5.2 TB/s against 6.1 in an isolated probe, and made the 4-token
-// verify kernel 172 us against 143 us.
+// K: plain (cached) loads.  A K row's 128-byte line is read by four load instructions of the wave
+// (32 bytes of each of 32 rows per instruction), which find it cached; nontemporal loads, which do
+// not keep it, streamed this pattern at 5.2 TB/s against 6.1 in an isolated probe, and made the
+// 4-token verify kernel 172 us against 143 us.
 template <typename T>
 __device__ __forceinline__ T ld_dir(const uint8_t *src) {
     return *(const T *)src;
+}
+
+// V: nontemporal loads.  Each V load instruction reads two whole 128-byte rows, so nothing of a
+// line is read again; streaming them past the caches made the 4-token verify kernel 135 us
+// against 143 us with plain loads.
+__device__ __forceinline__ uint32_t ld_dir_v(const uint8_t *src) {
+    return __builtin_nontemporal_load((const uint32_t *)src);
 }
 
 // Four 16-byte LDS reads at a + 0, 32, 64, 96 bytes, complete on return.
@@ -143,6 +150,9 @@ void direct_partition_kernel(Params p) {
                    uint32_t, fmaxf(fabsf(SCALE == SC_TENSOR ? tensor_v : 1.0f) * kMinNormal, kMinNormal))));
     const uint32_t row_bytes = (uint32_t)p.hkv * D;
     const int bsh = PAGED ? (B16 ? 4 : uni(__builtin_ctz((unsigned)p.block_size))) : 0;
+    // lane byte offsets in a full tile: K token li, bytes 32 lh ..; V token 4 lh, bytes 4 li ..
+    const uint32_t k_lane = __umul24((uint32_t)li, row_bytes) + 32 * lh;
+    const uint32_t v_lane = __umul24((uint32_t)lh4, row_bytes) + 4 * li;
 
     // ---- tile cursor (the same tiles for every wave; each wave its own unit of the unit group)
     int64_t pos = lo;
@@ -184,6 +194,8 @@ void direct_partition_kernel(Params p) {
         }
         n = max(0, min(ld_uniform(p.seq_len, b), p.max_seq_len));
     };
+    int pf_b = -1, pf_bi = -1;  // block-table entry (sequence, block) read ahead, and its value
+    int32_t pf_val = 0;
     struct Desc {
         int64_t row0, row1;  // first cache rows of the tile's two 16-token halves
         int b, kvh, ub, t0, last, nrel, seg;
@@ -197,14 +209,22 @@ void direct_partition_kernel(Params p) {
         d.t0 = tt * kTile;
         d.nrel = n - d.t0;
         d.last = min(d.nrel, kTile) - 1;
-        if constexpr (PAGED) {
-            d.row0 = ((int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 >> bsh)) << bsh) +
-                     (d.t0 & ((1 << bsh) - 1));
-            if constexpr (B16)
-                d.row1 = d.last < 16 ? d.row0 + 16
-                                     : (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 >> 4) + 1) << 4;
-            else
-                d.row1 = d.row0 + 16;
+        if constexpr (PAGED && !B16) {
+            // the block-table entry was read one tile ahead when it is the one the previous tile
+            // asked for, so the tile's loads do not wait for a scalar load
+            const int bi = d.t0 >> bsh;
+            const int32_t e = (pf_b == b && pf_bi == bi) ? pf_val
+                                                        : ld_uniform(p.block_table, (size_t)b * p.max_blocks + bi);
+            d.row0 = ((int64_t)e << bsh) + (d.t0 & ((1 << bsh) - 1));
+            d.row1 = d.row0 + 16;
+            // the next tile's block (an entry of the same table row even past the sequence's end)
+            pf_b = b;
+            pf_bi = min((d.t0 + kTile) >> bsh, p.max_blocks - 1);
+            pf_val = ld_uniform(p.block_table, (size_t)b * p.max_blocks + pf_bi);
+        } else if constexpr (PAGED) {
+            d.row0 = (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 >> 4)) << 4;
+            d.row1 = d.last < 16 ? d.row0 + 16
+                                 : (int64_t)ld_uniform(p.block_table, (size_t)b * p.max_blocks + (d.t0 >> 4) + 1) << 4;
         } else {
             d.row0 = (int64_t)ld_uniform(p.kv_start, b) + d.t0;
             d.row1 = d.row0 + 16;
@@ -258,8 +278,10 @@ void direct_partition_kernel(Params p) {
     f32x16_t acc[4];
     float m_run = -INFINITY, l_run = 0.0f;
     int ev = 0;  // per-token v scales: the accumulator holds values / 2^ev
+    int win_off = 0;  // a window column's tokens end this many before the sequence's end
     auto load_q = [&](const Desc &d) {
         const Col cl = col_of(d.ub);
+        win_off = p.nq - 1 - cl.m;
         const uint16_t *qrow =
             (const uint16_t *)p.q + (((size_t)d.b * p.nq + cl.m) * p.hq + d.kvh * p.group + cl.h) * D + 32 * lh;
         u32x4_t raw[8];
@@ -336,20 +358,36 @@ void direct_partition_kernel(Params p) {
         const uint8_t *kb = (const uint8_t *)p.k + (size_t)d.kvh * D + d.row0 * row_bytes;
         const uint8_t *vb = (const uint8_t *)p.v + (size_t)d.kvh * D + d.row0 * row_bytes;
         const int64_t jump = B16 ? (d.row1 - d.row0 - 16) * (int64_t)row_bytes : 0;
-        {
-            const int t = min(li, d.last);
-            const uint32_t ko = __umul24((uint32_t)t, row_bytes) + 32 * lh;
-            const uint8_t *kt = kb + ((B16 && t >= 16) ? jump : 0);
+        if (d.last == kTile - 1) {
+            // a full tile (wave-uniform): the lane offsets are the kernel's fixed ones and each V
+            // load's row goes into its scalar base, so no per-load address arithmetic
+            const uint8_t *kt = kb + ((B16 && li >= 16) ? jump : 0);
 #pragma unroll
-            for (int i = 0; i < 4; i++) r.k[i] = ld_dir<u32x4_t>(kt + ko + 64 * (i >> 1) + 16 * (i & 1));
-        }
+            for (int i = 0; i < 4; i++) r.k[i] = ld_dir<u32x4_t>(kt + k_lane + 64 * (i >> 1) + 16 * (i & 1));
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            const uint8_t *vt = vb + (ks ? jump : 0);  // tokens 16 ks ..: block 1 for ks = 1
+            for (int ks = 0; ks < 2; ks++) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int t = min(16 * ks + lh4 + (j < 4 ? j : j + 4), d.last);
-                r.v[ks][j] = ld_dir<uint32_t>(vt + __umul24((uint32_t)t, row_bytes) + 4 * li);
+                for (int j = 0; j < 8; j++) {
+                    const uint8_t *vrow = vb + (ks ? jump : 0) + (size_t)(16 * ks + (j < 4 ? j : j + 4)) * row_bytes;
+                    r.v[ks][j] = ld_dir_v(vrow + v_lane);
+                }
+            }
+        } else {
+            {
+                const int t = min(li, d.last);
+                const uint32_t ko = __umul24((uint32_t)t, row_bytes) + 32 * lh;
+                const uint8_t *kt = kb + ((B16 && t >= 16) ? jump : 0);
+#pragma unroll
+                for (int i = 0; i < 4; i++) r.k[i] = ld_dir<u32x4_t>(kt + ko + 64 * (i >> 1) + 16 * (i & 1));
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const uint8_t *vt = vb + (ks ? jump : 0);  // tokens 16 ks ..: block 1 for ks = 1
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const int t = min(16 * ks + lh4 + (j < 4 ? j : j + 4), d.last);
+                    r.v[ks][j] = ld_dir_v(vt + __umul24((uint32_t)t, row_bytes) + 4 * li);
+                }
             }
         }
         if constexpr (SCALE == SC_TOKEN_HEAD) {
@@ -400,7 +438,7 @@ void direct_partition_kernel(Params p) {
         // last token column li may see in this tile: a window row m stops nq - 1 - m tokens before
         // the sequence's end (a plain step: the tile's last valid token, whose copies fill the rest)
         int lastc = d.last;
-        if (p.nq > 1) lastc = min(d.nrel - (p.nq - 1 - col_of(d.ub).m), kTile) - 1;
+        if (p.nq > 1) lastc = min(d.nrel - win_off, kTile) - 1;
         const bool masked = __any(lastc < kTile - 1);  // wave-uniform
         if (masked) {
 #pragma unroll
@@ -418,9 +456,9 @@ void direct_partition_kernel(Params p) {
             lds_read_4x16_d(raw, sh_sc + 128 + 16 * lh);
             float vm = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 16; q++) {
-                const uint32_t w = raw[q >> 2][q & 3];
-                vm = fmaxf(vm, fabsf(__builtin_bit_cast(float, w)));
+            for (int q = 0; q < 16; q += 2) {
+                const uint32_t w0 = raw[q >> 2][q & 3], w1 = raw[q >> 2][(q & 3) + 1];
+                vm = fmaxf(vm, fmaxf(fabsf(__builtin_bit_cast(float, w0)), fabsf(__builtin_bit_cast(float, w1))));
             }
             vm = max_halves_d(vm);
             evt = uni(vm > 0.0f ? exp2_ceil(vm) : ev);
