@@ -89,10 +89,13 @@ def kernel_hash() -> str:
 
 def partition_kernel_name(case) -> str:
     """Which partition kernel the library's plan runs for this case: E4M3 or INT8 KV, head_dim 128
-    and a multiple of 64 query heads per kv head with one query token take the wide-group kernel;
-    otherwise E4M3 KV, head_dim 128 and a multiple of 32 MFMA columns per kv head (query heads x
-    query tokens) the 32-column kernel; everything else the 16-head kernel."""
-    if case.kv_dtype in ("fp8_e4m3", "int8") and case.d == 128 and case.group % 64 == 0 and case.nq == 1:
+    and a multiple of 64 query heads per kv head with one query token take the wide-group kernel
+    (f16 / bf16 KV: a multiple of 128 heads); otherwise E4M3 KV, head_dim 128 and a multiple of 32
+    MFMA columns per kv head (query heads x query tokens) the 32-column kernel; everything else
+    the 16-head kernel."""
+    if case.d == 128 and case.nq == 1 and (
+            (case.kv_dtype in ("fp8_e4m3", "int8") and case.group % 64 == 0)
+            or (case.kv_dtype in ("f16", "bf16") and case.group % 128 == 0)):
         return "wide_partition_kernel"
     if case.kv_dtype == "fp8_e4m3" and case.d == 128 and (case.group * case.nq) % 32 == 0:
         return "direct_partition_kernel"
@@ -108,8 +111,11 @@ def compute_note(case) -> str:
           "int8": ("INT8 K and V staged as exact f16 (once per workgroup), f16 MFMA q.k (q scaled "
                    "exactly into f16) and p.v" if kern == "wide_partition_kernel"
                    else "INT8 K/V -> f16 (exact) MFMA q.k (q scaled into f16) and p.v"),
-          "f16": "f16 MFMA q.k and p.v",
-          "bf16": "bf16 MFMA q.k, bf16 MFMA p.v (p split into two bf16 terms)"}[case.kv_dtype]
+          "f16": ("f16 MFMA q.k and p.v, K/V tiles shared through LDS" if kern == "wide_partition_kernel"
+                  else "f16 MFMA q.k and p.v"),
+          "bf16": ("bf16 MFMA q.k, bf16 MFMA p.v (p split into two bf16 terms), K/V tiles shared through LDS"
+                   if kern == "wide_partition_kernel"
+                   else "bf16 MFMA q.k, bf16 MFMA p.v (p split into two bf16 terms)")}[case.kv_dtype]
     return qk + ", f32 softmax and accumulate"
 
 

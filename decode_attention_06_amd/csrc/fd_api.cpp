@@ -46,12 +46,14 @@ struct Plan {
 
 // Groups of 64+ query heads per kv head with E4M3 or INT8 KV and head_dim 128 take the
 // wide-group kernel: 32 heads per wave, and 2 or 4 waves of one kv head share every K/V tile
-// through LDS.  (A window of several query tokens per sequence takes the 16-column kernel.)
+// through LDS; with f16 or bf16 KV, groups of 128+ (four waves: a 16-bit tile ring fits only two
+// workgroups per CU).  (A window of several query tokens per sequence takes the 16-column kernel.)
 // (the wide kernel forms in-tile row offsets with 24-bit multiplies: a cache row of all kv
-// heads, hkv * 128 bytes, stays below 2^24)
+// heads, hkv * 256 bytes at most, stays below 2^24)
 bool use_wide(int group, int hkv, int head_dim, int kv_dtype, int nq) {
-    return nq == 1 && (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) && head_dim == 128 && group % 64 == 0 &&
-           hkv < (1 << 16);
+    if (nq != 1 || head_dim != 128 || hkv >= (1 << 16)) return false;
+    if (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) return group % 64 == 0;
+    return (kv_dtype == FD_F16 || kv_dtype == FD_BF16) && group % 128 == 0;
 }
 
 // Otherwise, E4M3 KV with head_dim 128 and a multiple of 32 MFMA columns per kv head (a window of

@@ -1,5 +1,5 @@
 // fd_wide.hip -- gfx950 partition kernel for wide query groups: 64 or more query heads per kv
-// head (MQA / wide GQA), E4M3 KV, head_dim 128.
+// head (MQA / wide GQA), E4M3 or INT8 KV (128 or more heads: also f16 / bf16 KV), head_dim 128.
 //
 // Method: the split-KV online-softmax recurrence of the 16-head partition kernel in
 // fd_kernels.hip (same pages: "SGLang Prefill 性能优化" section 2.2 for the block recurrence;
@@ -32,6 +32,11 @@
 //     (i, hh) for d-tile dt holds d = 4i + dt of those 8 tokens: one 4-byte LDS read per token
 //     row, then a byte permute and the hardware E4M3 -> f16 convert per token pair.
 //   * Softmax in log2 units with v_exp_f32, as in the 16-head kernel.
+//   * f16 / bf16 KV (q of the same type): rows of 256 bytes; q.k^T on the MFMA of that type with K
+//     read from the ring as is (lane (i, hh), k-step kk: d = 64 hh + 8 kk + 0..7, one 16-byte
+//     chunk; chunk c of row r stored at c ^ (r & 15)); V re-laid into the staging buffer without
+//     conversion; bf16 p.V takes P as two bf16 terms (hi + lo), so the weights keep f32-like
+//     precision against exact V.  Partial rows stay fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,13 +65,17 @@ constexpr int kVStageBytes = 8 * kVStageBlock;
 constexpr int kKStageBlock = 1024;
 constexpr int kKStageBytes = 8 * kKStageBlock;
 
-template <int WPG, int SCALE>
+template <int KVT, int WPG, int SCALE>
 struct WideLayout {
-    static constexpr int ROWB = 128;                 // bytes of one token's K (or V) row, one kv head
+    static constexpr bool KV16 = KVT == KV_F16 || KVT == KV_BF16;
+    static constexpr int ROWB = KV16 ? 256 : 128;    // bytes of one token's K (or V) row, one kv head
     static constexpr int KV_BYTES = kTile * ROWB;    // one tile of K (or V)
+    static constexpr int RPC = 1024 / ROWB;          // rows per 1 KB copy
+    static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int NCK = KV_BYTES / 1024;      // 1 KB copies per tile of K (or V)
     static constexpr int SC_BYTES = 256;             // per wave: 32 k then 32 v scales of a tile
     static constexpr int SLOT = 2 * KV_BYTES + (SCALE == SC_TOKEN_HEAD ? WPG * SC_BYTES : 0);
-    static constexpr int OPS_KV = 8 / WPG;           // 1 KB copies per wave per tile
+    static constexpr int OPS_KV = 2 * NCK / WPG;     // 1 KB copies per wave per tile
     static constexpr int OPS = OPS_KV + (SCALE == SC_TOKEN_HEAD ? 1 : 0);
 };
 
@@ -145,6 +154,19 @@ __device__ __forceinline__ void lds_read_rows4(uint32_t (&w)[4], uint32_t a) {
         : "memory");
 }
 
+// Four 8-byte LDS reads from four consecutive 256-byte rows past a, complete on return.
+__device__ __forceinline__ void lds_read_rows4_b64(u32x2_t (&w)[4], uint32_t a) {
+    asm volatile(
+        "ds_read_b64 %0, %4 offset:0\n\t"
+        "ds_read_b64 %1, %4 offset:256\n\t"
+        "ds_read_b64 %2, %4 offset:512\n\t"
+        "ds_read_b64 %3, %4 offset:768\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+        : "v"(a)
+        : "memory");
+}
+
 // One 16-byte LDS read, complete on return.
 __device__ __forceinline__ void lds_read_1x16(u32x4_t (&r)[1], uint32_t a) {
     asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a) : "memory");
@@ -185,19 +207,25 @@ __device__ __forceinline__ void wg_barrier() {
 template <int KVT, int WPG, int NSLOT, int QT, int SCALE, bool PAGED, bool B16>
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
 void wide_partition_kernel(Params p) {
-    using LY = WideLayout<WPG, SCALE>;
+    using LY = WideLayout<KVT, WPG, SCALE>;
     constexpr int D = 128;
+    constexpr bool KV16 = LY::KV16;
+    constexpr int EB = KV16 ? 2 : 1;  // bytes per KV element
+    static_assert(!KV16 || (QT == KVT && SCALE == SC_NONE && WPG == 4), "16-bit KV: q of the same type, no scales");
     // tiles whose data is consumed ahead of the computed one: V one tile ahead; INT8 K two
     constexpr int AHEAD = KVT == KV_I8 ? 2 : 1;
     static_assert(NSLOT >= 3 + AHEAD, "the ring holds the tile being read, the ones being converted, one "
                                       "being refilled and at least one more in flight");
     static_assert((NSLOT - 2) * LY::OPS < 64, "vmcnt field is 6 bits");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * LY::SLOT];
-    // V of a tile as f16 in p.V's MFMA operand order, two buffers (the tile being computed and the
-    // next one, converted by all waves of the workgroup together, a quarter each)
+    // V of a tile as f16 (bf16 KV: bf16) in p.V's MFMA operand order, two buffers (the tile being
+    // computed and the next one, converted by all waves of the workgroup together, a quarter each)
     __shared__ __attribute__((aligned(16))) uint8_t vstage[2 * kVStageBytes];
     // INT8 KV: K the same way, as exact f16 for q.k^T on f16 MFMAs
     __shared__ __attribute__((aligned(16))) uint8_t kstage[KVT == KV_I8 ? 2 * kKStageBytes : 16];
+    // (16-bit KV: ring and staging alone fill 80 KB, two workgroups per CU; the arrays below are
+    // then never referenced and take no LDS, and tiles are located by a wave scan)
+    constexpr int LDS_BATCH = KV16 ? 0 : kWideLdsBatch;
     __shared__ int sh_prefix[kWideLdsBatch + 1];
 
     // (the wave index is uniform: kept in a scalar register, so per-wave choices are scalar)
@@ -205,7 +233,7 @@ void wide_partition_kernel(Params p) {
     const int li = lane & 31, lh = lane >> 5;
     const int64_t wg = blockIdx.x, W = gridDim.x;
     const int groups = p.groups;
-    const bool lds_prefix = p.batch <= kWideLdsBatch;
+    const bool lds_prefix = LDS_BATCH > 0 && p.batch <= LDS_BATCH;
 
     // ---- per-sequence tile prefix sums, once per workgroup
     if (lds_prefix) {
@@ -240,7 +268,7 @@ void wide_partition_kernel(Params p) {
     const float sc_floor = __builtin_bit_cast(
         float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                    uint32_t, fmaxf(fabsf(SCALE == SC_TENSOR ? tensor_v : 1.0f) * kMinNormal, kMinNormal))));
-    const uint32_t row_bytes = (uint32_t)p.hkv * D;  // bytes per cache row (all kv heads)
+    const uint32_t row_bytes = (uint32_t)p.hkv * D * EB;  // bytes per cache row (all kv heads)
 
     // ---- tile cursors: one issuing copies NSLOT-1 tiles ahead, one computing
     // kvh: kv head of the unit group grp (kept with the cursor: it changes only with the group)
@@ -330,20 +358,24 @@ void wide_partition_kernel(Params p) {
         uint8_t *slot = ring + si * LY::SLOT;
         // uniform base of the tile's first row; each lane adds a 32-bit offset (a tile of 32 rows
         // inside one block, or two 16-row blocks, each contiguous)
-        const uint8_t *kb = (const uint8_t *)p.k + (size_t)k.kvh * D + row0 * row_bytes;
-        const uint8_t *vb = (const uint8_t *)p.v + (size_t)k.kvh * D + row0 * row_bytes;
+        const uint8_t *kb = (const uint8_t *)p.k + (size_t)k.kvh * D * EB + row0 * row_bytes;
+        const uint8_t *vb = (const uint8_t *)p.v + (size_t)k.kvh * D * EB + row0 * row_bytes;
         const int64_t jump = B16 ? (row1 - row0 - 16) * row_bytes : 0;  // second block's shift
 #pragma unroll
         for (int u = 0; u < LY::OPS_KV; u++) {
-            const int o = wave * LY::OPS_KV + u;  // copies 0..3: K rows 8o..8o+7; 4..7: V rows
-            const int row = 8 * (o & 3) + (lane >> 3);
+            // copies 0..NCK-1: K rows RPC oo .. RPC oo + RPC-1; NCK..2 NCK-1: V rows (oo = o % NCK);
+            // lane L writes chunk position L % CPR of row RPC oo + L / CPR (a K chunk c sits at
+            // position c ^ (row % CPR))
+            const int o = wave * LY::OPS_KV + u;
+            const int oo = o % LY::NCK;
+            const int row = LY::RPC * oo + lane / LY::CPR, pos = lane % LY::CPR;
             const int r = min(row, last);
             const uint32_t off = __umul24((uint32_t)r, row_bytes);
             const int64_t shift = (B16 && r >= 16) ? jump : 0;
-            if (o < 4)
-                copy16_to_lds(kb + shift + off + 16 * ((lane & 7) ^ (row & 7)), slot + o * 1024);
+            if (o < LY::NCK)
+                copy16_to_lds(kb + shift + off + 16 * (pos ^ (row & (LY::CPR - 1))), slot + oo * 1024);
             else
-                copy16_to_lds(vb + shift + off + 16 * (lane & 7), slot + LY::KV_BYTES + (o - 4) * 1024);
+                copy16_to_lds(vb + shift + off + 16 * pos, slot + LY::KV_BYTES + oo * 1024);
         }
         if constexpr (SCALE == SC_TOKEN_HEAD) {
             const int t = min(lane & 31, last);
@@ -358,11 +390,15 @@ void wide_partition_kernel(Params p) {
     // K operand of the E4M3 q.k^T MFMA: token li; k-step ks = q / 2 (32x32x64): d = 64 ks + 32 lh
     // + 0..31, the row's 16-byte chunks 4 ks + 2 lh and 4 ks + 2 lh + 1.  Chunk c of row r is
     // stored at c ^ (r & 7).  (INT8 KV reads K from its f16 staging instead.)
+    // 16-bit KV: k-step kk (32x32x16) takes d = 64 lh + 8 kk + 0..7, chunk 8 lh + kk of token li,
+    // stored at (8 lh + kk) ^ (li & 15).
     constexpr bool I8 = KVT == KV_I8;
-    uint32_t koff[4];
+    constexpr int NKR = KV16 ? 8 : 4;  // K operand reads per tile
+    uint32_t koff[NKR];
 #pragma unroll
-    for (int q = 0; q < 4; q++)
-        koff[q] = li * LY::ROWB + 16 * ((4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
+    for (int q = 0; q < NKR; q++)
+        koff[q] = KV16 ? li * LY::ROWB + 16 * ((8 * lh + q) ^ (li & 15))
+                       : li * LY::ROWB + 16 * ((4 * (q >> 1) + 2 * lh + (q & 1)) ^ (li & 7));
     const uint32_t vst0 = lds_addr(vstage);
     const uint32_t soff = 2 * LY::KV_BYTES + wave * LY::SC_BYTES + 16 * lh;
 
@@ -374,9 +410,10 @@ void wide_partition_kernel(Params p) {
     //   INT8 KV: f16 of q * 2^eq (the largest |q * 2^eq| lies in [2^14, 2^15): every value within
     //            2^28 of it is an f16 normal number and converts exactly, bf16's 8-bit or f16's
     //            11-bit significand fitting f16's), d = 16 ks + 8 lh + j in half j of qh[ks].
+    //   16-bit KV: q as is, d = 64 lh + 8 kk + j in half j of qh[kk].
     constexpr int NQT = QT == KV_BF16 ? 2 : 3;
-    i32x8_t qf8[I8 ? 1 : NQT][2];
-    u32x4_t qh[I8 ? 8 : 1];
+    i32x8_t qf8[(I8 || KV16) ? 1 : NQT][2];
+    u32x4_t qh[(I8 || KV16) ? 8 : 1];
     float qk_head = qk_scale;
     f32x16_t acc[4];
     float m_run = -INFINITY, l_run = 0.0f;
@@ -386,75 +423,84 @@ void wide_partition_kernel(Params p) {
         const int u_in = grp * WPG + wave;
         const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
         const int head = kvh * p.group + hb * kWideHeadBlock + li;
-        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + (I8 ? 8 : 32) * lh;
-        // E4M3: raw[4 ks + c] holds d = 64 ks + 32 lh + 8 c + 0..7; INT8: raw[ks] holds
-        // d = 16 ks + 8 lh + 0..7
-        u32x4_t raw[8];
+        if constexpr (KV16) {
+            const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + 64 * lh;
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            raw[i] = *(const u32x4_t *)(qrow + (I8 ? 16 * i : 64 * (i >> 2) + 8 * (i & 3)));
-        // complete here (a drain, once per segment), so that no load is pending at the top of the
-        // tile loop and the compiler adds no wait on the in-flight tile copies there
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        // largest |q| of head li over its 128 values (this lane's 64 and lane li + 32 * (1 - lh)'s):
-        // bf16 / f16 bit patterns with the sign cleared order like the magnitudes
-        uint32_t mx = 0;
+            for (int kk = 0; kk < 8; kk++) qh[kk] = *(const u32x4_t *)(qrow + 8 * kk);
+            // complete here (once per segment; see below)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            qk_head = qk_scale;
+        } else {
+            const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + (I8 ? 8 : 32) * lh;
+            // E4M3: raw[4 ks + c] holds d = 64 ks + 32 lh + 8 c + 0..7; INT8: raw[ks] holds
+            // d = 16 ks + 8 lh + 0..7
+            u32x4_t raw[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++)
+            for (int i = 0; i < 8; i++)
+                raw[i] = *(const u32x4_t *)(qrow + (I8 ? 16 * i : 64 * (i >> 2) + 8 * (i & 3)));
+            // complete here (a drain, once per segment), so that no load is pending at the top of the
+            // tile loop and the compiler adds no wait on the in-flight tile copies there
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            // largest |q| of head li over its 128 values (this lane's 64 and lane li + 32 * (1 - lh)'s):
+            // bf16 / f16 bit patterns with the sign cleared order like the magnitudes
+            uint32_t mx = 0;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const uint32_t w = raw[i][e] & 0x7FFF7FFFu;
-                mx = max(mx, max(w & 0xFFFFu, w >> 16));
-            }
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
-        // 2^eq puts the largest |q| in [2^7, 2^8), inside E4M3's range (largest finite 448); for
-        // INT8 KV (f16 q) in [2^14, 2^15)
-        const int target = I8 ? 14 : 7;
-        int eq = 0;
-        if (mx != 0) eq = QT == KV_BF16 ? target + 127 - (int)(mx >> 7) : target + 15 - (int)(mx >> 10);
-        // per-tensor scale: the multiplier is kept >= 0 (the tile max is then taken on raw scores)
-        const bool flip = SCALE == SC_TENSOR && qk_scale < 0.0f;
-        qk_head = __builtin_amdgcn_ldexpf(flip ? -qk_scale : qk_scale, -eq);
-        auto to_f32 = [](uint32_t h) -> float {
-            if constexpr (QT == KV_BF16) return __builtin_bit_cast(float, h << 16);
-            else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-        };
+            for (int i = 0; i < 8; i++)
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-#pragma unroll
-            for (int e2 = 0; e2 < 2; e2++) {
-                // values 4 e2 .. 4 e2 + 3 of raw[i]: d = 8 c + 4 e2 + 0..3 -> dword 2 c + e2 of a term
-                float x[4];
-#pragma unroll
-                for (int h = 0; h < 4; h++) {
-                    const uint32_t w = raw[i][2 * e2 + (h >> 1)];
-                    const float v = to_f32((h & 1) ? (w >> 16) : (w & 0xFFFFu));
-                    x[h] = __builtin_amdgcn_ldexpf(flip ? -v : v, eq);
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t w = raw[i][e] & 0x7FFF7FFFu;
+                    mx = max(mx, max(w & 0xFFFFu, w >> 16));
                 }
-                if constexpr (I8) {
-                    // exact f16 pairs (d = 8 lh + 4 e2 + 0..3 of k-step i)
-                    qh[i][2 * e2] = pack_f16(x[0], x[1]);
-                    qh[i][2 * e2 + 1] = pack_f16(x[2], x[3]);
-                } else {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+            // 2^eq puts the largest |q| in [2^7, 2^8), inside E4M3's range (largest finite 448); for
+            // INT8 KV (f16 q) in [2^14, 2^15)
+            const int target = I8 ? 14 : 7;
+            int eq = 0;
+            if (mx != 0) eq = QT == KV_BF16 ? target + 127 - (int)(mx >> 7) : target + 15 - (int)(mx >> 10);
+            // per-tensor scale: the multiplier is kept >= 0 (the tile max is then taken on raw scores)
+            const bool flip = SCALE == SC_TENSOR && qk_scale < 0.0f;
+            qk_head = __builtin_amdgcn_ldexpf(flip ? -qk_scale : qk_scale, -eq);
+            auto to_f32 = [](uint32_t h) -> float {
+                if constexpr (QT == KV_BF16) return __builtin_bit_cast(float, h << 16);
+                else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+            };
 #pragma unroll
-                    for (int t = 0; t < NQT; t++) {
-                        // nearest E4M3 values (exact hardware convert, ties to even); the remainder is
-                        // exact in fp32 and has few enough significant bits for the next term
-                        i16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[0], x[1], 1.0f, false);
-                        c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[2], x[3], 1.0f, true);
-                        const uint32_t cw = __builtin_bit_cast(uint32_t, c);
-                        qf8[t][i >> 2][2 * (i & 3) + e2] = (int)cw;
-                        if (t + 1 < NQT) {
-                            const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, false);
-                            const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, true);
-                            x[0] -= lo[0];
-                            x[1] -= lo[1];
-                            x[2] -= hi[0];
-                            x[3] -= hi[1];
+            for (int i = 0; i < 8; i++)
+#pragma unroll
+                for (int e2 = 0; e2 < 2; e2++) {
+                    // values 4 e2 .. 4 e2 + 3 of raw[i]: d = 8 c + 4 e2 + 0..3 -> dword 2 c + e2 of a term
+                    float x[4];
+#pragma unroll
+                    for (int h = 0; h < 4; h++) {
+                        const uint32_t w = raw[i][2 * e2 + (h >> 1)];
+                        const float v = to_f32((h & 1) ? (w >> 16) : (w & 0xFFFFu));
+                        x[h] = __builtin_amdgcn_ldexpf(flip ? -v : v, eq);
+                    }
+                    if constexpr (I8) {
+                        // exact f16 pairs (d = 8 lh + 4 e2 + 0..3 of k-step i)
+                        qh[i][2 * e2] = pack_f16(x[0], x[1]);
+                        qh[i][2 * e2 + 1] = pack_f16(x[2], x[3]);
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < NQT; t++) {
+                            // nearest E4M3 values (exact hardware convert, ties to even); the remainder is
+                            // exact in fp32 and has few enough significant bits for the next term
+                            i16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, x[0], x[1], 1.0f, false);
+                            c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[2], x[3], 1.0f, true);
+                            const uint32_t cw = __builtin_bit_cast(uint32_t, c);
+                            qf8[t][i >> 2][2 * (i & 3) + e2] = (int)cw;
+                            if (t + 1 < NQT) {
+                                const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, false);
+                                const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, 1.0f, true);
+                                x[0] -= lo[0];
+                                x[1] -= lo[1];
+                                x[2] -= hi[0];
+                                x[3] -= hi[1];
+                            }
                         }
                     }
                 }
-            }
+        }
     };
     auto reset_state = [&]() {
 #pragma unroll
@@ -481,25 +527,41 @@ void wide_partition_kernel(Params p) {
         for (int jj = 0; jj < 4 / WPG; jj++) {
             const int j = wave * (4 / WPG) + jj;  // wave-uniform
             const int ks = j >> 1, hh = j & 1;
-            uint32_t w[4];
-            lds_read_rows4(w, vsrc + (16 * ks + 4 * hh + 8 * th) * LY::ROWB + 4 * lv);
             uint32_t o[4][2];  // [dt][token pair]
+            if constexpr (KV16) {
+                // 16-bit V: 8 bytes (d = 4 lv .. 4 lv + 3) of each of the four token rows; the pair
+                // (token 2u, token 2u + 1) of one d is a halfword permute, no conversion
+                u32x2_t w2[4];
+                lds_read_rows4_b64(w2, vsrc + (16 * ks + 4 * hh + 8 * th) * LY::ROWB + 8 * lv);
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
-                if constexpr (I8) {
-                    // byte k of rows 2u, 2u+1 -> bytes 0 and 2 of a dword (zeros between: selector
-                    // 0x0C) -> the exact f16 pair of the two codes
+                for (int u = 0; u < 2; u++) {
+                    const u32x2_t a = w2[2 * u + 1], b = w2[2 * u];
+                    const uint32_t a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+                    o[0][u] = __builtin_amdgcn_perm(a0, b0, 0x05040100u);
+                    o[1][u] = __builtin_amdgcn_perm(a0, b0, 0x07060302u);
+                    o[2][u] = __builtin_amdgcn_perm(a1, b1, 0x05040100u);
+                    o[3][u] = __builtin_amdgcn_perm(a1, b1, 0x07060302u);
+                }
+            } else {
+                uint32_t w[4];
+                lds_read_rows4(w, vsrc + (16 * ks + 4 * hh + 8 * th) * LY::ROWB + 4 * lv);
 #pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        o[k][u] = i8x2_to_f16x2(__builtin_amdgcn_perm(w[2 * u + 1], w[2 * u],
-                                                                      0x0C000C00u | ((4u + k) << 16) | (uint32_t)k));
-                } else {
-                    const uint32_t x = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x05010400u);
-                    const uint32_t y = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x07030602u);
-                    o[0][u] = cvt_fp8x2<KV_F16, false>(x);
-                    o[1][u] = cvt_fp8x2<KV_F16, true>(x);
-                    o[2][u] = cvt_fp8x2<KV_F16, false>(y);
-                    o[3][u] = cvt_fp8x2<KV_F16, true>(y);
+                for (int u = 0; u < 2; u++) {
+                    if constexpr (I8) {
+                        // byte k of rows 2u, 2u+1 -> bytes 0 and 2 of a dword (zeros between: selector
+                        // 0x0C) -> the exact f16 pair of the two codes
+#pragma unroll
+                        for (int k = 0; k < 4; k++)
+                            o[k][u] = i8x2_to_f16x2(__builtin_amdgcn_perm(w[2 * u + 1], w[2 * u],
+                                                                              0x0C000C00u | ((4u + k) << 16) | (uint32_t)k));
+                    } else {
+                        const uint32_t x = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x05010400u);
+                        const uint32_t y = __builtin_amdgcn_perm(w[2 * u + 1], w[2 * u], 0x07030602u);
+                        o[0][u] = cvt_fp8x2<KV_F16, false>(x);
+                        o[1][u] = cvt_fp8x2<KV_F16, true>(x);
+                        o[2][u] = cvt_fp8x2<KV_F16, false>(y);
+                        o[3][u] = cvt_fp8x2<KV_F16, true>(y);
+                    }
                 }
             }
             const uint32_t at = vdst + ks * 4 * kVStageBlock + 16 * (32 * hh + lv) + 8 * th;
@@ -510,7 +572,7 @@ void wide_partition_kernel(Params p) {
 
     // K operand of q.k^T for the tile about to be computed (read one tile ahead): E4M3 raw bytes
     // from the ring; INT8 exact f16 from its staging buffer
-    u32x4_t kr[4];
+    u32x4_t kr[NKR];
     u32x4_t kf[KVT == KV_I8 ? 8 : 1];
     auto read_kf = [&](int kbuf) {
         const u32x4_t *kp = (const u32x4_t *)(kstage + kbuf * kKStageBytes) + lane;
@@ -519,7 +581,13 @@ void wide_partition_kernel(Params p) {
     };
     auto read_k = [&](int si) {
         const uint32_t b = ring0 + si * LY::SLOT;
-        lds_read_4x16(kr, b + koff[0], b + koff[1], b + koff[2], b + koff[3]);
+#pragma unroll
+        for (int h = 0; h < NKR / 4; h++) {
+            u32x4_t r4[4];
+            lds_read_4x16(r4, b + koff[4 * h], b + koff[4 * h + 1], b + koff[4 * h + 2], b + koff[4 * h + 3]);
+#pragma unroll
+            for (int i = 0; i < 4; i++) kr[4 * h + i] = r4[i];
+        }
     };
     // ---- INT8 KV: K of the tile in ring slot si -> exact f16 staging buffer buf, this wave's share.
     // Operand layout: block ks of 1 KB holds, for each lane l = (i, hh) of the reading wave, the 8
@@ -596,6 +664,13 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
             for (int ks = 0; ks < 8; ks++) S = mfma32_f16(kf[ks], qh[ks], S);
             convert_next();
+        } else if constexpr (KV16) {
+            // 16-bit KV: K from the ring times q, both of q's type, eight 16-deep k-steps
+#pragma unroll
+            for (int r = 0; r < 16; r++) S[r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) S = mfma32_qk<KVT>(kr[kk], qh[kk], S);
+            convert_next();
         } else {
             // E4M3: FP8 MFMAs, two 64-deep k-steps, NQT terms of q each
 #pragma unroll
@@ -668,7 +743,8 @@ void wide_partition_kernel(Params p) {
 #pragma unroll
             for (int r = 0; r < 16; r++) keep_if_ge(pj[r], last - 8 * (r >> 2) - (r & 3), lh4);
         }
-        if constexpr (SCALE == SC_TOKEN_HEAD) {
+        if constexpr (SCALE == SC_TOKEN_HEAD || KVT == KV_BF16) {
+            // (bf16 KV: the weights p.V multiplies are hi + lo, the f32 weights to ~2^-16)
             float psum = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r++) psum += pj[r];
@@ -696,19 +772,39 @@ void wide_partition_kernel(Params p) {
                     vsc[j] = __builtin_bit_cast(float, w);
                 }
             }
-            uint32_t pp[4];
+            if constexpr (KVT == KV_BF16) {
+                // P as bf16 hi + lo against the staged bf16 V: two MFMAs per d-tile
+                uint32_t hi2[4], lo2[4];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                float p0 = pj[8 * ks + 2 * u], p1 = pj[8 * ks + 2 * u + 1];
-                if constexpr (SCALE == SC_TOKEN_HEAD) {
-                    p0 *= vsc[2 * u];
-                    p1 *= vsc[2 * u + 1];
+                for (int u = 0; u < 4; u++) {
+                    const float p0 = pj[8 * ks + 2 * u], p1 = pj[8 * ks + 2 * u + 1];
+                    const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+                    const float r0 = p0 - __builtin_bit_cast(float, h0 << 16);
+                    const float r1 = p1 - __builtin_bit_cast(float, h1 << 16);
+                    hi2[u] = h0 | (h1 << 16);
+                    lo2[u] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
                 }
-                pp[u] = pack_f16(p0, p1);
-            }
-            const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
+                const u32x4_t phi = {hi2[0], hi2[1], hi2[2], hi2[3]}, plo = {lo2[0], lo2[1], lo2[2], lo2[3]};
 #pragma unroll
-            for (int dt = 0; dt < 4; dt++) acc[dt] = mfma32_f16(va[ks][dt], pop, acc[dt]);
+                for (int dt = 0; dt < 4; dt++) {
+                    acc[dt] = mfma32_qk<KV_BF16>(va[ks][dt], phi, acc[dt]);
+                    acc[dt] = mfma32_qk<KV_BF16>(va[ks][dt], plo, acc[dt]);
+                }
+            } else {
+                uint32_t pp[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    float p0 = pj[8 * ks + 2 * u], p1 = pj[8 * ks + 2 * u + 1];
+                    if constexpr (SCALE == SC_TOKEN_HEAD) {
+                        p0 *= vsc[2 * u];
+                        p1 *= vsc[2 * u + 1];
+                    }
+                    pp[u] = pack_f16(p0, p1);
+                }
+                const u32x4_t pop = {pp[0], pp[1], pp[2], pp[3]};
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) acc[dt] = mfma32_f16(va[ks][dt], pop, acc[dt]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (I8) read_kf(buf ^ 1);  // converted last step, published by this step's barrier
@@ -739,6 +835,16 @@ void wide_partition_kernel(Params p) {
             // E4M3 KV: f16 of value / (largest |value| of the head's row, spread over the two lane
             // halves), the scale beside it
             const size_t slot = (((size_t)wg * 2 + (seg == 0 ? 0 : 1)) * WPG + wave) * kWideHeadBlock + li;
+            if constexpr (KV16) {
+                // 16-bit KV: fp32 rows (no scales: the accumulator is the value)
+                float *dst = p.ws_acc + slot * D;
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    *(float4 *)(dst + 4 * (8 * (r >> 2) + 4 * lh + (r & 3))) =
+                        make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+                if (lh == 0) p.ws_ml[slot] = make_float2(m_run, l_tot);
+                return;
+            }
             float mx = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r++)
@@ -834,7 +940,9 @@ static hipError_t launch_w(const Params &p, hipStream_t stream) {
     // tiles in flight per workgroup: up to NSLOT-1; ring + V staging (16 KB) fit two 4-wave
     // workgroups, or three 2-wave ones, in one CU's 160 KB of LDS; with INT8's K staging (16 KB
     // more) two workgroups of either size
-    constexpr int NSLOT = KVT == KV_I8 ? 5 : (WPG == 2 ? 4 : (SCALE == SC_TOKEN_HEAD ? 5 : 6));
+    // (16-bit KV: slots of 16 KB, four of them and the staging fill 80 KB, two workgroups per CU)
+    constexpr int NSLOT = (KVT == KV_I8 || KVT == KV_F16 || KVT == KV_BF16) ? (KVT == KV_I8 ? 5 : 4)
+                                                                           : (WPG == 2 ? 4 : (SCALE == SC_TOKEN_HEAD ? 5 : 6));
     dim3 grid(p.nparts), block(64 * WPG);
     if (p.block_table && p.block_size == 16)  // 32-token tiles span two blocks
         hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
@@ -858,6 +966,12 @@ static hipError_t launch_wq(const Params &p, int qt, int sc, hipStream_t stream)
 hipError_t launch_wide_partition(const Params &p, int kv_dtype, int q_dtype, int scale_mode, hipStream_t stream) {
     if (p.d != 128 || p.hb != kWideHeadBlock || (p.wpg != 2 && p.wpg != 4) || p.nhb % p.wpg)
         return hipErrorInvalidValue;
+    if (kv_dtype == KV_F16 || kv_dtype == KV_BF16) {
+        // 16-bit KV: q of the same type, no scales, four head blocks per workgroup
+        if (q_dtype != kv_dtype || scale_mode != SC_NONE || p.wpg != 4) return hipErrorInvalidValue;
+        if (kv_dtype == KV_F16) return launch_w<KV_F16, 4, KV_F16, SC_NONE>(p, stream);
+        return launch_w<KV_BF16, 4, KV_BF16, SC_NONE>(p, stream);
+    }
     if (kv_dtype != KV_FP8 && kv_dtype != KV_I8) return hipErrorInvalidValue;
     if (kv_dtype == KV_I8) {
         if (p.wpg == 4) return launch_wq<KV_I8, 4>(p, q_dtype, scale_mode, stream);

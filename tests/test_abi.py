@@ -58,8 +58,11 @@ def test_plan_and_workspace_sizes():
     # E4M3 group of 128 heads: wide kernel, 4 waves of 32 heads per workgroup, 2048 waves
     assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3") == 512
     assert fd.workspace_bytes(4, 128, 1, 128, 131072, 64, "fp8_e4m3") >= 512 * 2 * 4 * 32 * (12 + 128 * 2)
-    # same group with bf16 KV: 16-head kernel, 8 head blocks per workgroup
-    assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "bf16") == 256
+    # same group with bf16 KV: the wide kernel too (4 waves per workgroup, fp32 partial rows)
+    assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "bf16") == 512
+    assert fd.workspace_bytes(4, 128, 1, 128, 131072, 64, "bf16") >= 512 * 2 * 4 * 32 * (12 + 128 * 4)
+    # bf16 group of 64 (not a multiple of 128): 16-head kernel, 4 head blocks per workgroup
+    assert fd.plan_partitions(4, 64, 1, 128, 131072, 64, "bf16") == 512
     # group of 64 on 2 kv heads: wide kernel with 2 waves per workgroup, capped by 2*2*128 tiles
     assert fd.plan_partitions(2, 128, 2, 128, 4096, 64, "fp8_e4m3") == 512
     # group of 32 with E4M3: the 32-column kernel, one unit (one wave) per kv head, 2048 waves

@@ -4,7 +4,7 @@ turns into scratch-memory traffic on every tile -- a small source edit once adde
 to the 128K MQA variant and 16 % more HBM reads -- so the variants the workloads run are held at
 zero here:
   * every 16-head partition kernel and every combine kernel: 0 VGPR spills;
-  * the wide-group kernel with a per-tensor scale (the MQA workloads): 0;
+  * the wide-group kernel with a per-tensor scale (the MQA workloads) or none (f16 / bf16 KV): 0;
   * the wide-group kernel with per-token scales: at most 8 (a known cost at three waves per SIMD;
     no benchmark workload is wide with per-token scales).
 Skipped when the objects or the LLVM tools are not there."""
@@ -59,12 +59,16 @@ def test_partition_and_combine_kernels_do_not_spill():
 def test_wide_kernel_spills():
     sp = kernel_spills(os.path.join(BUILD, "fd_wide.hip.o"))
     assert sp
-    # template arguments <KVT, WPG, NSLOT, QT, SCALE, PAGED, B16>: SCALE 1 = per tensor, 2 = per token
+    # template arguments <KVT, WPG, NSLOT, QT, SCALE, PAGED, B16>: SCALE 0 = none, 1 = per tensor,
+    # 2 = per token; KVT 1 / 2 = f16 / bf16
+    kvts = set()
     for k, v in sp.items():
         m = re.search(r"wide_partition_kernelILi(\d)ELi(\d)ELi(\d)ELi(\d)ELi(\d)E", k)
         assert m, k
+        kvts.add(int(m.group(1)))
         scale = int(m.group(5))
-        assert v <= (0 if scale == 1 else 8), (k, v)
+        assert v <= (8 if scale == 2 else 0), (k, v)
+    assert kvts == {1, 2, 3, 4}, kvts
 
 
 def test_direct_kernel_spills():

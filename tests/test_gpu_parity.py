@@ -125,7 +125,6 @@ SMALL = [
                               scale="none", block_size=16)),
     ("bs16_wide_g128_tok", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1000, 31], kv="fp8_e4m3",
                                 q="bf16", scale="token_head", block_size=16)),
-    # wide-group kernel with INT8 KV (int8 MFMAs for q.k^T on the raw codes, q in three int8 terms)
     # 32-column units, K/V straight into registers (E4M3 KV, head_dim 128, 32 MFMA columns per kv head)
     ("direct_g32_tok", dict(batch=3, hq=64, hkv=2, d=128, seq_lens=[1000, 33, 4097], kv="fp8_e4m3",
                             q="bf16", scale="token_head", block_size=64)),
@@ -135,6 +134,7 @@ SMALL = [
                                         q="f16", scale="token_head", paged=False, block_size=0)),
     ("direct_g96_tok_bs32", dict(batch=2, hq=96, hkv=1, d=128, seq_lens=[1500, 64], kv="fp8_e4m3",
                                  q="bf16", scale="token_head", block_size=32)),
+    # wide-group kernel with INT8 KV (K and V staged once per workgroup as exact f16)
     ("wide_i8_g64_tok", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[1000, 33, 4097], kv="int8",
                              q="bf16", scale="token_head", block_size=64)),
     ("wide_i8_g128_tok_contig_f16q", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[300, 1], kv="int8",
@@ -145,6 +145,19 @@ SMALL = [
                                       q="bf16", scale="tensor", block_size=16)),
     ("bs16_wide_g64_tensor", dict(batch=3, hq=128, hkv=2, d=128, seq_lens=[65, 300, 1], kv="fp8_e4m3",
                                   q="bf16", scale="tensor", block_size=16)),
+    # wide-group kernel with f16 / bf16 KV (groups of 128+: K read from the ring as is, V re-laid
+    # without conversion, bf16 P in two terms): both types, paged (64, 32, 16) and contiguous, two
+    # workgroups per kv head (G = 256), two kv heads
+    ("wide16_bf16_g128", dict(batch=3, hq=128, hkv=1, d=128, seq_lens=[1000, 33, 4097], kv="bf16",
+                              q="bf16", scale="none", block_size=64)),
+    ("wide16_f16_g128_contig", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[300, 1], kv="f16", q="f16",
+                                    scale="none", paged=False, block_size=0)),
+    ("wide16_bf16_g256_bs32", dict(batch=2, hq=256, hkv=1, d=128, seq_lens=[700, 64], kv="bf16",
+                                   q="bf16", scale="none", block_size=32)),
+    ("wide16_f16_g128_hkv2_bs16", dict(batch=3, hq=256, hkv=2, d=128, seq_lens=[65, 300, 1], kv="f16",
+                                       q="f16", scale="none", block_size=16)),
+    ("wide16_bf16_g128_hkv2", dict(batch=2, hq=256, hkv=2, d=128, seq_lens=[2500, 95], kv="bf16",
+                                   q="bf16", scale="none", block_size=64)),
     # one long sequence over few units: many pieces per row, merged by several combine waves
     ("mqa8_d64_long_f16", dict(batch=1, hq=8, hkv=1, d=64, seq_lens=[4000], kv="f16", q="f16",
                                scale="none", block_size=32)),
@@ -195,13 +208,13 @@ def test_int8_length_edges(n, bs):
         check_case(f"i8_len{n}_bs{bs}/p{parts}", case, num_partitions=parts)
 
 
-@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8", "bf16"])
 @pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 191, 192, 193, 4095])
 def test_wide_length_edges(n, kv):
     lens = [n, 7, n]
     case = workloads.custom_case(seed=100 + n, device="cuda", batch=3, hq=128, hkv=1, d=128, seq_lens=lens,
-                                 kv=kv, q="bf16", scale="token_head", block_size=64,
-                                 max_seq_len=max(lens + [1]))
+                                 kv=kv, q="bf16", scale="none" if kv == "bf16" else "token_head",
+                                 block_size=64, max_seq_len=max(lens + [1]))
     for parts in (0, 3):
         check_case(f"wide_{kv}_len{n}/p{parts}", case, num_partitions=parts)
 
@@ -227,12 +240,12 @@ def test_block16_ragged_mix():
         check_case(f"bs16_ragged/p{parts}", case, num_partitions=parts)
 
 
-@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8", "f16"])
 def test_wide_ragged_mix(kv):
     lens = [0, 1, 5000, 33, 0, 64, 2047, 12000, 31, 0, 700, 96]
-    case = workloads.custom_case(seed=22, device="cuda", batch=len(lens), hq=128, hkv=2, d=128,
-                                 seq_lens=lens, kv=kv, q="bf16", scale="token_head",
-                                 block_size=32)
+    case = workloads.custom_case(seed=22, device="cuda", batch=len(lens), hq=256 if kv == "f16" else 128,
+                                 hkv=2, d=128, seq_lens=lens, kv=kv, q="f16" if kv == "f16" else "bf16",
+                                 scale="none" if kv == "f16" else "token_head", block_size=32)
     for parts in (1, 7, 100, 1024):
         check_case(f"wide_{kv}_ragged/p{parts}", case, num_partitions=parts)
 
@@ -395,6 +408,11 @@ def test_workload_mqa_fp8_128k_full():
 def test_workload_mqa_i8_128k_full():
     # INT8 KV, the same shape (the wide-group kernel's int8 path)
     check_case("mqa_i8_128k", workloads.make_case("mqa_i8_128k", device="cuda"))
+
+
+def test_workload_mqa_bf16_64k_full():
+    # bf16 KV, 128 heads on one kv head (the wide-group kernel's 16-bit path), every output row
+    check_case("mqa_bf16_64k", workloads.make_case("mqa_bf16_64k", device="cuda"))
 
 
 def test_workload_ragged_fp8_full():

@@ -19,6 +19,8 @@ Workloads (sizes as specified for the decode workloads this library targets):
                         32 q / 8 kv heads, head_dim 128, E4M3 KV, block_size 32, shuffled blocks.
 * ``int8_32k``          ``fp8_32k`` with INT8 KV (per-(token, kv-head) scales).
 * ``mqa_i8_128k``       ``mqa_fp8_128k`` with INT8 KV (one per-tensor scale).
+* ``mqa_bf16_64k``      batch 4, seq_len 65536, 128 q / 1 kv head, head_dim 128, bf16 KV
+                        (the same KV bytes as ``mqa_fp8_128k``), block_size 64.
 * ``verify_fp8_32k``    ``fp8_32k`` with a window of 4 query tokens per sequence (a speculative-
                         decoding verify pass over 4 draft tokens already in the cache).
 
@@ -80,6 +82,8 @@ WORKLOADS = {
                      q="bf16", block_size=64, scale="token_head", paged=True),
     "mqa_i8_128k": dict(batch=4, hq=128, hkv=1, d=128, lens=("fixed", 131072), kv="int8",
                         q="bf16", block_size=64, scale="tensor", paged=True),
+    "mqa_bf16_64k": dict(batch=4, hq=128, hkv=1, d=128, lens=("fixed", 65536), kv="bf16",
+                         q="bf16", block_size=64, scale="none", paged=True),
     "verify_fp8_32k": dict(batch=32, hq=64, hkv=8, d=128, lens=("loguniform", 1024, 32768),
                            kv="fp8_e4m3", q="bf16", block_size=64, scale="token_head", paged=True,
                            nq=4),
