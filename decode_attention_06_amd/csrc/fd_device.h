@@ -115,6 +115,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     return u >> 16;
 }
 
+// bf16 pair, a in the low half: round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// A pair of p.V weights as two bf16 terms: hi = bf16(p), lo = bf16(p - hi) (p - hi is exact in
+// fp32), so hi + lo carries p to ~2^-16 against a bf16 V operand.
+__device__ __forceinline__ void split_bf16_pair(float p0, float p1, uint32_t &hi, uint32_t &lo) {
+    hi = pack_bf16(p0, p1);
+    const float r0 = p0 - __builtin_bit_cast(float, hi << 16);
+    const float r1 = p1 - __builtin_bit_cast(float, hi & 0xFFFF0000u);
+    lo = pack_bf16(r0, r1);
+}
+
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
     f16x2_t v = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(uint32_t, v);

@@ -555,13 +555,7 @@ void partition_kernel(Params p) {
         if constexpr (KVT == KV_BF16) {
             uint32_t hi2[4], lo2[4];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const uint32_t h0 = f32_to_bf16_bits(pj[2 * u]), h1 = f32_to_bf16_bits(pj[2 * u + 1]);
-                const float r0 = pj[2 * u] - __builtin_bit_cast(float, h0 << 16);
-                const float r1 = pj[2 * u + 1] - __builtin_bit_cast(float, h1 << 16);
-                hi2[u] = h0 | (h1 << 16);
-                lo2[u] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-            }
+            for (int u = 0; u < 4; u++) split_bf16_pair(pj[2 * u], pj[2 * u + 1], hi2[u], lo2[u]);
             const u32x4_t phi = {hi2[0], hi2[1], hi2[2], hi2[3]}, plo = {lo2[0], lo2[1], lo2[2], lo2[3]};
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) {

@@ -776,14 +776,7 @@ void wide_partition_kernel(Params p) {
                 // P as bf16 hi + lo against the staged bf16 V: two MFMAs per d-tile
                 uint32_t hi2[4], lo2[4];
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const float p0 = pj[8 * ks + 2 * u], p1 = pj[8 * ks + 2 * u + 1];
-                    const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-                    const float r0 = p0 - __builtin_bit_cast(float, h0 << 16);
-                    const float r1 = p1 - __builtin_bit_cast(float, h1 << 16);
-                    hi2[u] = h0 | (h1 << 16);
-                    lo2[u] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-                }
+                for (int u = 0; u < 4; u++) split_bf16_pair(pj[8 * ks + 2 * u], pj[8 * ks + 2 * u + 1], hi2[u], lo2[u]);
                 const u32x4_t phi = {hi2[0], hi2[1], hi2[2], hi2[3]}, plo = {lo2[0], lo2[1], lo2[2], lo2[3]};
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) {
