@@ -89,11 +89,11 @@ def kernel_hash() -> str:
 
 def partition_kernel_name(case) -> str:
     """Which partition kernel the library's plan runs for this case: E4M3 or INT8 KV, head_dim 128
-    and a multiple of 64 query heads per kv head with one query token take the wide-group kernel
-    (f16 / bf16 KV: a multiple of 128 heads); otherwise E4M3 KV, head_dim 128 and a multiple of 32
+    and a multiple of 64 query heads per kv head take the wide-group kernel (f16 / bf16 KV: a
+    multiple of 128 heads; any query window); otherwise E4M3 KV, head_dim 128 and a multiple of 32
     MFMA columns per kv head (query heads x query tokens) the 32-column kernel; everything else
     the 16-head kernel."""
-    if case.d == 128 and case.nq == 1 and (
+    if case.d == 128 and (
             (case.kv_dtype in ("fp8_e4m3", "int8") and case.group % 64 == 0)
             or (case.kv_dtype in ("f16", "bf16") and case.group % 128 == 0)):
         return "wide_partition_kernel"

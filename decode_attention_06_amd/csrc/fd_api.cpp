@@ -45,13 +45,15 @@ struct Plan {
 };
 
 // Groups of 64+ query heads per kv head with E4M3 or INT8 KV and head_dim 128 take the
-// wide-group kernel: 32 heads per wave, and 2 or 4 waves of one kv head share every K/V tile
+// wide-group kernel: 32 columns per wave, and 2 or 4 waves of one kv head share every K/V tile
 // through LDS; with f16 or bf16 KV, groups of 128+ (four waves: a 16-bit tile ring fits only two
-// workgroups per CU).  (A window of several query tokens per sequence takes the 16-column kernel.)
-// (the wide kernel forms in-tile row offsets with 24-bit multiplies: a cache row of all kv
-// heads, hkv * 256 bytes at most, stays below 2^24)
+// workgroups per CU).  A window of nq query tokens multiplies the columns (each 32-column block
+// lies in one window row, the group being a multiple of 32).  (The wide kernel forms in-tile row
+// offsets with 24-bit multiplies: a cache row of all kv heads, hkv * 256 bytes at most, stays
+// below 2^24.)
 bool use_wide(int group, int hkv, int head_dim, int kv_dtype, int nq) {
-    if (nq != 1 || head_dim != 128 || hkv >= (1 << 16)) return false;
+    (void)nq;
+    if (head_dim != 128 || hkv >= (1 << 16)) return false;
     if (kv_dtype == FD_FP8_E4M3 || kv_dtype == FD_INT8) return group % 64 == 0;
     return (kv_dtype == FD_F16 || kv_dtype == FD_BF16) && group % 128 == 0;
 }
@@ -84,7 +86,7 @@ Plan make_plan(int batch, int nq, int hq, int hkv, int head_dim, int kv_dtype, i
     pl.direct = !pl.wide && use_direct(cols, hkv, head_dim, kv_dtype);
     if (pl.wide) {
         pl.hb = fd::kWideHeadBlock;
-        pl.nhb = group / pl.hb;
+        pl.nhb = cols / pl.hb;  // every column of the window (cols is a multiple of 64)
         pl.wpg = pl.nhb % 4 == 0 ? 4 : 2;
         pl.groups = hkv * pl.nhb / pl.wpg;
     } else {

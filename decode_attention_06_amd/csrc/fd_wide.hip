@@ -52,6 +52,10 @@ namespace {
 // larger batches locate tiles with a wave scan of seq_len instead).
 constexpr int kWideLdsBatch = 256;
 
+// Tile max of a window column that sees none of the tile's tokens (log2 units): finite, and far
+// below any score a finite input can give.
+constexpr float kNoScore = -1.0e30f;
+
 // s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 field layout:
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at bits 15:14).
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -204,7 +208,7 @@ __device__ __forceinline__ void wg_barrier() {
 
 }  // namespace
 
-template <int KVT, int WPG, int NSLOT, int QT, int SCALE, bool PAGED, bool B16>
+template <int KVT, int WPG, int NSLOT, int QT, int SCALE, bool PAGED, bool B16, bool WIN>
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2)))
 void wide_partition_kernel(Params p) {
     using LY = WideLayout<KVT, WPG, SCALE>;
@@ -419,19 +423,29 @@ void wide_partition_kernel(Params p) {
     float m_run = -INFINITY, l_run = 0.0f;
     // per-token v scales: the accumulator holds values / 2^ev (wave-uniform reference exponent)
     int ev = 0;
+    // a window of nq query tokens: column (row m, head h) of the kv head sees the sequence up to
+    // nq - 1 - m tokens before its end
+    int win_off = 0;
+    // lane column li of head block hb: column col = 32 hb + li of the kv head = query row m of the
+    // window, head h of the group; its out / lse row
+    auto out_row = [&](int b, int u_in) -> size_t {
+        const int kvh = u_in / p.nhb, col = (u_in % p.nhb) * kWideHeadBlock + li;
+        const int m = col / p.group, h = kvh * p.group + col % p.group;
+        return ((size_t)b * p.nq + m) * p.hq + h;
+    };
     auto load_q = [&](int b, int grp) {
         const int u_in = grp * WPG + wave;
-        const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
-        const int head = kvh * p.group + hb * kWideHeadBlock + li;
+        if constexpr (WIN) win_off = p.nq - 1 - ((u_in % p.nhb) * kWideHeadBlock + li) / p.group;
+        const size_t qrow_idx = out_row(b, u_in);
         if constexpr (KV16) {
-            const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + 64 * lh;
+            const uint16_t *qrow = (const uint16_t *)p.q + qrow_idx * D + 64 * lh;
 #pragma unroll
             for (int kk = 0; kk < 8; kk++) qh[kk] = *(const u32x4_t *)(qrow + 8 * kk);
             // complete here (once per segment; see below)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             qk_head = qk_scale;
         } else {
-            const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.hq + head) * D + (I8 ? 8 : 32) * lh;
+            const uint16_t *qrow = (const uint16_t *)p.q + qrow_idx * D + (I8 ? 8 : 32) * lh;
             // E4M3: raw[4 ks + c] holds d = 64 ks + 32 lh + 8 c + 0..7; INT8: raw[ks] holds
             // d = 16 ks + 8 lh + 0..7
             u32x4_t raw[8];
@@ -620,7 +634,8 @@ void wide_partition_kernel(Params p) {
     // (ring slot si_next) is converted into the other buffer while the q.k^T MFMAs run, and the
     // next tile's K is read while the p.V MFMAs run (that tile has landed and was published by
     // this step's barrier; its slot is refilled two steps later)
-    auto compute = [&](int si, int buf, int last, int si_next) {
+    auto compute = [&](int si, int buf, int nrel, int si_next) {
+        const int last = min(nrel, kTile) - 1;  // rows past it repeat it (valid; masked later)
         const uint32_t sbase = ring0 + si * LY::SLOT;
         // p.V's A operands of both k-steps, read now (plain loads: the staging buffer is never a
         // copy target, so the compiler waits for these reads only where p.V uses them)
@@ -697,12 +712,29 @@ void wide_partition_kernel(Params p) {
         float s[16];
 #pragma unroll
         for (int r = 0; r < 16; r++) s[r] = (SCALE == SC_TOKEN_HEAD) ? S[r] * (ksc[r] * qk_head) : S[r];
+        // a window's column stops nq - 1 - m tokens before the sequence's end: its later tokens are
+        // real rows (of other columns) and are kept out of the max and the weights
+        // (a separate instantiation: the one-token step keeps none of this in its registers)
+        const int lastc = WIN ? min(nrel - win_off, kTile) - 1 : last;
+        const bool wmask = WIN && __any(lastc < kTile - 1);  // wave-uniform
+        if (wmask) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (8 * (r >> 2) + lh4 + (r & 3) > lastc) s[r] = -INFINITY;
+        }
         float mt = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
         for (int r = 3; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[r]), s[r + 1]);
         mt = fmaxf(mt, s[15]);
-        mt = max_halves(mt);  // finite: token 0 of the tile is valid
-        if constexpr (SCALE != SC_TOKEN_HEAD) mt *= qk_head;
+        mt = max_halves(mt);
+        if constexpr (WIN) {
+            // (-inf only for a window column that sees nothing of the tile: a finite stand-in far
+            // below any score keeps m_run finite -- no -inf - -inf below -- and its weights are zeroed)
+            if constexpr (SCALE != SC_TOKEN_HEAD) mt = mt > -INFINITY ? mt * qk_head : kNoScore;
+            else mt = mt > -INFINITY ? mt : kNoScore;
+        } else if constexpr (SCALE != SC_TOKEN_HEAD) {
+            mt *= qk_head;  // finite: token 0 of the tile is valid
+        }
         // per-token v scales: reference exponent of the tile's largest |v scale| (the lane's 16
         // tokens, then the other lane half); it replaces ev when out of ev's window
         int evt = ev;
@@ -719,7 +751,7 @@ void wide_partition_kernel(Params p) {
         }
         const bool emove = evt > ev + kVrefHigh || evt < ev - kVrefLow;
         if (__any(mt > m_run + kRescaleSlack) || emove) {  // wave-uniform; always taken on a segment's first tile
-            const float m_new = fmaxf(m_run, mt);  // finite: token 0 of the tile is valid
+            const float m_new = fmaxf(m_run, mt);  // finite (mt is)
             const float dm = m_run - m_new;
             const float alpha = __builtin_amdgcn_exp2f(dm);
             // the accumulator also moves from units of 2^ev to units of 2^evt (exact for a power of two)
@@ -738,10 +770,15 @@ void wide_partition_kernel(Params p) {
         const float m_ref = m_run + (SCALE == SC_TOKEN_HEAD ? (float)ev : 0.0f);
 #pragma unroll
         for (int r = 0; r < 16; r++)
-            pj[r] = __builtin_amdgcn_exp2f((SCALE == SC_TOKEN_HEAD) ? s[r] - m_ref : __builtin_fmaf(S[r], qk_head, -m_ref));
+            pj[r] = __builtin_amdgcn_exp2f((SCALE == SC_TOKEN_HEAD) ? s[r] - m_ref : __builtin_fmaf(WIN ? s[r] : S[r], qk_head, -m_ref));
         if (last < kTile - 1) {  // a partial tile: weight 0 for tokens 8(r/4) + 4lh + r%4 past `last`
 #pragma unroll
             for (int r = 0; r < 16; r++) keep_if_ge(pj[r], last - 8 * (r >> 2) - (r & 3), lh4);
+        }
+        if (wmask) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (8 * (r >> 2) + lh4 + (r & 3) > lastc) pj[r] = 0.0f;
         }
         if constexpr (SCALE == SC_TOKEN_HEAD || KVT == KV_BF16) {
             // (bf16 KV: the weights p.V multiplies are hi + lo, the f32 weights to ~2^-16)
@@ -807,22 +844,20 @@ void wide_partition_kernel(Params p) {
 
     // ---- segment result (lane (li, lh) holds d = 4i + dt, i = 8(r/4) + 4lh + r%4, in acc[dt][r])
     auto finalize = [&](const Cursor &k, int seg, bool whole) {
-        const int u_in = k.grp * WPG + wave;
-        const int kvh = u_in / p.nhb, hb = u_in % p.nhb;
-        const int head = kvh * p.group + hb * kWideHeadBlock + li;
+        const size_t orow_idx = out_row(k.b, k.grp * WPG + wave);
         const float l_tot = l_run + shfl_xor_f(l_run, 32);
         // factor of the accumulator: the tensor v scale, or 2^ev with per-token scales
         // (2^ev is a normal float: |ev| <= 100)
         const float sv = (SCALE == SC_TENSOR) ? tensor_v : __builtin_bit_cast(float, (uint32_t)(ev + 127) << 23);
         if (whole) {
-            const size_t orow = ((size_t)k.b * p.hq + head) * D;
-            const float inv = sv / l_tot;
+            const size_t orow = orow_idx * D;
+            const float inv = l_tot > 0.0f ? sv / l_tot : 0.0f;  // 0: a window row that sees no token
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const float v[4] = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
                 store_row_chunk<4>(p.out, p.out_dtype, orow + 4 * (8 * (r >> 2) + 4 * lh + (r & 3)), v);
             }
-            if (p.lse && lh == 0) p.lse[(size_t)k.b * p.hq + head] = (m_run + log2f(l_tot)) * kLn2;
+            if (p.lse && lh == 0) p.lse[orow_idx] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
         } else {
             // slot 0: the range's first segment; slot 1: its last (a middle one is always whole).
             // E4M3 KV: f16 of value / (largest |value| of the head's row, spread over the two lane
@@ -907,7 +942,7 @@ void wide_partition_kernel(Params p) {
         // (computing converts the next tile's V; past the range end that slot holds a repeat of the
         // last tile: converted, never read)
         const int t0 = cc.tt * kTile;
-        compute(slot_c, buf, min(cc.n - t0, kTile) - 1, next_slot(slot_c));
+        compute(slot_c, buf, cc.n - t0, next_slot(slot_c));
         slot_c = next_slot(slot_c);
         buf ^= 1;
         const bool end_unit = cc.tt + 1 == cc.Tb;
@@ -937,12 +972,20 @@ static hipError_t launch_w(const Params &p, hipStream_t stream) {
     constexpr int NSLOT = (KVT == KV_I8 || KVT == KV_F16 || KVT == KV_BF16) ? (KVT == KV_I8 ? 5 : 4)
                                                                            : (WPG == 2 ? 4 : (SCALE == SC_TOKEN_HEAD ? 5 : 6));
     dim3 grid(p.nparts), block(64 * WPG);
-    if (p.block_table && p.block_size == 16)  // 32-token tiles span two blocks
-        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true>), grid, block, 0, stream, p);
-    else if (p.block_table)
-        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, false>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, false, false>), grid, block, 0, stream, p);
+    if (p.nq > 1) {  // a window of query tokens: per-column limits
+        if (p.block_table && p.block_size == 16)
+            hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true, true>), grid, block, 0, stream, p);
+        else if (p.block_table)
+            hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, false, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, false, false, true>), grid, block, 0, stream, p);
+    } else if (p.block_table && p.block_size == 16) {  // 32-token tiles span two blocks
+        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, true, false>), grid, block, 0, stream, p);
+    } else if (p.block_table) {
+        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, true, false, false>), grid, block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((wide_partition_kernel<KVT, WPG, NSLOT, QT, SCALE, false, false, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

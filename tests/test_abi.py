@@ -246,11 +246,20 @@ def test_window_of_one_matches_the_plain_plan():
 
 
 def test_window_workspace_grows_with_the_columns():
-    # G = 8, nq = 4: 32 columns per kv head = 2 sixteen-column blocks; MQA windows leave the wide kernel
+    # G = 8, nq = 4: 32 columns per kv head (the 32-column kernel)
     one = fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3")
     four = fd.workspace_bytes(32, 64, 8, 128, 32768, 64, "fp8_e4m3", num_query=4)
     assert four >= one
-    assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3", num_query=2) == 2048 // 8
+    # MQA windows stay on the wide kernel: 256 columns = 8 head blocks, 4 waves per workgroup
+    assert fd.plan_partitions(4, 128, 1, 128, 131072, 64, "fp8_e4m3", num_query=2) == 2048 // 4
+    # a group of 64 with a window of 3: 6 head blocks, 2 waves per workgroup
+    assert fd.plan_partitions(4, 64, 1, 128, 131072, 64, "int8", num_query=3) == 1024 // 2
+    # the head blocks of a wide window cover all its columns (every window row): capped at
+    # batch x unit groups x tiles = 9 x (2 kv heads x 8 blocks / 4) x 88 for 256 heads, nq 2
+    assert fd.plan_partitions(9, 256, 2, 128, 2795, 16, "fp8_e4m3", num_partitions=100000, num_query=2) \
+        == 9 * 4 * 88
+    assert fd.plan_partitions(2, 128, 1, 128, 2049, 64, "fp8_e4m3", num_partitions=100000, num_query=2) \
+        == 2 * 2 * 65
 
 
 # ------------------------------------------------------------------ fd_check_inputs (debug validation)

@@ -80,6 +80,18 @@ WINDOW = [
                                   q="f16", scale="token_head", block_size=32)),
     ("g6_nq3_fp8_f16q_bs32", dict(batch=2, hq=12, hkv=2, d=128, seq_lens=[95, 64], nq=3, kv="fp8_e4m3",
                                   q="f16", scale="tensor", block_size=32)),
+    # the wide-group kernel (groups of 64+, LDS-shared tiles) with a window: 2- and 4-wave
+    # workgroups, every KV type, sequences shorter than the window (rows that see nothing)
+    ("wide_g64_nq3_fp8_tok", dict(batch=3, hq=64, hkv=1, d=128, seq_lens=[700, 2, 33], nq=3,
+                                  kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64)),
+    ("wide_g128_nq4_i8_tensor_bs32", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1000, 3], nq=4,
+                                          kv="int8", q="bf16", scale="tensor", block_size=32)),
+    ("wide_g128_nq2_bf16_bs16", dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[500, 1], nq=2, kv="bf16",
+                                     q="bf16", scale="none", block_size=16)),
+    ("wide_g256_nq2_f16_contig", dict(batch=2, hq=256, hkv=1, d=128, seq_lens=[300, 64], nq=2, kv="f16",
+                                      q="f16", scale="none", paged=False, block_size=0)),
+    ("wide_g64x2_nq5_fp8_tok_f16q", dict(batch=2, hq=128, hkv=2, d=128, seq_lens=[260, 40], nq=5,
+                                         kv="fp8_e4m3", q="f16", scale="token_head", block_size=64)),
 ]
 
 
@@ -112,12 +124,14 @@ def test_window_of_one_equals_the_single_token_step_bitwise():
     assert torch.equal(a, b[:, 0])
 
 
-@pytest.mark.parametrize("nq", [3, 4])
-def test_window_rows_match_single_token_steps_on_prefixes(nq):
+@pytest.mark.parametrize("nq,hq", [(3, 16), (4, 16), (3, 128)])
+def test_window_rows_match_single_token_steps_on_prefixes(nq, hq):
     # row m of the window = the plain step over the first seq_len - nq + m + 1 tokens (GPU vs GPU;
-    # nq 4 with 8 heads: the window runs on the 32-column kernel, the single rows on the 16-head one)
-    case = workloads.custom_case(seed=42, device="cuda", batch=2, hq=16, hkv=2, d=128, seq_lens=[1000, 77],
-                                 nq=nq, kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64)
+    # nq 4 with 8 heads: the window runs on the 32-column kernel, the single rows on the 16-head one;
+    # 128 heads: both on the wide kernel)
+    case = workloads.custom_case(seed=42, device="cuda", batch=2, hq=hq, hkv=2 if hq == 16 else 1, d=128,
+                                 seq_lens=[1000, 77], nq=nq, kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=64)
     win = fd.decode_case(case)
     for m in range(nq):
         c = workloads.Case(**{k: getattr(case, k) for k in case.__dataclass_fields__})
