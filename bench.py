@@ -322,6 +322,7 @@ def main():
     ap.add_argument("--layout", choices=("contiguous", "ordered", "fragmented"), default=None,
                     help="contiguous rows, or pages in table order / shuffled")
     ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--nq", type=int, default=None, help="query tokens per sequence (a verify window)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -341,6 +342,8 @@ def main():
     overrides, seq_lens = {}, None
     if args.batch is not None:
         overrides["batch"] = args.batch
+    if args.nq is not None:
+        overrides["nq"] = args.nq
     if args.block_size is not None:
         overrides["block_size"] = args.block_size
     if args.layout is not None:
@@ -481,7 +484,7 @@ def main():
             "kv_read_bytes": kv_bytes, "partitions": nparts,
             "kv_copies_rotated": ncopy, "seed": args.seed,
             "overrides": {"block_size": args.block_size, "seq_len": args.seq_len, "layout": args.layout,
-                          "batch": args.batch} if (overrides or seq_lens) else None,
+                          "batch": args.batch, "nq": args.nq} if (overrides or seq_lens) else None,
             "compute": compute_note(case),
             "parallelism": "single GPU",
         },
