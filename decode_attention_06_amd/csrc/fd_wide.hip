@@ -19,24 +19,29 @@
 //     publishes the tile and frees the slot read one tile earlier, which the next copies refill.
 //     LDS reads of the ring are issued as inline ds_read so the compiler does not add its own
 //     (conservative: every in-flight copy) waits for the direct-to-LDS writes.
-//   * q.k^T runs on v_mfma_f32_32x32x16_{bf16,f16}: A = K (32 tokens x 16 d, converted to q's
-//     type -- exact), B = q^T (16 d x 32 heads).  Lane (i = l % 32, hh = l / 32) takes
-//     d = 64 hh + 8 kk + 0..7 at k-step kk in both operands, so its K operand for all 8 k-steps is
-//     one 64-byte half row of token i: four 16-byte LDS reads.  In the ring, 16-byte chunk c of
-//     K row r is stored at chunk c ^ (r & 7), so the 8 lanes of each LDS read phase hit 8
-//     different bank groups.
+//   * q.k^T, E4M3 KV: v_mfma_scale_f32_32x32x64_f8f6f4 straight on the ring's E4M3 bytes (no K
+//     conversion), q split exactly into E4M3 terms (two for a bf16 q, three for f16) scaled per
+//     head by a power of two the score multiplier takes back.  Lane (i = l % 32, hh = l / 32) reads
+//     d = 64 ks + 32 hh + 0..31 of token i at k-step ks (two 16-byte chunks); chunk c of K row r
+//     is stored at c ^ (r & 7), so the lanes of each LDS read phase hit different bank groups.
+//     INT8 KV: each wave converts a quarter of a tile's K into an exact-f16 staging buffer in the
+//     A-operand order, two tiles ahead; 32x32x16 f16 MFMAs against q scaled exactly into f16.
+//     f16 / bf16 KV (q of the same type): rows of 256 bytes; the 32x32x16 MFMA of that type reads
+//     K from the ring as is (k-step kk: d = 64 hh + 8 kk + 0..7, one 16-byte chunk, chunk c of
+//     row r at c ^ (r & 15)).
 //   * p.V: O^T (128 d x 32 heads) = V^T . P^T, four 32-row d-tiles, two 16-token k-steps.  The
 //     score C tile holds, in lane l register r, token 8(r/4) + 4hh + r%4 of head i; registers
 //     8s..8s+7 are exactly the B operand (P^T) of k-step s when k-slot j of lane half hh means
 //     token 16s + 8(j/4) + 4hh + j%4, so P never moves between lanes.  The A operand (V^T) of lane
-//     (i, hh) for d-tile dt holds d = 4i + dt of those 8 tokens: one 4-byte LDS read per token
-//     row, then a byte permute and the hardware E4M3 -> f16 convert per token pair.
-//   * Softmax in log2 units with v_exp_f32, as in the 16-head kernel.
-//   * f16 / bf16 KV (q of the same type): rows of 256 bytes; q.k^T on the MFMA of that type with K
-//     read from the ring as is (lane (i, hh), k-step kk: d = 64 hh + 8 kk + 0..7, one 16-byte
-//     chunk; chunk c of row r stored at c ^ (r & 15)); V re-laid into the staging buffer without
-//     conversion; bf16 p.V takes P as two bf16 terms (hi + lo), so the weights keep f32-like
-//     precision against exact V.  Partial rows stay fp32.
+//     (i, hh) for d-tile dt holds d = 4i + dt of those 8 tokens: each wave re-lays a quarter of the
+//     next tile's V into a staging buffer in that order (E4M3 and INT8: converted to f16; f16 and
+//     bf16: a halfword permute), so each d-tile's operand is one 16-byte LDS read.  bf16 V takes P
+//     as two bf16 terms (hi + lo), so the weights keep f32-like precision against exact V.
+//   * Softmax in log2 units with v_exp_f32, as in the 16-head kernel; per-token v scales move the
+//     accumulator's power-of-two reference exponent lazily, like the running max.
+//   * A window of query tokens (a separate instantiation) adds a per-column limit: scores past a
+//     column's last visible token are kept out of the tile max and get weight 0.
+//   * Partial rows: f16 of value / row scale for E4M3 and INT8, fp32 for f16 / bf16 KV.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,9 +52,9 @@
 namespace fd {
 namespace {
 
-// Largest batch whose per-sequence tile prefix sums a wide workgroup keeps in LDS (the ring
-// takes most of the LDS, and three workgroups of 4 waves or six of 2 share one CU's 160 KB;
-// larger batches locate tiles with a wave scan of seq_len instead).
+// Largest batch whose per-sequence tile prefix sums a wide workgroup keeps in LDS (the ring and
+// the staging buffers take most of the LDS, two workgroups share one CU's 160 KB; larger batches,
+// and 16-bit KV, whose ring and staging fill 80 KB, locate tiles with a wave scan of seq_len).
 constexpr int kWideLdsBatch = 256;
 
 // Tile max of a window column that sees none of the tile's tokens (log2 units): finite, and far
@@ -965,10 +970,11 @@ void wide_partition_kernel(Params p) {
 // ---------------------------------------------------------------- host-side dispatch
 template <int KVT, int WPG, int QT, int SCALE>
 static hipError_t launch_w(const Params &p, hipStream_t stream) {
-    // tiles in flight per workgroup: up to NSLOT-1; ring + V staging (16 KB) fit two 4-wave
-    // workgroups, or three 2-wave ones, in one CU's 160 KB of LDS; with INT8's K staging (16 KB
-    // more) two workgroups of either size
-    // (16-bit KV: slots of 16 KB, four of them and the staging fill 80 KB, two workgroups per CU)
+    // Ring slots (tiles in flight per workgroup: up to NSLOT-1).  E4M3: 6 (5 with per-token scales,
+    // 4 for 2-wave workgroups); ring + V staging (16 KB) fit two 4-wave workgroups, or three 2-wave
+    // ones, in one CU's 160 KB of LDS.  INT8: 5, with its K staging (16 KB more) two workgroups
+    // of either size.  16-bit KV: slots of 16 KB, four of them and the staging fill 80 KB, two
+    // workgroups per CU.
     constexpr int NSLOT = (KVT == KV_I8 || KVT == KV_F16 || KVT == KV_BF16) ? (KVT == KV_I8 ? 5 : 4)
                                                                            : (WPG == 2 ? 4 : (SCALE == SC_TOKEN_HEAD ? 5 : 6));
     dim3 grid(p.nparts), block(64 * WPG);
