@@ -150,3 +150,9 @@ def test_window_rows_match_single_token_steps_on_prefixes(nq, hq):
 
 def test_workload_verify_fp8_32k_full():
     check_window("verify_fp8_32k", workloads.make_case("verify_fp8_32k", device="cuda"))
+
+
+def test_workload_mqa_fp8_128k_window2_full():
+    # the 128K MQA step with a 2-token window: the wide kernel's window path at full size (256
+    # columns per kv head, ~130 pieces per row through the 8-wave combine), every output row
+    check_window("mqa_fp8_128k_nq2", workloads.make_case("mqa_fp8_128k", device="cuda", nq=2))
