@@ -764,9 +764,13 @@ void partition_kernel(Params p) {
 // sequences over many workgroups) make the single-wave merge a chain of dependent load rounds;
 // NW > 1 splits that chain.  Also writes out = 0, lse = -inf for empty sequences.  Fixed order
 // throughout: deterministic for a given NW.
-template <int D, int NW>
+template <int D, int NW, bool P16>
 __global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
     constexpr int PER = D / 8;  // output elements per lane
+    // pieces in flight per lane group and round: a single-wave row with 16-bit pieces takes two
+    // (8 + 3 registers each), which keeps the kernel within 64 VGPRs -- eight resident waves per
+    // SIMD, so the many one-wave workgroups of a multi-token window or a large batch run in one
+    // residency round; otherwise four
     // per-wave merged state: D outputs, then m and l; rows padded to a 16-byte multiple
     __shared__ __attribute__((aligned(16))) float sh_state[NW > 1 ? NW : 1][D + 4];
     const int mq = blockIdx.x / p.hq, h = blockIdx.x % p.hq, b = blockIdx.y;
@@ -846,38 +850,50 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
     float m = -INFINITY, l = 0.0f, o[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) o[i] = 0.0f;
-    for (int i0 = g; i0 < np; i0 += 4 * gstride) {
-        float2 ml[4];
-        float4 x[4][PER / 4];
+    constexpr int NF = (NW == 1 && P16) ? 2 : 4;
+    for (int i0 = g; i0 < np; i0 += NF * gstride) {
+        float2 ml[NF];
+        float sc[NF];
+        u32x4_t raw[NF][P16 ? PER / 8 : PER / 4];  // f16 words, or fp32 bit patterns
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < NF; u++) {
             const size_t slot = slot_of(min(i0 + gstride * u, np - 1));
             ml[u] = p.ws_ml[slot];
-            if (p.part16) {  // f16 of value / row scale
-                const float sc = p.ws_sc[slot];
+            if constexpr (P16) {  // f16 of value / row scale
+                sc[u] = p.ws_sc[slot];
                 const uint16_t *src = (const uint16_t *)p.ws_acc + slot * D + PER * k;
 #pragma unroll
-                for (int e = 0; e < PER / 8; e++) {
-                    const u32x4_t w = *(const u32x4_t *)(src + 8 * e);
-                    float f[8];
-#pragma unroll
-                    for (int h = 0; h < 4; h++) {
-                        const uint32_t wh = w[h];
-                        f[2 * h] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wh & 0xFFFFu)) * sc;
-                        f[2 * h + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wh >> 16)) * sc;
-                    }
-                    x[u][2 * e] = make_float4(f[0], f[1], f[2], f[3]);
-                    x[u][2 * e + 1] = make_float4(f[4], f[5], f[6], f[7]);
-                }
+                for (int e = 0; e < PER / 8; e++) raw[u][e] = *(const u32x4_t *)(src + 8 * e);
             } else {
                 const float *src = p.ws_acc + slot * D + PER * k;
 #pragma unroll
-                for (int e = 0; e < PER / 4; e++) x[u][e] = *(const float4 *)(src + 4 * e);
+                for (int e = 0; e < PER / 4; e++) raw[u][e] = *(const u32x4_t *)(src + 4 * e);
             }
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < NF; u++) {
             if (i0 + gstride * u < np) {
+                float x[PER];
+                if constexpr (P16) {
+#pragma unroll
+                    for (int e = 0; e < PER / 8; e++)
+#pragma unroll
+                        for (int h2 = 0; h2 < 4; h2++) {
+                            const uint32_t wh = raw[u][e][h2];
+                            x[8 * e + 2 * h2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wh & 0xFFFFu)) * sc[u];
+                            x[8 * e + 2 * h2 + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wh >> 16)) * sc[u];
+                        }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < PER / 4; e++)
+#pragma unroll
+                        for (int h2 = 0; h2 < 4; h2++) {
+                            // through a scalar: a bit cast of the vector element itself reads
+                            // element 0 (hipcc, ROCm 7.2)
+                            const uint32_t w = raw[u][e][h2];
+                            x[4 * e + h2] = __builtin_bit_cast(float, w);
+                        }
+                }
                 // a piece of a window row can hold no visible token (m = -inf, l = 0): the max with
                 // -kMaxFloat gives it weight 0 (and an all-empty state weight 1 on zeros), not NaN
                 const float mn = fmaxf(m, ml[u].x);
@@ -885,12 +901,7 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
                 const float wa = __builtin_amdgcn_exp2f(ma - mc), wb = __builtin_amdgcn_exp2f(mb - mc);
                 l = l * wa + ml[u].y * wb;
 #pragma unroll
-                for (int e = 0; e < PER / 4; e++) {
-                    o[4 * e + 0] = o[4 * e + 0] * wa + x[u][e].x * wb;
-                    o[4 * e + 1] = o[4 * e + 1] * wa + x[u][e].y * wb;
-                    o[4 * e + 2] = o[4 * e + 2] * wa + x[u][e].z * wb;
-                    o[4 * e + 3] = o[4 * e + 3] * wa + x[u][e].w * wb;
-                }
+                for (int e = 0; e < PER; e++) o[e] = o[e] * wa + x[e] * wb;
                 m = mn;
             }
         }
@@ -1049,18 +1060,23 @@ static int combine_waves(const Params &p) {
     return per_seq > 64 ? 8 : per_seq > 16 ? 4 : 1;
 }
 
-template <int D>
+template <int D, bool P16>
 static void launch_combine_d(const Params &p, int nw, hipStream_t stream) {
     dim3 grid(p.hq * p.nq, p.batch);
-    if (nw == 8) hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(512), 0, stream, p);
-    else if (nw == 4) hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((combine_kernel<D, 1>), grid, dim3(64), 0, stream, p);
+    if (nw == 8) hipLaunchKernelGGL((combine_kernel<D, 8, P16>), grid, dim3(512), 0, stream, p);
+    else if (nw == 4) hipLaunchKernelGGL((combine_kernel<D, 4, P16>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((combine_kernel<D, 1, P16>), grid, dim3(64), 0, stream, p);
 }
 
 hipError_t launch_combine(const Params &p, hipStream_t stream) {
     const int nw = combine_waves(p);
-    if (p.d == 128) launch_combine_d<128>(p, nw, stream);
-    else launch_combine_d<64>(p, nw, stream);
+    if (p.d == 128) {
+        if (p.part16) launch_combine_d<128, true>(p, nw, stream);
+        else launch_combine_d<128, false>(p, nw, stream);
+    } else {
+        if (p.part16) launch_combine_d<64, true>(p, nw, stream);
+        else launch_combine_d<64, false>(p, nw, stream);
+    }
     return hipGetLastError();
 }
 
