@@ -269,14 +269,16 @@ def test_ragged_mix_partition_counts(parts):
     check_case(f"ragged_mix/p{parts}", case, num_partitions=parts)
 
 
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "bf16"])
 @pytest.mark.parametrize("parts", [40, 160, 600])
-def test_combine_many_pieces_per_row(parts):
+def test_combine_many_pieces_per_row(parts, kv):
     # one long sequence among short ones, over 10 to 150 partitions per sequence: rows of the long
-    # sequence hold up to ~250 pieces, merged by 1, 4 or 8 combine waves
+    # sequence hold up to ~250 pieces, merged by 1, 4 or 8 combine waves, in several rounds of
+    # loads per lane group (16-bit pieces of E4M3 KV, fp32 pieces of bf16 KV)
     case = workloads.custom_case(seed=21, device="cuda", batch=4, hq=16, hkv=2, d=128,
-                                 seq_lens=[8000, 40, 700, 1], kv="fp8_e4m3", q="bf16",
-                                 scale="token_head", block_size=64)
-    check_case(f"many_pieces/p{parts}", case, num_partitions=parts)
+                                 seq_lens=[8000, 40, 700, 1], kv=kv, q="bf16",
+                                 scale="token_head" if kv == "fp8_e4m3" else "none", block_size=64)
+    check_case(f"many_pieces/{kv}/p{parts}", case, num_partitions=parts)
 
 
 def test_wide_kernel_batch_beyond_lds_prefix_table():
