@@ -757,20 +757,16 @@ void partition_kernel(Params p) {
 // (an empty state has m = -inf and weight 0), then out = acc / l, lse = (M + log2 l) ln 2 (a
 // window row that sees no token: out = 0, lse = -inf).
 // Lane group j = lane / 8 of wave w (global group g = 8 w + j) folds pieces g, g + 8 NW, ... in
-// order over output elements [k*D/8, (k+1)*D/8), k = lane % 8, four pieces' loads in flight at a
+// order over output elements [k*D/8, (k+1)*D/8), k = lane % 8, NF pieces' loads in flight at a
 // time; the eight lane-group states of a wave are merged by a fixed butterfly (both partners
 // compute the same sums), and the NW wave states, in wave order, through LDS.  A row of at most
-// 32 pieces is merged by wave 0 alone (one round of loads).  Many pieces per row (a few very long
-// sequences over many workgroups) make the single-wave merge a chain of dependent load rounds;
-// NW > 1 splits that chain.  Also writes out = 0, lse = -inf for empty sequences.  Fixed order
+// 32 pieces is merged by wave 0 alone (in rounds of 8 * NF pieces' loads).  Many pieces per row
+// (a few very long sequences over many workgroups) make the single-wave merge a chain of
+// dependent load rounds; NW > 1 splits that chain.  Also writes out = 0, lse = -inf for empty sequences.  Fixed order
 // throughout: deterministic for a given NW.
 template <int D, int NW, bool P16>
 __global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
     constexpr int PER = D / 8;  // output elements per lane
-    // pieces in flight per lane group and round: a single-wave row with 16-bit pieces takes two
-    // (8 + 3 registers each), which keeps the kernel within 64 VGPRs -- eight resident waves per
-    // SIMD, so the many one-wave workgroups of a multi-token window or a large batch run in one
-    // residency round; otherwise four
     // per-wave merged state: D outputs, then m and l; rows padded to a 16-byte multiple
     __shared__ __attribute__((aligned(16))) float sh_state[NW > 1 ? NW : 1][D + 4];
     const int mq = blockIdx.x / p.hq, h = blockIdx.x % p.hq, b = blockIdx.y;
@@ -850,6 +846,10 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(Params p) {
     float m = -INFINITY, l = 0.0f, o[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) o[i] = 0.0f;
+    // NF, pieces in flight per lane group and round: a single-wave row with 16-bit pieces takes
+    // two (8 + 3 registers each), which keeps the kernel within 64 VGPRs -- eight resident waves
+    // per SIMD, so the many one-wave workgroups of a multi-token window or a large batch run in
+    // one residency round; otherwise four
     constexpr int NF = (NW == 1 && P16) ? 2 : 4;
     for (int i0 = g; i0 < np; i0 += NF * gstride) {
         float2 ml[NF];
