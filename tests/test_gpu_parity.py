@@ -292,6 +292,18 @@ def test_wide_kernel_batch_beyond_lds_prefix_table():
         check_case(f"wide_batch300/p{parts}", case, num_partitions=parts)
 
 
+def test_largest_batch():
+    # 65535 sequences (the interface's limit; the combine's grid has one row of workgroups per
+    # sequence), lengths 0..40, every fifth one empty
+    rng = np.random.default_rng(12)
+    lens = [int(x) for x in rng.integers(0, 41, size=65535)]
+    for i in range(0, 65535, 5):
+        lens[i] = 0
+    case = workloads.custom_case(seed=12, device="cuda", batch=65535, hq=2, hkv=1, d=64, seq_lens=lens,
+                                 kv="f16", q="f16", scale="none", block_size=16)
+    check_case("batch65535", case)
+
+
 def test_partition_kernel_batch_beyond_lds_prefix_table():
     # 4100 sequences: past the 4096 the 16-head kernel keeps in LDS
     lens = [int(x) for x in np.random.default_rng(8).integers(0, 40, size=4100)]

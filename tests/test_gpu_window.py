@@ -92,6 +92,12 @@ WINDOW = [
                                       q="f16", scale="none", paged=False, block_size=0)),
     ("wide_g64x2_nq5_fp8_tok_f16q", dict(batch=2, hq=128, hkv=2, d=128, seq_lens=[260, 40], nq=5,
                                          kv="fp8_e4m3", q="f16", scale="token_head", block_size=64)),
+    # the largest window the interface takes (64 query tokens): 16-head kernel (one head per kv
+    # head: 64 columns), 32-column kernel (two heads: 128 columns), sequences shorter than it
+    ("g1_nq64_f16_bs32", dict(batch=3, hq=2, hkv=2, d=128, seq_lens=[300, 64, 10], nq=64, kv="f16",
+                              q="f16", scale="none", block_size=32)),
+    ("g2_nq64_fp8_tok_bs64", dict(batch=2, hq=4, hkv=2, d=128, seq_lens=[500, 40], nq=64,
+                                  kv="fp8_e4m3", q="bf16", scale="token_head", block_size=64)),
 ]
 
 
