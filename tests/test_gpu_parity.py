@@ -304,6 +304,16 @@ def test_largest_batch():
     check_case("batch65535", case)
 
 
+def test_longest_sequence():
+    # one sequence of 2^24 tokens (the interface's largest max_seq_len; 4.3 GB of E4M3 K and V)
+    # beside a short one: every workgroup takes a piece of it, so its row merges 256 pieces (one
+    # head: the oracle's single thread for the sequence takes ~35 s)
+    case = workloads.custom_case(seed=14, device="cuda", batch=2, hq=1, hkv=1, d=128,
+                                 seq_lens=[1 << 24, 100], kv="fp8_e4m3", q="bf16", scale="token_head",
+                                 block_size=64)
+    check_case("seq_2^24", case)
+
+
 def test_partition_kernel_batch_beyond_lds_prefix_table():
     # 4100 sequences: past the 4096 the 16-head kernel keeps in LDS
     lens = [int(x) for x in np.random.default_rng(8).integers(0, 40, size=4100)]
