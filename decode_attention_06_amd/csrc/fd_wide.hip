@@ -448,7 +448,13 @@ void wide_partition_kernel(Params p) {
             for (int kk = 0; kk < 8; kk++) qh[kk] = *(const u32x4_t *)(qrow + 8 * kk);
             // complete here (once per segment; see below)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            qk_head = qk_scale;
+            // the multiplier is kept >= 0 (the tile max is taken on raw scores): a negative softmax
+            // scale flips q's sign bits instead (exact)
+            if (qk_scale < 0.0f) {
+#pragma unroll
+                for (int kk = 0; kk < 8; kk++) qh[kk] ^= u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            }
+            qk_head = fabsf(qk_scale);
         } else {
             const uint16_t *qrow = (const uint16_t *)p.q + qrow_idx * D + (I8 ? 8 : 32) * lh;
             // E4M3: raw[4 ks + c] holds d = 64 ks + 32 lh + 8 c + 0..7; INT8: raw[ks] holds
