@@ -11,7 +11,8 @@ every other quantised case: max_abs 5e-3 and rel_l2 3e-3, with the outputs measu
 the V sources' standard deviation (out / v_mag), since the bar is stated for unit-sized data.
 All three partition kernels (a group of 8: 16-head kernel; 32: the 32-column kernel for E4M3;
 128: the wide kernel, also with a 2-token window), E4M3 and INT8, per-token and per-tensor scales;
-f16 / bf16 KV of small and large magnitude on the 16-head and the wide kernel.
+f16 / bf16 KV of small and large magnitude on the 16-head and the wide kernel; q of small and
+large magnitude on every kernel and KV type.
 """
 import itertools
 
@@ -99,6 +100,30 @@ def test_kv_magnitudes(kern, kv, scale, k_mag, v_mag):
     # two partition counts: whole units written directly, and pieces merged by the combine
     check_scaled(f"{kern}-{kv}-{scale}-k{k_mag:g}-v{v_mag:g}", case, num_partitions=0, unit=v_mag)
     check_scaled(f"{kern}-{kv}-{scale}-k{k_mag:g}-v{v_mag:g}-p7", case, num_partitions=7, unit=v_mag)
+
+
+# (q x 1000 makes the logits ~1000 times their usual size.  The E4M3 paths of the wide and 32-column
+# kernels hold q as two E4M3 terms, exact except for values below 2^-9 of the head's largest |q|,
+# which keep an absolute error under 2^-10 of it: harmless at usual logit sizes, it moves such a
+# near one-hot softmax by ~1e-2 there (the 16-head kernel's bf16 q is exact and is run there by
+# test_q_magnitudes); those two cases stop at q x 30.)
+QCASES = [(kern, kv, scale, qm) for kern in ("g8", "g32", "g128")
+          for kv, scale in (("fp8_e4m3", "token_head"), ("int8", "tensor"), ("bf16", "none"))
+          for qm in (1e-20, 1e-3, 30.0, 1e3)
+          if not (kv == "fp8_e4m3" and kern != "g8" and qm > 30.0)]
+
+
+@pytest.mark.parametrize("kern,kv,scale,q_mag", QCASES,
+                         ids=[f"{k}-{kv}-{s}-q{qm:g}" for k, kv, s, qm in QCASES])
+def test_q_magnitudes_every_kernel(kern, kv, scale, q_mag):
+    """q far from unit size (bf16) on every kernel: the E4M3 kernels split q * 2^eq into exact E4M3
+    terms (wide and 32-column kernels) or multiply it as it is (16-head kernel), INT8
+    scales it by a power of two into f16's range, bf16 KV multiplies it as it is; a small q makes
+    the softmax nearly uniform, a large one nearly one-hot."""
+    kw = dict(KERNELS[kern])
+    case = workloads.custom_case(seed=17, device="cuda", kv=kv, q="bf16", scale=scale, q_mag=q_mag, **kw)
+    check_scaled(f"{kern}-{kv}-{scale}-q{q_mag:g}", case, unit=1.0)
+    check_scaled(f"{kern}-{kv}-{scale}-q{q_mag:g}-p7", case, num_partitions=7, unit=1.0)
 
 
 @pytest.mark.parametrize("k_mag,v_mag", [(1e-3, 1.0), (1.0, 1e-3), (1e2, 1.0), (1.0, 1e2), (1e-3, 1e-3)])
