@@ -442,3 +442,28 @@ def test_workload_mqa_bf16_64k_full():
 def test_workload_ragged_fp8_full():
     # every output row (256 sequences x 32 heads, 2.4M tokens)
     check_case("ragged_fp8", workloads.make_case("ragged_fp8", device="cuda"))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(hq=16, hkv=2, kv="fp8_e4m3", scale="token_head", block_size=32),
+    dict(hq=128, hkv=1, kv="bf16", scale="none", block_size=16),
+    dict(hq=128, hkv=1, kv="fp8_e4m3", scale="tensor", block_size=64),
+    dict(hq=16, hkv=2, kv="fp8_e4m3", scale="token_head", block_size=16, nq=4),
+], ids=["g8_fp8_bs32", "wide_bf16_bs16", "wide_fp8_bs64", "direct_nq4_bs16"])
+def test_shared_and_repeated_blocks(kw):
+    # block tables may point several sequences at the same physical blocks (a shared prefix, a
+    # whole duplicated sequence) or one sequence at one block many times: all reads, no writes
+    kw = dict(kw)
+    q = "bf16"
+    case = workloads.custom_case(seed=71, device="cuda", batch=4, d=128, seq_lens=[900, 700, 900, 500],
+                                 q=q, **kw)
+    bs = case.block_size
+    table = case.block_table.clone()
+    full0 = 900 // bs  # whole blocks of sequence 0
+    share = min(full0, 700 // bs) - 1
+    table[1, :share] = table[0, :share]          # sequence 1 starts with sequence 0's blocks
+    table[2] = table[0]                          # sequence 2 is sequence 0's table (same length)
+    nb3 = -(-500 // bs)
+    table[3, :nb3] = table[3, 0]                 # sequence 3 reads its first block over and over
+    case.block_table = table
+    check_case(f"shared_blocks/{kw['kv']}/bs{bs}", case)
