@@ -467,3 +467,29 @@ def test_shared_and_repeated_blocks(kw):
     table[3, :nb3] = table[3, 0]                 # sequence 3 reads its first block over and over
     case.block_table = table
     check_case(f"shared_blocks/{kw['kv']}/bs{bs}", case)
+
+
+@pytest.mark.parametrize("kv", ["int8", "fp8_e4m3"])
+@pytest.mark.parametrize("hq,hkv,nq", [(16, 2, 1), (128, 1, 1), (16, 2, 4)], ids=["g8", "wide_g128", "direct_nq4"])
+def test_every_code_in_the_cache(kv, hq, hkv, nq):
+    # K and V bytes drawn uniformly over every code the format has (INT8: -128..127, -128 included,
+    # which row-absmax quantisation never writes; E4M3: every byte but the two NaNs, so +-448 and
+    # the subnormals too), with per-token scales: the in-kernel conversions of the whole code set
+    # against the oracle's decoder
+    case = workloads.custom_case(seed=81, device="cuda", batch=2, hq=hq, hkv=hkv, d=128, seq_lens=[700, 45],
+                                 nq=nq, kv=kv, q="bf16", scale="token_head", block_size=32)
+    g = torch.Generator(device="cuda").manual_seed(81)
+    for t in (case.k_cache, case.v_cache):
+        raw = torch.randint(0, 256, t.shape, generator=g, device="cuda", dtype=torch.int32)
+        if kv == "fp8_e4m3":
+            raw = torch.where((raw & 0x7F) == 0x7F, raw ^ 0x01, raw)  # 0x7F / 0xFF (NaN) -> 0x7E / 0xFE
+            t.copy_(raw.to(torch.uint8))
+        else:
+            t.copy_((raw - 128).to(torch.int8))
+    # scales that keep the dequantised values near unit size (codes reach 448 / 128)
+    f = 1.0 / 448.0 if kv == "fp8_e4m3" else 1.0 / 128.0
+    case.k_scale = f * (0.5 + torch.rand(case.k_scale.shape, generator=g, device="cuda"))
+    case.v_scale = f * (0.5 + torch.rand(case.v_scale.shape, generator=g, device="cuda"))
+    if kv == "int8":
+        assert int(case.k_cache.min()) == -128 and int(case.v_cache.min()) == -128
+    check_case(f"every_code/{kv}/g{hq // hkv}/nq{nq}", case)
