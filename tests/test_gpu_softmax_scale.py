@@ -33,6 +33,10 @@ KERNELS = [
                            scale="none", block_size=16)),
     ("direct_g8_nq4_fp8_tok", dict(batch=2, hq=16, hkv=2, d=128, seq_lens=[700, 40], nq=4,
                                    kv="fp8_e4m3", q="bf16", scale="token_head", block_size=32)),
+    ("direct_g32_fp8_tensor", dict(batch=2, hq=64, hkv=2, d=128, seq_lens=[700, 40], kv="fp8_e4m3",
+                                   q="f16", scale="tensor", block_size=64)),
+    ("g8_i8_tensor_f16q", dict(batch=2, hq=16, hkv=2, d=128, seq_lens=[700, 40], kv="int8", q="f16",
+                               scale="tensor", block_size=16)),
 ]
 # (multiple of 1/sqrt(head_dim), K source magnitude): at 8 x 4 the scaled scores of a tile span
 # ~2^200 in base 2, past fp32's range for weights taken against anything but the tile's true max;
