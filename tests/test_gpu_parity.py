@@ -493,3 +493,16 @@ def test_every_code_in_the_cache(kv, hq, hkv, nq):
     if kv == "int8":
         assert int(case.k_cache.min()) == -128 and int(case.v_cache.min()) == -128
     check_case(f"every_code/{kv}/g{hq // hkv}/nq{nq}", case)
+
+
+@pytest.mark.parametrize("hq,hkv,kv,scale", [
+    (1024, 1, "fp8_e4m3", "tensor"),    # wide kernel, 32 head blocks of one kv head (8 unit groups)
+    (512, 2, "bf16", "none"),           # wide 16-bit path, 256 heads per kv head
+    (64, 64, "fp8_e4m3", "token_head"), # one head per kv head, 64 kv heads (16-head kernel)
+    (256, 32, "int8", "token_head"),    # 32 kv heads of 8 heads
+], ids=["wide_g1024_fp8", "wide_g256x2_bf16", "g1_hkv64_fp8", "g8_hkv32_i8"])
+def test_many_heads(hq, hkv, kv, scale):
+    case = workloads.custom_case(seed=91, device="cuda", batch=2, hq=hq, hkv=hkv, d=128, seq_lens=[600, 37],
+                                 kv=kv, q="bf16", scale=scale, block_size=64)
+    check_case(f"heads/{hq}x{hkv}/{kv}", case)
+    check_case(f"heads/{hq}x{hkv}/{kv}/p9", case, num_partitions=9)
