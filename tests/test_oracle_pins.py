@@ -264,3 +264,19 @@ def test_seq_mask_computes_only_selected():
     full, _ = oracle.decode_attention(prob, nthreads=1)
     part, _ = oracle.decode_attention(prob, seqs=[1], nthreads=1)
     assert np.array_equal(part[1], full[1]) and np.all(np.isnan(part[0]))
+
+
+@pytest.mark.parametrize("mult", [0.0, -1.0, -6.0, 6.0])
+@pytest.mark.parametrize("kv,qd,scale", [("fp8_e4m3", "bf16", "token_head"), ("int8", "f16", "tensor"),
+                                         ("bf16", "bf16", "none")])
+def test_oracle_vs_bruteforce_any_softmax_scale(kv, qd, scale, mult):
+    """Any finite softmax scale: zero (uniform weights), negative (the ranking reversed) and large
+    ones, against the literal brute force (which subtracts no maximum)."""
+    d = 16
+    dn = Dense(33, [19, 40, 1], 4, 2, d, kv=kv, q=qd, scale=scale)
+    kw = dn.paged(8, seed=34)
+    kw["softmax_scale"] = mult / math.sqrt(d)
+    out, lse = oracle.decode_attention(oracle.Problem(**kw), nthreads=2)
+    bo, bl = brute_attention(*dn.dense_values(), mult / math.sqrt(d))
+    np.testing.assert_allclose(out, np.array(bo), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(bl), rtol=1e-11, atol=1e-12)
