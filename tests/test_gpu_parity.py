@@ -352,13 +352,23 @@ def test_peaky_scores(hq, kv):
     check_case(f"peaky_q4_hq{hq}_{kv}", case, num_partitions=0)
 
 
+@pytest.mark.parametrize("parts", [0, 1])
+@pytest.mark.parametrize("kern", [
+    dict(hq=16, hkv=2, kv="fp8_e4m3", scale="token_head"),
+    dict(hq=128, hkv=1, kv="fp8_e4m3", scale="tensor"),
+    dict(hq=128, hkv=1, kv="bf16", scale="none"),
+    dict(hq=16, hkv=2, kv="fp8_e4m3", scale="token_head", nq=4),
+], ids=["g8_fp8", "wide_fp8", "wide_bf16", "direct_nq4"])
 @pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
-def test_half_outputs_are_rounded_f32(out_dtype):
-    case = workloads.custom_case(seed=11, device="cuda", batch=2, hq=16, hkv=2, d=128,
-                                 seq_lens=[900, 3], kv="fp8_e4m3", q="bf16", scale="token_head",
-                                 block_size=64)
-    o32, _ = run_gpu(case, out_dtype="f32")
-    oh, _ = run_gpu(case, out_dtype=out_dtype)
+def test_half_outputs_are_rounded_f32(out_dtype, kern, parts):
+    # rows finished by a partition kernel (the short sequence; everything with one partition) and
+    # rows merged by the combine (the long sequence cut into pieces) both round the fp32 result
+    kw = dict(kern)
+    q = "bf16" if kw["kv"] != "f16" else "f16"
+    case = workloads.custom_case(seed=11, device="cuda", batch=2, d=128, seq_lens=[900, 3], q=q,
+                                 block_size=64, **kw)
+    o32, _ = run_gpu(case, out_dtype="f32", num_partitions=parts)
+    oh, _ = run_gpu(case, out_dtype=out_dtype, num_partitions=parts)
     ref = o32.to({"f16": torch.float16, "bf16": torch.bfloat16}[out_dtype])
     assert torch.equal(oh, ref)
 
