@@ -100,8 +100,10 @@ typedef enum {
  *   scale_mode   FD_SCALE_NONE for f16/bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 / INT8
  *                KV (15.11: quantised KV, per-token k/v scales).
  *   k_scale,     fp32 dequantisation scales (value = decode(byte) * scale), NULL when none.
- *   v_scale
- *   softmax_scale  multiplies q . k (natural-exp softmax); usually 1/sqrt(head_dim).
+ *   v_scale      Per tensor: [1]; per token and kv head: one per cache row and kv head, in the
+ *                cache's row order.  Any finite values, zero and negative included.
+ *   softmax_scale  multiplies q . k (natural-exp softmax); usually 1/sqrt(head_dim).  Any finite
+ *                value (zero and negative included); NaN or infinity is FD_ERR_INVALID_ARG.
  *   out          [batch][num_q_heads][head_dim] in out_dtype (FD_F32, FD_F16 or FD_BF16).
  *   lse          optional [batch][num_q_heads] fp32 natural-log sum of exp(scores); NULL = skip.
  *                An empty sequence (seq_len 0) yields out = 0 and lse = -inf.
